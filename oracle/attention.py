@@ -1,0 +1,203 @@
+"""Plain float64 CPU oracle for the attention forward pass (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use this module.  It shares no code with the HIP library and
+imports nothing from it.
+
+What is computed
+----------------
+The pages name the operation without writing it out: the nvFuser issue #2278
+"Investigate a new SDPA IR node" (Priya2698's meeting summary) pairs a forward
+SDPA node with a backward one and points at PyTorch's
+``scaled_dot_product_attention``; the AOTriton PR #31 "Add varlen support to
+AOTriton's Flash Attention" (opening comment) adds the variable-length forward.
+The plainest reading, used here, is for one (batch or sequence, head) with
+``Lq`` query rows and ``Lk`` key rows::
+
+    S[i, j]  = scale * sum_d Q[i, d] * K[j, d]
+    allowed  = (j < Lk) and (not causal or j <= i)      # top-left causal
+    m[i]     = max_{allowed j} S[i, j]
+    P[i, j]  = exp(S[i, j] - m[i]) if allowed else 0
+    l[i]     = sum_j P[i, j]
+    O[i, :]  = sum_j (P[i, j] / l[i]) * V[j, :]
+    LSE[i]   = m[i] + ln(l[i])                          # natural log
+
+A row with no allowed key (only possible when ``Lk == 0``) has ``O = 0`` and
+``LSE = -inf``.  The forward returns LSE because the nvFuser issue's discussion
+(IvanYashchuk's and jjsjann123's replies) leaves it to the forward to hand the
+backward what it cannot cheaply recompute; one number per query row is enough
+to rebuild P.
+
+Causal alignment when ``Lq != Lk`` is not stated on the pages; this oracle
+takes the top-left reading (query i sees keys 0..i, local indices), which is
+what PyTorch's ``is_causal`` does.
+
+The three modes differ only in which rows and keys form each (sequence, head):
+
+* dense BHSD: batch b uses all ``Sq`` rows of Q[b, h] and ``Sk`` rows of K/V;
+* compact varlen (AOTriton PR #31, opening comment): one batch of packed
+  tokens; sequence z owns query tokens ``[cu_q[z], cu_q[z+1])`` and key tokens
+  ``[cu_k[z], cu_k[z+1])``; no attention crosses sequences;
+* padded varlen (AOTriton PR #31, the fwd_kernel.py excerpt in xinyazhang's
+  last code reply): batch b keeps its own rank-4 slab, its true lengths are the
+  differences ``cu[b+1] - cu[b]`` and its rows and keys start at offset 0.
+
+Everything is float64.  Inputs of lower precision convert exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "attention_head",
+    "sdpa_dense",
+    "sdpa_compact_varlen",
+    "sdpa_padded_varlen",
+    "lengths_from_cu",
+]
+
+
+def attention_head(q, k, v, scale, causal, rows=None):
+    """Attention of one (sequence, head) in float64, score matrix materialised.
+
+    q: (Lq, D), k: (Lk, D), v: (Lk, Dv).  ``rows`` optionally selects which
+    local query indices to compute (their causal limit is still their own
+    index).  Returns ``(O, LSE)`` with shapes ``(len(rows), Dv)`` and
+    ``(len(rows),)``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lq, lk = q.shape[0], k.shape[0]
+    if v.shape[0] != lk:
+        raise ValueError("K and V must have the same number of rows")
+    if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
+        raise ValueError("Q and K must be (rows, D) with the same D")
+    if rows is None:
+        rows = np.arange(lq)
+    rows = np.asarray(rows, dtype=np.int64)
+    dv = v.shape[1]
+    out = np.zeros((rows.size, dv), dtype=np.float64)
+    lse = np.full((rows.size,), -np.inf, dtype=np.float64)
+    if rows.size == 0 or lk == 0:
+        return out, lse
+
+    # Step 1: scaled scores (one library matmul).
+    s = float(scale) * (q[rows] @ k.T)
+    # Step 2: which keys each row may see.
+    key_idx = np.arange(lk)[None, :]
+    allowed = np.ones((rows.size, lk), dtype=bool)
+    if causal:
+        allowed = key_idx <= rows[:, None]
+    has_key = allowed.any(axis=1)
+    # Step 3: row max over allowed keys, exponentials, row sums.
+    s_masked = np.where(allowed, s, -np.inf)
+    m = s_masked.max(axis=1)
+    m_safe = np.where(has_key, m, 0.0)
+    p = np.where(allowed, np.exp(s_masked - m_safe[:, None]), 0.0)
+    l = p.sum(axis=1)
+    # Step 4: normalised weights times V, and the natural-log logsumexp.
+    l_safe = np.where(has_key, l, 1.0)
+    out = (p / l_safe[:, None]) @ v
+    lse = np.where(has_key, m_safe + np.log(l_safe), -np.inf)
+    out[~has_key] = 0.0
+    return out, lse
+
+
+def lengths_from_cu(cu, total=None):
+    """Per-sequence lengths from an int32 exclusive prefix-sum array.
+
+    The AOTriton PR #31 excerpt takes each length as the difference of two
+    neighbouring ``cu_seqlens`` entries.  ``cu`` must start at 0 and never
+    decrease; ``total`` (if given) bounds the last entry.
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2:
+        raise ValueError("cu_seqlens needs at least two entries")
+    if cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0")
+    lengths = np.diff(cu)
+    if (lengths < 0).any():
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if total is not None and cu[-1] > total:
+        raise ValueError("cu_seqlens ends past the token count")
+    return lengths
+
+
+def sdpa_dense(q, k, v, scale, causal, heads=None):
+    """Dense BHSD forward.  q: (B,H,Sq,D), k/v: (B,H,Sk,D).
+
+    Returns ``(O, LSE)`` shaped (B,H,Sq,Dv) and (B,H,Sq).  ``heads``
+    optionally restricts the work to a list of (b, h) pairs; the other
+    entries are left as NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, h_, sq, _ = q.shape
+    out = np.full(q.shape[:3] + (v.shape[3],), np.nan)
+    lse = np.full((b_, h_, sq), np.nan)
+    pairs = [(b, h) for b in range(b_) for h in range(h_)] if heads is None else heads
+    for b, h in pairs:
+        out[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal)
+    return out, lse
+
+
+def sdpa_compact_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    """Compact variable-length forward over packed THD tokens.
+
+    q: (Tq, H, D), k/v: (Tk, H, D).  Sequence z owns query tokens
+    ``[cu_q[z], cu_q[z+1])`` and key tokens ``[cu_k[z], cu_k[z+1])``; the mask
+    uses indices local to the sequence.  Returns ``(O, LSE)`` shaped
+    (Tq, H, Dv) and (H, Tq); tokens past ``cu_q[-1]`` stay NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    tq, h_, _ = q.shape
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    lengths_from_cu(cu_q, tq)
+    lengths_from_cu(cu_k, k.shape[0])
+    if cu_q.size != cu_k.size:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same sequence count")
+    out = np.full((tq, h_, v.shape[2]), np.nan)
+    lse = np.full((h_, tq), np.nan)
+    for z in range(cu_q.size - 1):
+        qs, qe = cu_q[z], cu_q[z + 1]
+        ks, ke = cu_k[z], cu_k[z + 1]
+        for h in range(h_):
+            o_zh, lse_zh = attention_head(q[qs:qe, h], k[ks:ke, h], v[ks:ke, h], scale, causal)
+            out[qs:qe, h] = o_zh
+            lse[h, qs:qe] = lse_zh
+    return out, lse
+
+
+def sdpa_padded_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    """Padded variable-length forward over rank-4 BHSD slabs.
+
+    q: (B,H,Sq_max,D), k/v: (B,H,Sk_max,D).  Batch b uses rows
+    ``0 .. cu_q[b+1]-cu_q[b]-1`` and keys ``0 .. cu_k[b+1]-cu_k[b]-1``.  Rows
+    past a batch's true length are not defined and stay NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, h_, sq, _ = q.shape
+    lq = lengths_from_cu(cu_q)
+    lk = lengths_from_cu(cu_k)
+    if lq.size != b_ or lk.size != b_:
+        raise ValueError("padded varlen needs B+1 cu_seqlens entries")
+    if (lq > sq).any() or (lk > k.shape[2]).any():
+        raise ValueError("a true length exceeds the padded length")
+    out = np.full(q.shape[:3] + (v.shape[3],), np.nan)
+    lse = np.full((b_, h_, sq), np.nan)
+    for b in range(b_):
+        for h in range(h_):
+            o_bh, lse_bh = attention_head(
+                q[b, h, : lq[b]], k[b, h, : lk[b]], v[b, h, : lk[b]], scale, causal
+            )
+            out[b, h, : lq[b]] = o_bh
+            lse[b, h, : lq[b]] = lse_bh
+    return out, lse
