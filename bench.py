@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the flash-attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+One step is one pass of the whole forward path over the dense bf16 BHSD
+workload B=4, H=16, Sq=Sk=2048, D=128 with scale 1/sqrt(128): the
+non-causal forward followed by the causal forward (both masks of that
+workload), inputs resident in HBM.  FLOPs are 4*Sq*Sk*D*H*B per forward,
+halved for causal.  The line also carries the compact varlen THD workload
+(16 sequences, lengths U{1..4096} from seed 4, H=16, D=128, bf16, causal)
+timed the same way, a roofline record for the dominant kernel (the
+non-causal forward, timed per launch with HIP events on the stream it runs
+on) and the float64 CPU oracle timed on a bounded sample of the same
+workload.
+
+Prints ONE JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16 BHSD S=2048 D=128; varlen THD)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/attn_fwd.hip",
+                  "scaled_dot_product_03_amd/csrc/dispatch_table.inc"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_tag: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel_tag}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha:\s*(\w+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def dense_flops(B, H, Sq, Sk, D, causal):
+    f = 4.0 * Sq * Sk * D * H * B
+    return f / 2 if causal else f
+
+
+def varlen_flops(lengths, H, D, causal):
+    f = sum(4.0 * L * L * D * H for L in lengths)
+    return f / 2 if causal else f
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The float64 oracle, as it is, on a bounded sample of the workload's
+    heads (both masks), on this host's cores."""
+    from oracle import attention_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        threads = os.cpu_count() or 1
+    B, H, Sq, D = x.q.shape
+    Sk = x.k.shape[2]
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        q = x.q[b, h].double().numpy()
+        k = x.k[b, h].double().numpy()
+        v = x.v[b, h].double().numpy()
+        for causal in x.causal_modes:
+            attention_head(q, k, v, x.scale, causal)
+            flops += dense_flops(1, 1, Sq, Sk, D, causal)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{done} of {len(pairs)} (batch, head) pairs of B{B} H{H} S{Sq} D{D} bf16 "
+                  f"(inputs widened to fp64), non-causal + causal, {dt:.1f} s wall",
+        "cpu_model": _cpu_model(), "host_cpu_count": os.cpu_count(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the kernels are single-GPU; --gpus {args.gpus} "
+              "is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from scaled_dot_product_03_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    wl = "dense_bf16_b4h16s2048d128"
+    x = inputs.workload(wl)
+    B, H, Sq, D = x.q.shape
+    Sk = x.k.shape[2]
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    f_nc = dense_flops(B, H, Sq, Sk, D, False)
+    f_c = dense_flops(B, H, Sq, Sk, D, True)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        binding.attn_fwd(q, k, v, scale=x.scale, causal=False, out=o, lse=lse)
+        if events is not None:
+            events[1].record(stream)
+        binding.attn_fwd(q, k, v, scale=x.scale, causal=True, out=o, lse=lse)
+        if events is not None:
+            events[2].record(stream)
+
+    log(f"warmup {args.warmup} steps on {wl}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nc_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    c_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    log(f"timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step")
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = (f_nc + f_c) / (ms_per_step * 1e-3) / 1e12
+    nc_avg = float(np.mean(nc_ms))
+    c_avg = float(np.mean(c_ms))
+    achieved = f_nc / (nc_avg * 1e-3) / 1e12
+    traffic = traffic_from_profiles("dense_bf16_b4h16s2048d128_noncausal")
+
+    breakdown = {
+        "noncausal": {"flops": f_nc, "avg_ms": nc_avg, "median_ms": float(np.median(nc_ms)),
+                      "min_ms": float(np.min(nc_ms)), "tflops": achieved,
+                      "pct_mfma_peak": 100 * achieved / PEAK_BF16_TFLOPS},
+        "causal": {"flops": f_c, "avg_ms": c_avg, "median_ms": float(np.median(c_ms)),
+                   "min_ms": float(np.min(c_ms)),
+                   "tflops": f_c / (c_avg * 1e-3) / 1e12,
+                   "pct_mfma_peak": 100 * f_c / (c_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+    }
+
+    if not args.no_varlen:
+        vx = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
+        vq, vk, vv = vx.q.to(dev), vx.k.to(dev), vx.v.to(dev)
+        cu = torch.from_numpy(vx.cu_seqlens_q).to(dev)
+        lengths = vx.meta["lengths_q"]
+        maxlen = int(max(lengths))
+        vo = torch.empty_like(vq)
+        vlse = torch.empty((1, vq.shape[1], vq.shape[0]), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            binding.attn_fwd_compact_varlen(vq, vk, vv, cu, cu, maxlen, maxlen, scale=vx.scale,
+                                            causal=True, out=vo, lse=vlse)
+        ve = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ve[i][0].record(stream)
+            binding.attn_fwd_compact_varlen(vq, vk, vv, cu, cu, maxlen, maxlen, scale=vx.scale,
+                                            causal=True, out=vo, lse=vlse)
+            ve[i][1].record(stream)
+        torch.cuda.synchronize()
+        v_ms = [a.elapsed_time(b) for a, b in ve]
+        vf = varlen_flops(lengths, vq.shape[1], vq.shape[2], True)
+        breakdown["varlen_thd_causal"] = {
+            "workload": "thd_bf16_16seq_len1to4096_h16d128_causal (seed 4, T=%d)" % vq.shape[0],
+            "flops": vf, "avg_ms": float(np.mean(v_ms)), "median_ms": float(np.median(v_ms)),
+            "tflops": vf / (np.mean(v_ms) * 1e-3) / 1e12,
+            "pct_mfma_peak": 100 * vf / (np.mean(v_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del vq, vk, vv, vo, vlse
+
+    bm, bn, waves = binding.kernel_config(torch.bfloat16, D)
+    record = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense_bf16_b4h16s2048d128: BHSD B=4 H=16 Sq=Sk=2048 D=128 bf16, "
+                               "scale 1/sqrt(128), one non-causal + one causal forward per step",
+                   "global_batch": B, "seq_len": Sq, "heads": H, "head_dim": D,
+                   "parallelism": "single GPU",
+                   "kernel": {"block_m": bm, "block_n": bn, "waves": waves}},
+        "pct_mfma_peak": 100 * value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "attn_fwd_kernel<bf16, D=128, dense, non-causal>",
+                     "flops_per_launch": f_nc, "avg_launch_ms": nc_avg},
+        "breakdown": breakdown,
+        "kernel_source_sha": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 CPU oracle on a bounded sample")
+        record["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * sdpa03.h -- C ABI of libsdpa03.so: the flash-attention forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation.  For one (batch or sequence, head) with Lq query rows and Lk
+ * key rows, every entry point computes
+ *
+ *     S    = scale * Q K^T                      (fp32 accumulation)
+ *     P    = softmax over the allowed keys of each row of S
+ *     O    = P V                                 (stored in the input dtype)
+ *     LSE  = per-row natural-log logsumexp of the allowed scaled scores (fp32)
+ *
+ * tile by tile with a running max and running sum, never writing S to
+ * memory.  With causal != 0 query row i sees keys 0..i in indices local to
+ * its sequence (top-left alignment; it equals bottom-right when Lq == Lk).
+ * A row that sees no key (only when Lk == 0) gets O = 0 and LSE = -inf.
+ * The operation is the scaled-dot-product attention that nvFuser issue
+ * #2278 "Investigate a new SDPA IR node" wants as a forward node; LSE is the
+ * per-row value that the issue's discussion of what to stash for the
+ * backward pass calls for.
+ *
+ * Three entry points share one kernel family, as AOTriton PR #31 "Add
+ * varlen support to AOTriton's Flash Attention" does for its forward
+ * (opening comment): dense, compact variable-length and padded
+ * variable-length.  Following the same PR's closing reply, a new layout
+ * would get a new entry point rather than a flag on these.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ *  - Tensors are rank-4 views (batch, head, seq, dim) given as a device
+ *    pointer and four strides counted in ELEMENTS (the rank-4 view with
+ *    pointer plus sizes plus strides that the PR's TensorView<4> names).
+ *    stride[3] (dim) must be 1.  Q, K, V and O share one dtype; K and V
+ *    share their sizes; Q and O share their sizes; Q and K may differ only
+ *    in sequence length (AOTriton issue #12, xinyazhang's reply on the
+ *    attn_fwd constraints).
+ *  - Base pointers must be 16-byte aligned and strides[0..2] times the
+ *    element size must be multiples of 16 bytes (the kernels use 128-bit
+ *    loads).
+ *  - lse is a contiguous fp32 array written for valid rows only.
+ *  - Sequence-length arguments are int32, as the PR unifies them.
+ *  - head_dim must be 64 or 128.  dtype is one of sdpa_dtype.
+ *  - scale must be finite and > 0 (callers usually pass 1/sqrt(head_dim)).
+ *  - Ownership: the caller allocates and owns every buffer.  The library
+ *    allocates nothing, keeps no state between calls, never synchronises
+ *    and may be called from several host threads at once.  Work is queued on
+ *    hip_stream (a hipStream_t; NULL means the null stream) and completes
+ *    asynchronously; outputs are valid once that stream has reached the
+ *    launch.  Calls that share output buffers on different streams race.
+ *  - Errors: every argument is checked on the host before anything is
+ *    launched.  On any error nothing is launched and no output is touched;
+ *    the status says what was wrong (sdpa_status_string).  A launch the HIP
+ *    runtime rejects returns SDPA_ERR_HIP.  An empty problem (no query row
+ *    to produce) returns SDPA_OK without launching.
+ *  - Unsupported inputs are rejected, never silently mis-computed: Triton
+ *    issue #2267 "[RFC] Goal for triton.ops.flash_attention" (opening
+ *    comment) describes an attention op that gave wrong answers for inputs
+ *    outside its assumptions, and nvFuser issue #2278 notes that flash
+ *    attention does not cover every input.
+ */
+#ifndef SDPA03_H
+#define SDPA03_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDPA_F32 = 0,  /* float32 in and out; fp32 products (no 16-bit rounding) */
+  SDPA_F16 = 1,  /* IEEE half in and out; fp32 accumulation */
+  SDPA_BF16 = 2  /* bfloat16 in and out; fp32 accumulation */
+} sdpa_dtype;
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL = 1,      /* a required pointer is NULL */
+  SDPA_ERR_DTYPE = 2,     /* dtype is not an sdpa_dtype value */
+  SDPA_ERR_HEAD_DIM = 3,  /* head_dim is not 64 or 128 */
+  SDPA_ERR_SHAPE = 4,     /* a size is negative, or the problem is too large to index */
+  SDPA_ERR_STRIDE = 5,    /* stride[3] != 1, a negative stride, or offsets overflow */
+  SDPA_ERR_ALIGN = 6,     /* a base pointer or stride breaks 16-byte alignment */
+  SDPA_ERR_BATCH = 7,     /* compact varlen called with B != 1 */
+  SDPA_ERR_SEQLEN = 8,    /* bad sequence-length arguments or cu_seqlens contents */
+  SDPA_ERR_SCALE = 9,     /* scale is not finite and positive */
+  SDPA_ERR_HIP = 10       /* the HIP runtime rejected the launch */
+} sdpa_status;
+
+/* Static text for a status code (never NULL). */
+const char* sdpa_status_string(sdpa_status status);
+
+/*
+ * Dense forward.  Q: (B, H, seqlen_q, head_dim), K and V:
+ * (B, H, seqlen_k, head_dim), O like Q, lse: (B, H, seqlen_q) fp32
+ * contiguous.  seqlen_q != seqlen_k is allowed (Triton issue #2267 lists
+ * differing query and key counts as a use case).  Sizes may be zero.
+ */
+sdpa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                     int32_t seqlen_k, int32_t head_dim,
+                     const int64_t q_stride[4], const int64_t k_stride[4],
+                     const int64_t v_stride[4], const int64_t o_stride[4],
+                     float scale, int32_t causal, void* hip_stream);
+
+/*
+ * Compact variable-length forward (AOTriton PR #31, opening comment: rank-4
+ * tensors whose batch size is exactly 1, over packed tokens).  Packed
+ * (total, H, head_dim) token memory is passed as the (1, H, total, head_dim)
+ * view with strides (total*H*D, D, H*D, 1); any view with dim stride 1 works.
+ *
+ * Sequence z owns query tokens [cu_seqlens_q[z], cu_seqlens_q[z+1]) and key
+ * tokens [cu_seqlens_k[z], cu_seqlens_k[z+1]); no attention crosses
+ * sequences and the causal mask uses indices local to the sequence.
+ * cu_seqlens_q and cu_seqlens_k are DEVICE arrays of num_seqs + 1 int32
+ * exclusive prefix sums; they are read only by the kernel.
+ * lse: (1, H, total_q) fp32 contiguous.  Tokens past cu_seqlens_q[num_seqs]
+ * are neither read nor written.
+ *
+ * B must be 1 (SDPA_ERR_BATCH otherwise: extra batches are refused rather
+ * than ignored).  num_seqs >= 0; 0 <= max_seqlen_q <= total_q and
+ * 0 <= max_seqlen_k <= total_k.
+ *
+ * Contract not checked on the device (the contents of device memory are not
+ * read on the host): cu_seqlens_*[0] == 0, entries non-decreasing, the last
+ * entry <= total_*, every length <= max_seqlen_*.  Host code that holds a
+ * copy can check it with sdpa_check_cu_seqlens_host first.
+ */
+sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                                    int32_t total_q, int32_t total_k, int32_t head_dim,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t num_seqs, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k,
+                                    const int64_t q_stride[4], const int64_t k_stride[4],
+                                    const int64_t v_stride[4], const int64_t o_stride[4],
+                                    float scale, int32_t causal, void* hip_stream);
+
+/*
+ * Padded variable-length forward.  Q: (B, H, seqlen_q_max, head_dim), K and
+ * V: (B, H, seqlen_k_max, head_dim), O like Q, lse: (B, H, seqlen_q_max)
+ * fp32 contiguous.  Batch b's true lengths are cu_seqlens_q[b+1] -
+ * cu_seqlens_q[b] and cu_seqlens_k[b+1] - cu_seqlens_k[b] (DEVICE int32
+ * arrays of B + 1 entries); its rows and keys start at offset 0 of its own
+ * slab, as in the padded branch of the fwd_kernel.py excerpt that AOTriton
+ * PR #31 quotes.  Rows and keys at or past a batch's true length are never
+ * read; their O and lse entries are left untouched.
+ *
+ * Contract not checked on the device: entries non-decreasing and every
+ * length <= seqlen_*_max.
+ */
+sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                                   int32_t seqlen_q_max, int32_t seqlen_k_max,
+                                   int32_t head_dim, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k,
+                                   const int64_t q_stride[4], const int64_t k_stride[4],
+                                   const int64_t v_stride[4], const int64_t o_stride[4],
+                                   float scale, int32_t causal, void* hip_stream);
+
+/*
+ * Host-side check of a HOST copy of a cu_seqlens array of n + 1 entries:
+ * starts at 0, non-decreasing, last entry <= total, every length <=
+ * max_len.  Returns SDPA_OK or SDPA_ERR_SEQLEN (SDPA_ERR_NULL for NULL).
+ */
+sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t total,
+                                       int32_t max_len);
+
+/*
+ * The compiled-in kernel choice for a problem class: query rows per
+ * workgroup (block_m), keys per tile (block_n) and wavefronts per
+ * workgroup.  mode: 0 dense, 1 compact varlen, 2 padded varlen.  Any output
+ * pointer may be NULL.  Returns SDPA_ERR_DTYPE / SDPA_ERR_HEAD_DIM for
+ * unsupported classes.
+ */
+sdpa_status sdpa_kernel_config(sdpa_dtype dtype, int32_t head_dim, int32_t causal,
+                               int32_t mode, int32_t* block_m, int32_t* block_n,
+                               int32_t* waves);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA03_H */

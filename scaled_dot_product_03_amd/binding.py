@@ -1,0 +1,234 @@
+"""ctypes binding of libsdpa03.so (argument marshalling only).
+
+Each function takes torch tensors that live on a ROCm device, reads their
+pointers and strides, allocates outputs with torch, and calls the C entry
+point of the same name on the current torch stream.  Every step of the
+attention itself runs in the library's HIP kernels; if the library is not
+built, the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+from .build import LIB_PATH
+
+_DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_BAD_DTYPE = 99  # lets the library report SDPA_ERR_DTYPE itself
+
+STATUS_NAMES = {
+    0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_DTYPE", 3: "SDPA_ERR_HEAD_DIM",
+    4: "SDPA_ERR_SHAPE", 5: "SDPA_ERR_STRIDE", 6: "SDPA_ERR_ALIGN", 7: "SDPA_ERR_BATCH",
+    8: "SDPA_ERR_SEQLEN", 9: "SDPA_ERR_SCALE", 10: "SDPA_ERR_HIP",
+}
+
+EXPORTED = (
+    "sdpa_status_string",
+    "attn_fwd",
+    "attn_fwd_compact_varlen",
+    "attn_fwd_padded_varlen",
+    "sdpa_check_cu_seqlens_host",
+    "sdpa_kernel_config",
+)
+
+
+class SdpaError(RuntimeError):
+    """A non-zero sdpa_status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_stride = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; build it with `python -m scaled_dot_product_03_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.sdpa_status_string.restype = ctypes.c_char_p
+    lib.sdpa_status_string.argtypes = [ctypes.c_int]
+    common_tail = [_stride, _stride, _stride, _stride, ctypes.c_float, _i32, _p]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32] + common_tail
+    lib.attn_fwd_compact_varlen.restype = ctypes.c_int
+    lib.attn_fwd_compact_varlen.argtypes = (
+        [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32, _i32]
+        + common_tail)
+    lib.attn_fwd_padded_varlen.restype = ctypes.c_int
+    lib.attn_fwd_padded_varlen.argtypes = (
+        [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p] + common_tail)
+    lib.sdpa_check_cu_seqlens_host.restype = ctypes.c_int
+    lib.sdpa_check_cu_seqlens_host.argtypes = [_i32p, _i32, _i32, _i32]
+    lib.sdpa_kernel_config.restype = ctypes.c_int
+    lib.sdpa_kernel_config.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32p, _i32p, _i32p]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().sdpa_status_string(status).decode()
+        raise SdpaError(status, msg)
+
+
+def _strides(t: torch.Tensor):
+    return (ctypes.c_int64 * 4)(*t.stride())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return _DTYPE_CODES.get(t.dtype, _BAD_DTYPE)
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale(scale, head_dim):
+    return 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("inputs must be ROCm device tensors")
+
+
+def kernel_config(dtype: torch.dtype, head_dim: int, causal: bool = False, mode: int = 0):
+    """(block_m, block_n, waves) of the compiled kernel for a problem class."""
+    lib = load_library()
+    bm, bn, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.sdpa_kernel_config(_DTYPE_CODES.get(dtype, _BAD_DTYPE), head_dim, int(causal), mode,
+                                  ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(w)))
+    return bm.value, bn.value, w.value
+
+
+def check_cu_seqlens_host(cu, total: int, max_len: int) -> None:
+    """Validate a host cu_seqlens array with the library's own check."""
+    arr = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    ptr = arr.ctypes.data_as(_i32p)
+    _check(load_library().sdpa_check_cu_seqlens_host(ptr, arr.size - 1, int(total), int(max_len)))
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """Dense forward.  q: (B,H,Sq,D), k/v: (B,H,Sk,D) -> (o, lse (B,H,Sq) fp32)."""
+    lib = load_library()
+    _require_gpu(q, k, v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        _dtype_code(q), B, H, Sq, Sk, D,
+        _strides(q), _strides(k), _strides(v), _strides(o),
+        _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    return o, lse
+
+
+def _device_cu(cu, device, total, max_len, check):
+    if isinstance(cu, torch.Tensor) and cu.is_cuda:
+        if cu.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        return cu
+    arr = np.asarray(cu.cpu().numpy() if isinstance(cu, torch.Tensor) else cu, dtype=np.int32)
+    if check:
+        check_cu_seqlens_host(arr, total, max_len)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def attn_fwd_compact_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None,
+                            max_seqlen_k=None, scale=None, causal=False, out=None, lse=None,
+                            check=True):
+    """Compact varlen forward over packed (T, H, D) tokens.
+
+    cu_seqlens may be host arrays (checked with the library's host check,
+    then copied to the device) or device int32 tensors (used as given).
+    Returns (o (Tq,H,D), lse (1,H,Tq) fp32).  Max lengths default to the
+    largest length in host cu_seqlens.
+    """
+    lib = load_library()
+    _require_gpu(q, k, v)
+    Tq, H, D = q.shape
+    Tk = k.shape[0]
+    if k.shape != (Tk, H, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+
+    def _max_len(cu, given):
+        if given is not None:
+            return int(given)
+        if isinstance(cu, torch.Tensor) and cu.is_cuda:
+            raise ValueError("max_seqlen is required with device cu_seqlens")
+        c = np.asarray(cu.cpu().numpy() if isinstance(cu, torch.Tensor) else cu, dtype=np.int64)
+        return int(np.diff(c).max()) if c.size > 1 else 0
+
+    max_q = _max_len(cu_seqlens_q, max_seqlen_q)
+    max_k = _max_len(cu_seqlens_k, max_seqlen_k)
+    cu_q = _device_cu(cu_seqlens_q, q.device, Tq, max_q, check)
+    cu_k = _device_cu(cu_seqlens_k, q.device, Tk, max_k, check)
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same length")
+    num_seqs = cu_q.numel() - 1
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((1, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    # (T, H, D) token memory seen as the rank-4 view (1, H, T, D).
+    qv, kv, vv, ov = (t.transpose(0, 1).unsqueeze(0) for t in (q, k, v, o))
+    _check(lib.attn_fwd_compact_varlen(
+        qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
+        _dtype_code(q), 1, H, Tq, Tk, D, cu_q.data_ptr(), cu_k.data_ptr(), num_seqs, max_q, max_k,
+        _strides(qv), _strides(kv), _strides(vv), _strides(ov),
+        _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    return o, lse
+
+
+def attn_fwd_padded_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False,
+                           out=None, lse=None, check=True):
+    """Padded varlen forward.  q: (B,H,Sq_max,D), k/v: (B,H,Sk_max,D).
+
+    Batch b's true lengths are the differences of cu_seqlens.  Rows past a
+    true length are left as allocated (uninitialised unless ``out``/``lse``
+    are given).  Returns (o, lse (B,H,Sq_max) fp32).
+    """
+    lib = load_library()
+    _require_gpu(q, k, v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    cu_q = _device_cu(cu_seqlens_q, q.device, B * Sq, Sq, check)
+    cu_k = _device_cu(cu_seqlens_k, q.device, B * Sk, Sk, check)
+    if cu_q.numel() != B + 1 or cu_k.numel() != B + 1:
+        raise ValueError("padded varlen needs B + 1 cu_seqlens entries")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.attn_fwd_padded_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        _dtype_code(q), B, H, Sq, Sk, D, cu_q.data_ptr(), cu_k.data_ptr(),
+        _strides(q), _strides(k), _strides(v), _strides(o),
+        _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    return o, lse

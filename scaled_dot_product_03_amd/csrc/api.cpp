@@ -1,0 +1,267 @@
+// C-ABI entry points of libsdpa03.so: argument validation on the host, then
+// one kernel launch.  The declarations and the contract are in sdpa03.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sdpa03.h"
+#include "fwd_args.h"
+
+namespace {
+
+using sdpa03::FwdArgs;
+
+constexpr int64_t kMaxGrid = (int64_t(1) << 32) / 256 - 1;  // workgroups per launch
+
+int elem_size(sdpa_dtype dt) { return dt == SDPA_F32 ? 4 : 2; }
+
+bool dtype_ok(int dt) { return dt == SDPA_F32 || dt == SDPA_F16 || dt == SDPA_BF16; }
+
+// One rank-4 view: (batch, head, seq, dim) sizes and element strides.
+struct View {
+  const void* ptr;
+  int64_t size[4];
+  const int64_t* stride;
+};
+
+// Largest element offset the view can reach, or -1 on overflow.
+int64_t max_offset(const View& v) {
+  int64_t off = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (v.size[i] == 0) return 0;
+    const int64_t span = v.size[i] - 1;
+    if (v.stride[i] != 0 && span > INT64_MAX / 4 / v.stride[i]) return -1;
+    off += span * v.stride[i];
+    if (off > INT64_MAX / 4) return -1;
+  }
+  return off;
+}
+
+sdpa_status check_view(const View& v, int esize) {
+  if (v.stride == nullptr) return SDPA_ERR_NULL;
+  if (v.stride[3] != 1) return SDPA_ERR_STRIDE;
+  for (int i = 0; i < 3; ++i) {
+    if (v.stride[i] < 0) return SDPA_ERR_STRIDE;
+    if ((v.stride[i] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
+  }
+  if (reinterpret_cast<uintptr_t>(v.ptr) % 16 != 0) return SDPA_ERR_ALIGN;
+  if (max_offset(v) < 0) return SDPA_ERR_STRIDE;
+  return SDPA_OK;
+}
+
+// Shared checks of dtype, head_dim and scale.
+sdpa_status check_common(int dtype, int32_t head_dim, float scale) {
+  if (!dtype_ok(dtype)) return SDPA_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return SDPA_ERR_HEAD_DIM;
+  if (!(isfinite(scale) && scale > 0.f)) return SDPA_ERR_SCALE;
+  return SDPA_OK;
+}
+
+sdpa_status check_pointers(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse) {
+  if (!q || !k || !v || !o || !lse) return SDPA_ERR_NULL;
+  return SDPA_OK;
+}
+
+void set_strides(const int64_t* s, int64_t& sb, int64_t& sh, int64_t& ss) {
+  sb = s[0];
+  sh = s[1];
+  ss = s[2];
+}
+
+sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, int mode,
+                              int32_t causal, void* stream) {
+  sdpa03::KernelConfig cfg;
+  if (!sdpa03::kernel_config(dtype, head_dim, causal != 0, mode, &cfg)) return SDPA_ERR_HEAD_DIM;
+  const int64_t m_tiles = (static_cast<int64_t>(a.seqlen_q) + cfg.block_m - 1) / cfg.block_m;
+  const int64_t grid = m_tiles * a.num_heads * static_cast<int64_t>(a.num_z);
+  if (grid > kMaxGrid) return SDPA_ERR_SHAPE;
+  if (grid == 0) return SDPA_OK;
+  a.m_tiles = static_cast<int32_t>(m_tiles);
+  const int err = sdpa03::launch_attn_fwd(a, dtype, head_dim, mode, causal != 0, stream);
+  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdpa_status_string(sdpa_status status) {
+  switch (status) {
+    case SDPA_OK: return "ok";
+    case SDPA_ERR_NULL: return "a required pointer is NULL";
+    case SDPA_ERR_DTYPE: return "unsupported dtype (expected fp32, fp16 or bf16)";
+    case SDPA_ERR_HEAD_DIM: return "unsupported head_dim (expected 64 or 128)";
+    case SDPA_ERR_SHAPE: return "invalid or too large sizes";
+    case SDPA_ERR_STRIDE: return "invalid strides (dim stride must be 1, no negative or overflowing strides)";
+    case SDPA_ERR_ALIGN: return "base pointers and strides must be 16-byte aligned";
+    case SDPA_ERR_BATCH: return "compact varlen needs batch size exactly 1";
+    case SDPA_ERR_SEQLEN: return "invalid sequence-length arguments";
+    case SDPA_ERR_SCALE: return "scale must be finite and positive";
+    case SDPA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+  }
+  return "unknown status";
+}
+
+sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t total,
+                                       int32_t max_len) {
+  if (cu == nullptr) return SDPA_ERR_NULL;
+  if (n < 0 || total < 0 || max_len < 0) return SDPA_ERR_SEQLEN;
+  if (cu[0] != 0) return SDPA_ERR_SEQLEN;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = static_cast<int64_t>(cu[i + 1]) - cu[i];
+    if (len < 0 || len > max_len) return SDPA_ERR_SEQLEN;
+  }
+  if (cu[n] > total) return SDPA_ERR_SEQLEN;
+  return SDPA_OK;
+}
+
+sdpa_status sdpa_kernel_config(sdpa_dtype dtype, int32_t head_dim, int32_t causal, int32_t mode,
+                               int32_t* block_m, int32_t* block_n, int32_t* waves) {
+  if (!dtype_ok(dtype)) return SDPA_ERR_DTYPE;
+  if (mode < 0 || mode > 2) return SDPA_ERR_SHAPE;
+  sdpa03::KernelConfig cfg;
+  if (!sdpa03::kernel_config(dtype, head_dim, causal != 0, mode, &cfg)) return SDPA_ERR_HEAD_DIM;
+  if (block_m) *block_m = cfg.block_m;
+  if (block_n) *block_n = cfg.block_n;
+  if (waves) *waves = cfg.waves;
+  return SDPA_OK;
+}
+
+sdpa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                     int32_t seqlen_k, int32_t head_dim, const int64_t q_stride[4],
+                     const int64_t k_stride[4], const int64_t v_stride[4],
+                     const int64_t o_stride[4], float scale, int32_t causal, void* hip_stream) {
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H * seqlen_q == 0) return SDPA_OK;
+  if ((st = check_pointers(q, k, v, o, lse)) != SDPA_OK) return st;
+  const int es = elem_size(dtype);
+  const View vq{q, {B, H, seqlen_q, head_dim}, q_stride};
+  const View vk{k, {B, H, seqlen_k, head_dim}, k_stride};
+  const View vv{v, {B, H, seqlen_k, head_dim}, v_stride};
+  const View vo{o, {B, H, seqlen_q, head_dim}, o_stride};
+  for (const View* vw : {&vq, &vk, &vv, &vo}) {
+    if ((st = check_view(*vw, es)) != SDPA_OK) return st;
+  }
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.cu_q = nullptr; a.cu_k = nullptr;
+  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
+  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
+  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
+  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
+  a.lse_sh = seqlen_q;
+  a.lse_sb = static_cast<int64_t>(H) * seqlen_q;
+  a.seqlen_q = seqlen_q;
+  a.seqlen_k = seqlen_k;
+  a.total_q = seqlen_q;
+  a.total_k = seqlen_k;
+  a.num_heads = H;
+  a.num_z = B;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_DENSE, causal, hip_stream);
+}
+
+sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                                    int32_t total_q, int32_t total_k, int32_t head_dim,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t num_seqs, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k, const int64_t q_stride[4],
+                                    const int64_t k_stride[4], const int64_t v_stride[4],
+                                    const int64_t o_stride[4], float scale, int32_t causal,
+                                    void* hip_stream) {
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (B != 1) return SDPA_ERR_BATCH;
+  if (H < 0 || total_q < 0 || total_k < 0) return SDPA_ERR_SHAPE;
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > total_q ||
+      max_seqlen_k > total_k)
+    return SDPA_ERR_SEQLEN;
+  if (static_cast<int64_t>(H) * num_seqs * max_seqlen_q == 0) return SDPA_OK;
+  if ((st = check_pointers(q, k, v, o, lse)) != SDPA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
+  const int es = elem_size(dtype);
+  const View vq{q, {1, H, total_q, head_dim}, q_stride};
+  const View vk{k, {1, H, total_k, head_dim}, k_stride};
+  const View vv{v, {1, H, total_k, head_dim}, v_stride};
+  const View vo{o, {1, H, total_q, head_dim}, o_stride};
+  for (const View* vw : {&vq, &vk, &vv, &vo}) {
+    if ((st = check_view(*vw, es)) != SDPA_OK) return st;
+  }
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
+    return SDPA_ERR_ALIGN;
+
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
+  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
+  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
+  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
+  a.lse_sh = total_q;
+  a.lse_sb = static_cast<int64_t>(H) * total_q;
+  a.seqlen_q = max_seqlen_q;
+  a.seqlen_k = max_seqlen_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.num_heads = H;
+  a.num_z = num_seqs;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_COMPACT, causal, hip_stream);
+}
+
+sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                                   int32_t seqlen_q_max, int32_t seqlen_k_max,
+                                   int32_t head_dim, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, const int64_t q_stride[4],
+                                   const int64_t k_stride[4], const int64_t v_stride[4],
+                                   const int64_t o_stride[4], float scale, int32_t causal,
+                                   void* hip_stream) {
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (B < 0 || H < 0 || seqlen_q_max < 0 || seqlen_k_max < 0) return SDPA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H * seqlen_q_max == 0) return SDPA_OK;
+  if ((st = check_pointers(q, k, v, o, lse)) != SDPA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
+  const int es = elem_size(dtype);
+  const View vq{q, {B, H, seqlen_q_max, head_dim}, q_stride};
+  const View vk{k, {B, H, seqlen_k_max, head_dim}, k_stride};
+  const View vv{v, {B, H, seqlen_k_max, head_dim}, v_stride};
+  const View vo{o, {B, H, seqlen_q_max, head_dim}, o_stride};
+  for (const View* vw : {&vq, &vk, &vv, &vo}) {
+    if ((st = check_view(*vw, es)) != SDPA_OK) return st;
+  }
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
+    return SDPA_ERR_ALIGN;
+
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
+  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
+  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
+  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
+  a.lse_sh = seqlen_q_max;
+  a.lse_sb = static_cast<int64_t>(H) * seqlen_q_max;
+  a.seqlen_q = seqlen_q_max;
+  a.seqlen_k = seqlen_k_max;
+  a.total_q = seqlen_q_max;
+  a.total_k = seqlen_k_max;
+  a.num_heads = H;
+  a.num_z = B;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_PADDED, causal, hip_stream);
+}
+
+}  // extern "C"

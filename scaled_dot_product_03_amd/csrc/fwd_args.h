@@ -1,0 +1,51 @@
+// Internal kernel arguments of the attention forward (not part of the C ABI).
+#pragma once
+
+#include <stdint.h>
+
+namespace sdpa03 {
+
+enum Mode : int { MODE_DENSE = 0, MODE_COMPACT = 1, MODE_PADDED = 2 };
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// Everything a workgroup needs, passed by value in the kernel-argument
+// segment.  Strides are in elements; lse rows are contiguous.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_q;  // device cu_seqlens (varlen modes), else nullptr
+  const int32_t* cu_k;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t lse_sb, lse_sh;
+  int32_t seqlen_q;   // dense: Sq; compact: max_seqlen_q; padded: Sq_max
+  int32_t seqlen_k;   // dense: Sk; compact: max_seqlen_k; padded: Sk_max
+  int32_t total_q;    // rows addressable along seq: compact total_q, else seqlen_q
+  int32_t total_k;    // likewise for keys
+  int32_t num_heads;
+  int32_t num_z;      // batches (dense, padded) or sequences (compact)
+  int32_t m_tiles;    // ceil(seqlen_q / block_m)
+  float scale_log2;   // scale * log2(e): scores go straight into exp2
+};
+
+// One compiled kernel shape.
+struct KernelConfig {
+  int block_m;
+  int block_n;
+  int waves;
+};
+
+// Picks the compiled kernel for a problem class; false if unsupported.
+bool kernel_config(int dtype, int head_dim, bool causal, int mode, KernelConfig* cfg);
+
+// Launches the forward on `stream` (a hipStream_t).  Returns the HIP error
+// code of the launch (0 on success).  Arguments are assumed validated.
+int launch_attn_fwd(const FwdArgs& args, int dtype, int head_dim, int mode, bool causal,
+                    void* stream);
+
+}  // namespace sdpa03

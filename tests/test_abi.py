@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side validation returns the documented status codes.
+
+No test here launches a kernel.  Error-path calls carry dummy (non-null,
+never dereferenced) device pointers plus at least one invalid argument, so
+validation rejects them before any HIP call; they are skipped on a machine
+with a visible GPU, where the GPU tests exercise the same paths with real
+device buffers.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_03_amd import binding
+from scaled_dot_product_03_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa03.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libsdpa03.so not built")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="dummy-pointer validation tests run only without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_fwd_compact_varlen", "attn_fwd_padded_varlen", "sdpa_status_string"):
+        assert n in names
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = binding.load_library()
+    for code in range(0, 11):
+        s = lib.sdpa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.sdpa_status_string(123).decode() == "unknown status"
+
+
+def test_kernel_config_table():
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        for d in (64, 128):
+            bm, bn, w = binding.kernel_config(dt, d)
+            assert bm == 32 * w and bn % 32 == 0 and bm > 0
+    with pytest.raises(binding.SdpaError) as e:
+        binding.kernel_config(torch.float16, 96)
+    assert e.value.status == 3
+    with pytest.raises(binding.SdpaError) as e:
+        binding.kernel_config(torch.float64, 64)
+    assert e.value.status == 2
+
+
+def test_host_cu_seqlens_check():
+    binding.check_cu_seqlens_host([0, 3, 3, 10], total=10, max_len=7)
+    bad = [([1, 3], 10, 5), ([0, 5, 4], 10, 5), ([0, 5, 11], 11, 5), ([0, 5, 12], 11, 7)]
+    for cu, total, mx in bad:
+        with pytest.raises(binding.SdpaError) as e:
+            binding.check_cu_seqlens_host(cu, total, mx)
+        assert e.value.status == 8
+
+
+# --- validation with dummy pointers (never dereferenced) --------------------
+
+DUMMY = 0x7F0000000000  # 16-byte aligned, never touched
+
+
+def _st(*s):
+    return (ctypes.c_int64 * 4)(*s)
+
+
+def _dense(**kw):
+    lib = binding.load_library()
+    a = dict(q=DUMMY, k=DUMMY, v=DUMMY, o=DUMMY, lse=DUMMY, dtype=2, B=1, H=2, Sq=8, Sk=8, D=64,
+             qs=_st(1024, 512, 64, 1), ks=_st(1024, 512, 64, 1), vs=_st(1024, 512, 64, 1),
+             os_=_st(1024, 512, 64, 1), scale=0.125, causal=0)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dtype"], a["B"], a["H"],
+                        a["Sq"], a["Sk"], a["D"], a["qs"], a["ks"], a["vs"], a["os_"],
+                        a["scale"], a["causal"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(dtype=7), 2), (dict(D=96), 3), (dict(D=256), 3),
+    (dict(B=-1), 4), (dict(Sk=-3), 4), (dict(qs=_st(1024, 512, 64, 2)), 5),
+    (dict(ks=_st(1024, -512, 64, 1)), 5), (dict(vs=_st(1024, 512, 60, 1)), 6),
+    (dict(o=DUMMY + 8), 6), (dict(scale=0.0), 9), (dict(scale=float("nan")), 9),
+    (dict(scale=-1.0), 9), (dict(scale=float("inf")), 9),
+    (dict(qs=_st(2 ** 61, 512, 64, 1), B=8), 5),
+])
+def test_dense_validation(kw, status):
+    assert _dense(**kw) == status
+
+
+@no_gpu
+def test_empty_problem_is_ok_without_launch():
+    # no query rows: nothing to launch, pointers are not even needed
+    assert _dense(q=None, k=None, v=None, o=None, lse=None, Sq=0) == 0
+    assert _dense(q=None, B=0) == 0
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=2), 7), (dict(B=0), 7), (dict(cu_q=None), 1), (dict(num_seqs=-1), 8),
+    (dict(max_q=-1), 8), (dict(max_q=100), 8), (dict(D=32), 3),
+    (dict(qs=_st(64 * 2 * 64, 64, 124, 1)), 6),
+])
+def test_compact_validation(kw, status):
+    lib = binding.load_library()
+    a = dict(B=1, H=2, Tq=64, Tk=64, D=64, cu_q=DUMMY, cu_k=DUMMY, num_seqs=3, max_q=40, max_k=40,
+             qs=_st(64 * 2 * 64, 64, 128, 1), scale=0.125)
+    a.update(kw)
+    st = _st(64 * 2 * 64, 64, 128, 1)
+    r = lib.attn_fwd_compact_varlen(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, a["B"], a["H"], a["Tq"],
+                                    a["Tk"], a["D"], a["cu_q"], a["cu_k"], a["num_seqs"],
+                                    a["max_q"], a["max_k"], a["qs"], st, st, st, a["scale"], 1,
+                                    None)
+    assert r == status
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_k=None), 1), (dict(B=-2), 4), (dict(dtype=-1), 2), (dict(cu_q=DUMMY + 2), 6),
+])
+def test_padded_validation(kw, status):
+    lib = binding.load_library()
+    a = dict(B=2, dtype=1, cu_q=DUMMY, cu_k=DUMMY)
+    a.update(kw)
+    st = _st(2 * 32 * 64, 32 * 64, 64, 1)
+    r = lib.attn_fwd_padded_varlen(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, a["dtype"], a["B"], 2, 32,
+                                   32, 64, a["cu_q"], a["cu_k"], st, st, st, st, 0.125, 0, None)
+    assert r == status

@@ -1,0 +1,372 @@
+"""GPU parity: the HIP library against the float64 oracle on seeded inputs.
+
+Small and ragged shapes are compared element by element over every output;
+the five named workloads at their full sizes are compared on sampled rows
+(the oracle computes those rows one by one) and checked for properties that
+hold at any size.  Bookkeeping (which rows are written, which keys are read)
+is checked bit-exactly.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_head, sdpa_compact_varlen, sdpa_dense, sdpa_padded_varlen
+from parity import check, sample_rows, to64
+from scaled_dot_product_03_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(x):
+    return x.to(DEV)
+
+
+# ---------------------------------------------------------------------------
+# Small and ragged dense shapes: every output element
+# ---------------------------------------------------------------------------
+
+SMALL_DENSE = [
+    # B, H, Sq, Sk, D, dtype
+    (1, 2, 128, 128, 64, "fp32"),
+    (2, 3, 1, 1, 64, "bf16"),
+    (1, 2, 127, 129, 128, "bf16"),
+    (2, 2, 129, 127, 64, "fp16"),
+    (1, 3, 200, 451, 128, "fp16"),
+    (1, 2, 257, 64, 128, "fp32"),
+    (2, 1, 64, 300, 64, "fp32"),
+    (1, 1, 384, 384, 128, "bf16"),
+    (1, 2, 33, 1000, 64, "bf16"),
+    (1, 1, 1000, 33, 128, "fp16"),
+    (1, 1, 65, 2, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL_DENSE, ids=lambda s: "x".join(map(str, s)))
+def test_dense_small(shape, causal):
+    B, H, Sq, Sk, D, dt = shape
+    _log(f"dense {shape} causal={causal}")
+    x = inputs.dense_inputs(B, H, Sq, Sk, D, dt, seed=100 + Sq + Sk + D)
+    o, lse = binding.attn_fwd(_dev(x.q), _dev(x.k), _dev(x.v), scale=x.scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_dense(to64(x.q), to64(x.k), to64(x.v), x.scale, causal)
+    check(to64(o), to64(lse), ro, rl, dt, label=f"{shape} causal={causal}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_dense_strided_bshd_view_and_custom_scale(dt):
+    """Q/K/V/O passed as BHSD views of BSHD memory, scale != 1/sqrt(D)."""
+    _log(f"strided {dt}")
+    B, S, H, D = 2, 190, 3, 64
+    rng = np.random.default_rng(77)
+    mk = lambda: torch.from_numpy(rng.standard_normal((B, S, H, D), dtype=np.float32)).to(
+        inputs.DTYPES[dt])
+    q, k, v = mk(), mk(), mk()
+    qd, kd, vd = (_dev(t).transpose(1, 2) for t in (q, k, v))
+    out = torch.empty((B, S, H, D), dtype=qd.dtype, device=DEV).transpose(1, 2)
+    o, lse = binding.attn_fwd(qd, kd, vd, scale=0.3, causal=True, out=out)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_dense(to64(q.transpose(1, 2)), to64(k.transpose(1, 2)), to64(v.transpose(1, 2)),
+                        float(np.float32(0.3)), True)
+    check(to64(o), to64(lse), ro, rl, dt, label=f"strided {dt}")
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------
+
+def test_workload_tiny_fp32_full():
+    x = inputs.workload("tiny_dense_fp32_b1h2s128d64")
+    for causal in x.causal_modes:
+        _log(f"tiny fp32 causal={causal}")
+        o, lse = binding.attn_fwd(_dev(x.q), _dev(x.k), _dev(x.v), scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = sdpa_dense(to64(x.q), to64(x.k), to64(x.v), x.scale, causal)
+        check(to64(o), to64(lse), ro, rl, "fp32", label=f"tiny causal={causal}")
+
+
+def _dense_sampled(x, name, pairs, seeds_rows=0):
+    dt = x.dtype
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    rng = np.random.default_rng(seeds_rows)
+    for causal in x.causal_modes:
+        _log(f"{name} causal={causal}")
+        o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        if causal:
+            # row 0 sees key 0 only: weight exactly 1, so O[...,0,:] == V[...,0,:] bit-exactly
+            assert torch.equal(o[:, :, 0], v[:, :, 0])
+        go, gl, ro, rl = [], [], [], []
+        for b, h in pairs:
+            rows = sample_rows(x.q.shape[2], rng)
+            r_o, r_l = attention_head(to64(x.q[b, h]), to64(x.k[b, h]), to64(x.v[b, h]), x.scale,
+                                      causal, rows=rows)
+            go.append(to64(o[b, h, rows]))
+            gl.append(to64(lse[b, h, rows]))
+            ro.append(r_o)
+            rl.append(r_l)
+        stats = check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro),
+                      np.concatenate(rl), dt, label=f"{name} causal={causal}")
+        _log(f"  {stats}")
+
+
+def test_workload_dense_bf16_s2048_sampled():
+    x = inputs.workload("dense_bf16_b4h16s2048d128")
+    _dense_sampled(x, "dense bf16 B4H16S2048D128", [(0, 0), (1, 7), (2, 9), (3, 15)], 2)
+
+
+def test_workload_dense_fp16_sq512_sk8192_sampled():
+    x = inputs.workload("dense_fp16_b2h32sq512sk8192d64")
+    _dense_sampled(x, "dense fp16 B2H32 Sq512 Sk8192 D64", [(0, 0), (0, 31), (1, 16)], 3)
+
+
+def test_workload_compact_thd_sampled():
+    x = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
+    _log(f"compact THD lengths {x.meta['lengths_q']}")
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                             scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    cu = x.cu_seqlens_q
+    rng = np.random.default_rng(4)
+    go, gl, ro, rl = [], [], [], []
+    for z in range(len(cu) - 1):
+        s, e = int(cu[z]), int(cu[z + 1])
+        # first token of every sequence sees only itself: O == V bit-exactly
+        assert torch.equal(o[s], v[s])
+        for h in (z % 16, (5 * z + 3) % 16):
+            rows = sample_rows(e - s, rng, extra=6)
+            r_o, r_l = attention_head(to64(x.q[s:e, h]), to64(x.k[s:e, h]), to64(x.v[s:e, h]),
+                                      x.scale, True, rows=rows)
+            go.append(to64(o[s + rows, h]))
+            gl.append(to64(lse[0, h, s + rows]))
+            ro.append(r_o)
+            rl.append(r_l)
+    stats = check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl),
+                  "bf16", label="compact THD")
+    _log(f"  {stats}")
+
+
+def test_workload_padded_sampled():
+    x = inputs.workload("padded_bf16_b8h32smax8192d128_len2048to8192_causal")
+    _log(f"padded lengths {x.meta['lengths_q']}")
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    sentinel = float("nan")
+    o = torch.full_like(q, sentinel)
+    lse = torch.full((q.shape[0], q.shape[1], q.shape[2]), sentinel, device=DEV)
+    o, lse = binding.attn_fwd_padded_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                            scale=x.scale, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    lengths = x.meta["lengths_q"]
+    rng = np.random.default_rng(5)
+    go, gl, ro, rl = [], [], [], []
+    for b, L in enumerate(lengths):
+        # rows past the true length are left untouched, rows before it are written
+        assert torch.isnan(lse[b, :, L:]).all() and torch.isnan(o[b, :, L:]).all()
+        assert torch.isfinite(lse[b, :, :L]).all() and torch.isfinite(o[b, :, :L]).all()
+        for h in (b % 32, (7 * b + 5) % 32):
+            rows = sample_rows(L, rng, extra=6)
+            r_o, r_l = attention_head(to64(x.q[b, h, :L]), to64(x.k[b, h, :L]),
+                                      to64(x.v[b, h, :L]), x.scale, True, rows=rows)
+            go.append(to64(o[b, h, rows]))
+            gl.append(to64(lse[b, h, rows]))
+            ro.append(r_o)
+            rl.append(r_l)
+    stats = check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl),
+                  "bf16", label="padded")
+    _log(f"  {stats}")
+
+
+# ---------------------------------------------------------------------------
+# Variable-length modes at small sizes: every output element
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("fp32", 64), ("fp32", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_compact_small_full(dt, D, causal):
+    lengths_q = [1, 128, 129, 300, 0, 77, 255]
+    lengths_k = [1, 128, 129, 300, 5, 0, 400]
+    _log(f"compact small {dt} D{D} causal={causal}")
+    x = inputs.compact_inputs(len(lengths_q), 3, D, dt, seed=31, len_lo=1, len_hi=2,
+                              lengths_q=lengths_q, lengths_k=lengths_k, extra_tokens=5)
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 3, q.shape[0]), float("nan"), device=DEV)
+    binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k, scale=x.scale,
+                                    causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_compact_varlen(to64(x.q), to64(x.k), to64(x.v), x.cu_seqlens_q,
+                                 x.cu_seqlens_k, x.scale, causal)
+    t = int(x.cu_seqlens_q[-1])
+    # tokens past the last sequence are untouched
+    assert torch.isnan(o[t:]).all() and torch.isnan(lse[0, :, t:]).all()
+    check(to64(o[:t]), to64(lse[0, :, :t]), ro[:t], rl[:, :t], dt, label="compact small")
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("fp32", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_small_full(dt, D, causal):
+    B, H, Sq, Sk = 4, 2, 300, 270
+    lengths_q = [300, 1, 129, 0]
+    lengths_k = [270, 64, 1, 33]
+    _log(f"padded small {dt} D{D} causal={causal}")
+    x = inputs.padded_inputs(B, H, Sq, Sk, D, dt, seed=41, len_lo=1, len_hi=2,
+                             lengths_q=lengths_q, lengths_k=lengths_k)
+    # poison everything past the true lengths: it must never be read
+    q, k, v = x.q.clone(), x.k.clone(), x.v.clone()
+    for b in range(B):
+        q[b, :, lengths_q[b]:] = float("nan")
+        k[b, :, lengths_k[b]:] = float("inf")
+        v[b, :, lengths_k[b]:] = float("nan")
+    o = torch.full((B, H, Sq, D), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full((B, H, Sq), float("nan"), device=DEV)
+    binding.attn_fwd_padded_varlen(_dev(q), _dev(k), _dev(v), x.cu_seqlens_q, x.cu_seqlens_k,
+                                   scale=x.scale, causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_padded_varlen(to64(x.q), to64(x.k), to64(x.v), x.cu_seqlens_q, x.cu_seqlens_k,
+                                x.scale, causal)
+    for b in range(B):
+        L = lengths_q[b]
+        assert torch.isnan(o[b, :, L:]).all() and torch.isnan(lse[b, :, L:]).all()
+        if L:
+            check(to64(o[b, :, :L]), to64(lse[b, :, :L]), ro[b, :, :L], rl[b, :, :L], dt,
+                  label=f"padded small b={b}")
+
+
+# ---------------------------------------------------------------------------
+# Bookkeeping, bit-exact
+# ---------------------------------------------------------------------------
+
+def test_compact_no_cross_sequence_leak_bit_exact():
+    """V of sequence z is the one-hot vector e_z: any weight on another
+    sequence's keys would make another output column non-zero."""
+    lengths = [5, 130, 1, 257, 64, 63, 200]
+    H, D = 2, 64
+    x = inputs.compact_inputs(len(lengths), H, D, "bf16", seed=51, len_lo=1, len_hi=2,
+                              lengths_q=lengths, lengths_k=lengths)
+    v = torch.zeros_like(x.v)
+    cu = x.cu_seqlens_q
+    for z in range(len(lengths)):
+        v[cu[z]:cu[z + 1], :, z] = 1.0
+    for causal in (False, True):
+        o, _ = binding.attn_fwd_compact_varlen(_dev(x.q), _dev(x.k), _dev(v), cu, cu,
+                                               scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        o = o.cpu().float()
+        for z in range(len(lengths)):
+            blk = o[cu[z]:cu[z + 1]]
+            others = torch.cat([blk[..., :z], blk[..., z + 1:]], dim=-1)
+            assert torch.count_nonzero(others) == 0, f"sequence {z} leaked"
+            assert torch.allclose(blk[..., z], torch.ones_like(blk[..., z]), atol=1e-2)
+
+
+def test_padded_no_cross_batch_leak_bit_exact():
+    B, H, S, D = 3, 2, 200, 128
+    lengths = [200, 17, 129]
+    x = inputs.padded_inputs(B, H, S, S, D, "fp16", seed=52, len_lo=1, len_hi=2,
+                             lengths_q=lengths, lengths_k=lengths)
+    v = torch.zeros_like(x.v)
+    for b in range(B):
+        v[b, :, :, b] = 1.0
+        v[b, :, lengths[b]:, :] = 7.0  # padding keys: must carry no weight
+    o, _ = binding.attn_fwd_padded_varlen(_dev(x.q), _dev(x.k), _dev(v), x.cu_seqlens_q,
+                                          x.cu_seqlens_k, scale=x.scale, causal=False)
+    torch.cuda.synchronize()
+    o = o.cpu().float()
+    for b in range(B):
+        blk = o[b, :, : lengths[b]]
+        others = torch.cat([blk[..., :b], blk[..., b + 1:]], dim=-1)
+        assert torch.count_nonzero(others) == 0
+
+
+def test_deterministic_bitwise():
+    x = inputs.dense_inputs(2, 4, 300, 700, 128, "bf16", seed=61)
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    a = binding.attn_fwd(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = binding.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Degenerate inputs and errors with real device buffers
+# ---------------------------------------------------------------------------
+
+def test_no_keys_gives_zero_and_minus_inf():
+    x = inputs.dense_inputs(1, 2, 70, 1, 64, "bf16", seed=71)
+    q = _dev(x.q)
+    k = torch.empty((1, 2, 0, 64), dtype=q.dtype, device=DEV)
+    o, lse = binding.attn_fwd(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert (o == 0).all() and torch.isneginf(lse).all()
+
+
+def test_no_queries_is_a_noop():
+    q = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.randn((1, 2, 5, 64), device=DEV).bfloat16()
+    o, lse = binding.attn_fwd(q, k, k)
+    assert o.shape == (1, 2, 0, 64) and lse.shape == (1, 2, 0)
+
+
+@pytest.mark.parametrize("case", ["head_dim", "dtype", "batch", "stride", "scale"])
+def test_errors_leave_outputs_untouched(case):
+    q = torch.randn((2, 2, 16, 64), device=DEV).bfloat16()
+    o = torch.full_like(q, 3.0)
+    lse = torch.full((2, 2, 16), 5.0, device=DEV)
+    want = {"head_dim": 3, "dtype": 2, "batch": 7, "stride": 5, "scale": 9}[case]
+    with pytest.raises(binding.SdpaError) as e:
+        if case == "head_dim":
+            q96 = torch.randn((2, 2, 16, 96), device=DEV).bfloat16()
+            binding.attn_fwd(q96, q96, q96, out=torch.full_like(q96, 3.0), lse=lse)
+        elif case == "dtype":
+            q64 = q.double()
+            binding.attn_fwd(q64, q64, q64, out=o.double(), lse=lse)
+        elif case == "batch":
+            lib = binding.load_library()
+            st = binding._strides(q)
+            cu = torch.tensor([0, 16], dtype=torch.int32, device=DEV)
+            binding._check(lib.attn_fwd_compact_varlen(
+                q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(), 2, 2, 2,
+                16, 16, 64, cu.data_ptr(), cu.data_ptr(), 1, 16, 16, st, st, st, st, 0.125, 0,
+                None))
+        elif case == "stride":
+            wide = torch.randn((2, 2, 16, 128), device=DEV).bfloat16()[..., ::2]
+            binding.attn_fwd(wide, wide, wide, out=o, lse=lse)
+        else:
+            binding.attn_fwd(q, q, q, scale=-1.0, out=o, lse=lse)
+    assert e.value.status == want
+    torch.cuda.synchronize()
+    assert (o == 3.0).all() and (lse == 5.0).all()
+
+
+def test_native_library_is_loaded():
+    """The compute path is the in-tree HIP library, nothing else."""
+    from scaled_dot_product_03_amd.build import LIB_PATH
+    binding.load_library()
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert os.path.realpath(LIB_PATH) in maps or LIB_PATH in maps
