@@ -36,7 +36,9 @@
  *    attn_fwd constraints).
  *  - Base pointers must be 16-byte aligned and strides[0..2] times the
  *    element size must be multiples of 16 bytes (the kernels use 128-bit
- *    loads).
+ *    loads).  k and v may be NULL only when the key axis is empty
+ *    (seqlen_k, total_k or seqlen_k_max is 0); every other pointer is
+ *    required whenever there is a query row to produce.
  *  - lse is a contiguous fp32 array written for valid rows only.
  *  - Sequence-length arguments are int32, as the PR unifies them.
  *  - head_dim must be 64 or 128.  dtype is one of sdpa_dtype.

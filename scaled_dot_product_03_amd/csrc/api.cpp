@@ -39,6 +39,7 @@ int64_t max_offset(const View& v) {
 
 sdpa_status check_view(const View& v, int esize) {
   if (v.stride == nullptr) return SDPA_ERR_NULL;
+  if (v.ptr == nullptr) return SDPA_OK;  // empty tensor (checked by check_pointers)
   if (v.stride[3] != 1) return SDPA_ERR_STRIDE;
   for (int i = 0; i < 3; ++i) {
     if (v.stride[i] < 0) return SDPA_ERR_STRIDE;
@@ -57,9 +58,12 @@ sdpa_status check_common(int dtype, int32_t head_dim, float scale) {
   return SDPA_OK;
 }
 
+// q, o and lse are always required; k and v only when they hold any row
+// (an empty key axis is legal and its pointers are never dereferenced).
 sdpa_status check_pointers(const void* q, const void* k, const void* v, const void* o,
-                           const float* lse) {
-  if (!q || !k || !v || !o || !lse) return SDPA_ERR_NULL;
+                           const float* lse, int64_t key_rows) {
+  if (!q || !o || !lse) return SDPA_ERR_NULL;
+  if (key_rows > 0 && (!k || !v)) return SDPA_ERR_NULL;
   return SDPA_OK;
 }
 
@@ -137,7 +141,7 @@ sdpa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   if (st != SDPA_OK) return st;
   if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
   if (static_cast<int64_t>(B) * H * seqlen_q == 0) return SDPA_OK;
-  if ((st = check_pointers(q, k, v, o, lse)) != SDPA_OK) return st;
+  if ((st = check_pointers(q, k, v, o, lse, seqlen_k)) != SDPA_OK) return st;
   const int es = elem_size(dtype);
   const View vq{q, {B, H, seqlen_q, head_dim}, q_stride};
   const View vk{k, {B, H, seqlen_k, head_dim}, k_stride};
@@ -184,7 +188,7 @@ sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v,
       max_seqlen_k > total_k)
     return SDPA_ERR_SEQLEN;
   if (static_cast<int64_t>(H) * num_seqs * max_seqlen_q == 0) return SDPA_OK;
-  if ((st = check_pointers(q, k, v, o, lse)) != SDPA_OK) return st;
+  if ((st = check_pointers(q, k, v, o, lse, total_k)) != SDPA_OK) return st;
   if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
   const int es = elem_size(dtype);
   const View vq{q, {1, H, total_q, head_dim}, q_stride};
@@ -230,7 +234,7 @@ sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, 
   if (st != SDPA_OK) return st;
   if (B < 0 || H < 0 || seqlen_q_max < 0 || seqlen_k_max < 0) return SDPA_ERR_SHAPE;
   if (static_cast<int64_t>(B) * H * seqlen_q_max == 0) return SDPA_OK;
-  if ((st = check_pointers(q, k, v, o, lse)) != SDPA_OK) return st;
+  if ((st = check_pointers(q, k, v, o, lse, seqlen_k_max)) != SDPA_OK) return st;
   if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
   const int es = elem_size(dtype);
   const View vq{q, {B, H, seqlen_q_max, head_dim}, q_stride};

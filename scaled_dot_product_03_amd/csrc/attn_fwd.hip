@@ -130,10 +130,33 @@ struct Path16 {
     }
   }
 
-  // p[nb][r] is the weight of key 32nb + 16h + r for this lane's row.
+  // V rows keep their 16-byte chunks XOR-swizzled too, so that the
+  // transposing reads below (4 rows x 32 bytes per 16 lanes) hit distinct banks.
+  __device__ static __forceinline__ int v_swizzle(int r) {
+    if constexpr (kChunks == 16) {
+      return (r & 3) << 2;
+    } else {
+      return ((r >> 1) & 1) << 2;
+    }
+  }
+
+  // O^T += V^T P^T.  p[nb][r] is the weight of key 32nb + 16h + r for this
+  // lane's row, so the B operand of k-step (nb, half) is p[nb][8half ..+8].
+  // The A operand needs V[key .. key+7][d] (eight keys, one column d = the
+  // lane's li) -- a transposed access.  ds_read_b64_tr_b16 serves it: within
+  // each group of 16 lanes, lane i receives element (i & 3) of the 64-bit
+  // words read by lanes 4j + (i >> 2), j = 0..3.  If lane t of the group
+  // points at row R0 + t/4, column C0 + 4(t & 3), lane i therefore receives
+  // V[R0 + j][C0 + i] for j = 0..3: four consecutive keys of its own column.
+  // Two such reads (R0 and R0 + 4) give the eight keys of one operand.
   template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const T* v_tile, const f32x16 (&p)[NB], int li,
-                                            int lh, f32x16 (&acc)[DB]) {
+  __device__ static __forceinline__ void pv(const T* v_tile, const f32x16 (&p)[NB], int lane,
+                                            f32x16 (&acc)[DB]) {
+    using s16x4 = short __attribute__((ext_vector_type(4)));
+    const int t = lane & 15;
+    const int grp = lane >> 4;
+    const int row_lane = (grp >> 1) * 16 + (t >> 2);    // + 32nb + 8half + 4sub
+    const int col_lane = (grp & 1) * 16 + 4 * (t & 3);  // + 32db
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -141,12 +164,19 @@ struct Path16 {
         frag pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = static_cast<T>(p[nb][half * 8 + e]);
-        const T* vrow = v_tile + (nb * 32 + lh * 16 + half * 8) * D + li;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          frag vf;
+          s16x4 w[2];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = vrow[e * D + db * 32];
+          for (int sub = 0; sub < 2; ++sub) {
+            const int row = nb * 32 + half * 8 + sub * 4 + row_lane;
+            const int col = db * 32 + col_lane;
+            const T* src = v_tile + row * D + (((col >> 3) ^ v_swizzle(row)) << 3) + (col & 7);
+            w[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(src));
+          }
+          frag vf;
+          __builtin_memcpy(&vf, w, sizeof(vf));
           acc[db] = Mma16<T>::mma(vf, pf, acc[db]);
         }
       }
@@ -191,9 +221,16 @@ struct Path32 {
     }
   }
 
+  // V rows are stored unswizzled; each lane reads single fp32 elements.
+  __device__ static __forceinline__ int v_swizzle(int) { return 0; }
+
+  // O^T += V^T P^T with one key per k-step: lane (i, h) supplies p[nb][r]
+  // (key 32nb + 16h + r) and V[32nb + 16h + r][32db + i].
   template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const float* v_tile, const f32x16 (&p)[NB], int li,
-                                            int lh, f32x16 (&acc)[DB]) {
+  __device__ static __forceinline__ void pv(const float* v_tile, const f32x16 (&p)[NB], int lane,
+                                            f32x16 (&acc)[DB]) {
+    const int li = lane & 31;
+    const int lh = lane >> 5;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -249,7 +286,8 @@ struct SeqRange {
 // tokens [cu[z], cu[z+1]).  Padded: batch z, lengths cu[z+1] - cu[z] from
 // offset 0 (the padded branch of the fwd_kernel.py excerpt quoted in
 // AOTriton PR #31).  Ranges are clamped to the addressable rows so that
-// malformed cu_seqlens can never move an access out of bounds.
+// malformed cu_seqlens can never move an access out of bounds: compact
+// token ranges to [0, total), padded lengths to [0, padded length].
 template <int MODE>
 __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
   SeqRange r;
@@ -259,22 +297,24 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
     r.k_start = 0;
     r.len_q = a.seqlen_q;
     r.len_k = a.seqlen_k;
-  } else {
+  } else if constexpr (MODE == MODE_COMPACT) {
     const int q0 = min(max(a.cu_q[z], 0), a.total_q);
     const int q1 = min(max(a.cu_q[z + 1], q0), a.total_q);
     const int k0 = min(max(a.cu_k[z], 0), a.total_k);
     const int k1 = min(max(a.cu_k[z + 1], k0), a.total_k);
+    r.b = 0;
+    r.q_start = q0;
+    r.k_start = k0;
     r.len_q = min(q1 - q0, a.seqlen_q);
     r.len_k = min(k1 - k0, a.seqlen_k);
-    if constexpr (MODE == MODE_COMPACT) {
-      r.b = 0;
-      r.q_start = q0;
-      r.k_start = k0;
-    } else {
-      r.b = z;
-      r.q_start = 0;
-      r.k_start = 0;
-    }
+  } else {
+    const int64_t lq = static_cast<int64_t>(a.cu_q[z + 1]) - a.cu_q[z];
+    const int64_t lk = static_cast<int64_t>(a.cu_k[z + 1]) - a.cu_k[z];
+    r.b = z;
+    r.q_start = 0;
+    r.k_start = 0;
+    r.len_q = static_cast<int>(min(max(lq, int64_t(0)), static_cast<int64_t>(a.seqlen_q)));
+    r.len_k = static_cast<int>(min(max(lk, int64_t(0)), static_cast<int64_t>(a.seqlen_k)));
   }
   return r;
 }
@@ -284,7 +324,7 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 // ---------------------------------------------------------------------------
 
 template <typename T, int D, int NW, int BN, int MODE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   using Path = typename PathFor<T, D>::type;
   constexpr int BM = NW * 32;
   constexpr int NT = NW * 64;
@@ -365,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       const int r = id / NCH;
       const int ch = id % NCH;
       *reinterpret_cast<chunk_t*>(&k_lds[buf][r * D + (ch ^ chunk_swizzle<NCH>(r)) * EPC]) = k_stage[c];
-      *reinterpret_cast<chunk_t*>(&v_lds[buf][r * D + ch * EPC]) = v_stage[c];
+      *reinterpret_cast<chunk_t*>(&v_lds[buf][r * D + (ch ^ Path::v_swizzle(r)) * EPC]) = v_stage[c];
     }
   };
 
@@ -429,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
           l_run += p;
         }
       }
-      Path::template pv<NB, DB>(v_lds[buf], s, li, lh, acc);
+      Path::template pv<NB, DB>(v_lds[buf], s, lane, acc);
     }
 
     if (t + 1 < n_tiles) lds_store(buf ^ 1);

@@ -23,7 +23,8 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
     assert np.isfinite(o_gpu).all(), f"{label}: non-finite O"
     d = np.abs(o_gpu - o_ref)
     both_inf = np.isneginf(lse_gpu) & np.isneginf(lse_ref)
-    dl = np.where(both_inf, 0.0, np.abs(lse_gpu - lse_ref))
+    with np.errstate(invalid="ignore"):
+        dl = np.where(both_inf, 0.0, np.abs(lse_gpu - lse_ref))
     stats = dict(max_o=float(d.max(initial=0.0)), mean_o=float(d.mean()) if d.size else 0.0,
                  max_lse=float(dl.max(initial=0.0)))
     max_tol, mean_tol = O_TOL[dtype]
