@@ -20,7 +20,6 @@ Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -127,6 +126,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB (a kernel of "
+                         "known HBM traffic, for scaling counter readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the kernels are single-GPU; --gpus {args.gpus} "
@@ -162,6 +164,16 @@ def main():
         binding.attn_fwd(q, k, v, scale=x.scale, causal=True, out=o, lse=lse)
         if events is not None:
             events[2].record(stream)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read + {n} bytes written per launch, 3 launches")
+        del src, dst
 
     log(f"warmup {args.warmup} steps on {wl}")
     for _ in range(args.warmup):

@@ -30,7 +30,9 @@
  *  - Tensors are rank-4 views (batch, head, seq, dim) given as a device
  *    pointer and four strides counted in ELEMENTS (the rank-4 view with
  *    pointer plus sizes plus strides that the PR's TensorView<4> names).
- *    stride[3] (dim) must be 1.  Q, K, V and O share one dtype; K and V
+ *    stride[3] (dim) must be 1 and stride[2] (seq) at least head_dim (rows
+ *    do not overlap); K and V row strides are at most 16 MiB (the kernels
+ *    fetch K/V tiles with 32-bit buffer offsets).  Q, K, V and O share one dtype; K and V
  *    share their sizes; Q and O share their sizes; Q and K may differ only
  *    in sequence length (AOTriton issue #12, xinyazhang's reply on the
  *    attn_fwd constraints).

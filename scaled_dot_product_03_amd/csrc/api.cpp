@@ -37,10 +37,16 @@ int64_t max_offset(const View& v) {
   return off;
 }
 
-sdpa_status check_view(const View& v, int esize) {
+// K and V tiles are fetched with 32-bit buffer offsets of up to 64 rows:
+// their row stride is limited to 16 MiB.
+constexpr int64_t kMaxKvRowBytes = int64_t(1) << 24;
+
+sdpa_status check_view(const View& v, int esize, bool key_side) {
   if (v.stride == nullptr) return SDPA_ERR_NULL;
   if (v.ptr == nullptr) return SDPA_OK;  // empty tensor (checked by check_pointers)
   if (v.stride[3] != 1) return SDPA_ERR_STRIDE;
+  if (v.size[2] > 1 && v.stride[2] < v.size[3]) return SDPA_ERR_STRIDE;  // rows must not overlap
+  if (key_side && v.stride[2] * esize > kMaxKvRowBytes) return SDPA_ERR_STRIDE;
   for (int i = 0; i < 3; ++i) {
     if (v.stride[i] < 0) return SDPA_ERR_STRIDE;
     if ((v.stride[i] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
@@ -147,9 +153,9 @@ sdpa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   const View vk{k, {B, H, seqlen_k, head_dim}, k_stride};
   const View vv{v, {B, H, seqlen_k, head_dim}, v_stride};
   const View vo{o, {B, H, seqlen_q, head_dim}, o_stride};
-  for (const View* vw : {&vq, &vk, &vv, &vo}) {
-    if ((st = check_view(*vw, es)) != SDPA_OK) return st;
-  }
+  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
+      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
+    return st;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
 
   FwdArgs a{};
@@ -195,9 +201,9 @@ sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v,
   const View vk{k, {1, H, total_k, head_dim}, k_stride};
   const View vv{v, {1, H, total_k, head_dim}, v_stride};
   const View vo{o, {1, H, total_q, head_dim}, o_stride};
-  for (const View* vw : {&vq, &vk, &vv, &vo}) {
-    if ((st = check_view(*vw, es)) != SDPA_OK) return st;
-  }
+  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
+      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
+    return st;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
@@ -241,9 +247,9 @@ sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, 
   const View vk{k, {B, H, seqlen_k_max, head_dim}, k_stride};
   const View vv{v, {B, H, seqlen_k_max, head_dim}, v_stride};
   const View vo{o, {B, H, seqlen_q_max, head_dim}, o_stride};
-  for (const View* vw : {&vq, &vk, &vv, &vo}) {
-    if ((st = check_view(*vw, es)) != SDPA_OK) return st;
-  }
+  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
+      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
+    return st;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)

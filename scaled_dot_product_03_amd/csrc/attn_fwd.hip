@@ -2,15 +2,16 @@
 //
 // One workgroup computes block_m = 32 * waves query rows of one
 // (batch or sequence, head); each wavefront owns 32 rows.  The workgroup
-// walks the key axis in tiles of block_n keys: K and V tiles are copied from
-// HBM into LDS (double-buffered, 128-bit loads), every wave multiplies its Q
-// rows (held in VGPRs for the whole loop) against the K tile on the matrix
-// cores, folds the tile into a running max and running sum (online softmax),
-// and accumulates P.V on the matrix cores.  The score matrix never leaves
-// registers.  This is the forward pass behind the scaled-dot-product
-// attention node of nvFuser issue #2278 "Investigate a new SDPA IR node",
-// with the variable-length modes of AOTriton PR #31 "Add varlen support to
-// AOTriton's Flash Attention".
+// walks the key axis in tiles of block_n keys.  K and V tiles go from HBM
+// straight into LDS with buffer loads (double-buffered, no register
+// staging, rows past the sequence read back as zeros).  Every wave keeps its
+// Q rows in VGPRs for the whole loop, multiplies them against the K tile on
+// the matrix cores, folds the tile into a running max and running sum
+// (online softmax) and accumulates P.V on the matrix cores.  The score
+// matrix never leaves registers.  This is the forward pass behind the
+// scaled-dot-product attention node of nvFuser issue #2278 "Investigate a
+// new SDPA IR node", with the variable-length modes of AOTriton PR #31 "Add
+// varlen support to AOTriton's Flash Attention".
 //
 // Register layout.  The kernel computes S^T = K . Q^T and O^T = V^T . P^T
 // with v_mfma_f32_32x32x16_{bf16,f16} (v_mfma_f32_32x32x2_f32 for fp32
@@ -23,6 +24,11 @@
 // rho = 8*(r/4) + 4*(l/32) + r%4; K rows are loaded in the order
 // key_of(rho) = 16*(l/32) + r so that each half-wave holds 16 consecutive
 // keys of its query row.
+//
+// Software pipeline.  Iteration t turns the scores of tile t into
+// probabilities (VALU) while the matrix cores compute the scores of tile
+// t+1, then accumulates P(t).V(t) (matrix cores) while the VALU takes the row
+// max of tile t+1.  Tile t+2's K and tile t+1's V are in flight meanwhile.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -35,6 +41,7 @@ using f32x16 = float __attribute__((ext_vector_type(16)));
 using f32x4 = float __attribute__((ext_vector_type(4)));
 using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
 using f16x8 = _Float16 __attribute__((ext_vector_type(8)));
+using lds_void_ptr = __attribute__((address_space(3))) void*;
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
@@ -42,6 +49,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 // powers of two (a wave-uniform decision); until then exponents are taken
 // against the stale max, so p <= 2^8 and the fp32 sums stay exact enough.
 constexpr float kRescaleLog2 = 8.0f;
+// Fourth dword of a raw buffer descriptor on gfx9 (32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
 
 // Key index (within a 32-key block) loaded into accumulator row rho.
 __device__ __forceinline__ int key_of(int rho) {
@@ -69,11 +78,13 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // ---------------------------------------------------------------------------
 // Matrix-core paths.  Each provides: Q fragments held in registers, the
-// S^T = K Q^T product from a K tile in LDS, and O^T += V^T P^T from a V tile
-// in LDS.  Tiles in LDS are row-major [key][dim]; K rows have their 16-byte
-// chunks XOR-swizzled by chunk_swizzle(row).
+// S^T = K Q^T product from a K tile in LDS, the probabilities P of a score
+// tile, and O^T += V^T P^T from a V tile in LDS.  Tiles in LDS are row-major
+// [key][dim] with 16-byte chunks XOR-swizzled per row.
 // ---------------------------------------------------------------------------
 
 template <typename T>
@@ -95,15 +106,29 @@ struct Mma16<_Float16> {
   }
 };
 
+// Sum of the 16 floats of an accumulator as a balanced tree (short
+// dependency chains for the in-order VALU).
+__device__ __forceinline__ float tree_sum16(const float (&x)[16]) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+  float b0 = (a[0] + a[1]) + (a[2] + a[3]);
+  float b1 = (a[4] + a[5]) + (a[6] + a[7]);
+  return b0 + b1;
+}
+
 // bf16 / fp16: one 32x32x16 product per 16 elements of the contraction.
 template <typename T, int D>
 struct Path16 {
-  static constexpr int kElemsPerChunk = 8;
-  static constexpr int kChunks = D / 8;
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
   static constexpr int kQFrags = D / 16;
   using frag = typename Mma16<T>::frag;
   struct QRegs {
     frag f[kQFrags];
+  };
+  template <int NB>
+  struct PRegs {
+    frag f[NB][2];
   };
 
   // Q^T operand of k-step ks: lane (i, h) holds Q[i][16ks + 8h .. +8].
@@ -124,14 +149,15 @@ struct Path16 {
         const int r = nb * 32 + key_of(li);
         const int ch = 2 * ks + lh;
         const frag a = *reinterpret_cast<const frag*>(
-            k_tile + r * D + ((ch ^ chunk_swizzle<kChunks>(r)) * kElemsPerChunk));
+            k_tile + r * D + ((ch ^ chunk_swizzle<kChunks>(r)) * 8));
         s[nb] = Mma16<T>::mma(a, q.f[ks], s[nb]);
       }
     }
   }
 
   // V rows keep their 16-byte chunks XOR-swizzled too, so that the
-  // transposing reads below (4 rows x 32 bytes per 16 lanes) hit distinct banks.
+  // transposing reads in pv() (4 rows x 32 bytes per 16 lanes) hit distinct
+  // banks.
   __device__ static __forceinline__ int v_swizzle(int r) {
     if constexpr (kChunks == 16) {
       return (r & 3) << 2;
@@ -140,17 +166,39 @@ struct Path16 {
     }
   }
 
-  // O^T += V^T P^T.  p[nb][r] is the weight of key 32nb + 16h + r for this
-  // lane's row, so the B operand of k-step (nb, half) is p[nb][8half ..+8].
-  // The A operand needs V[key .. key+7][d] (eight keys, one column d = the
-  // lane's li) -- a transposed access.  ds_read_b64_tr_b16 serves it: within
-  // each group of 16 lanes, lane i receives element (i & 3) of the 64-bit
-  // words read by lanes 4j + (i >> 2), j = 0..3.  If lane t of the group
-  // points at row R0 + t/4, column C0 + 4(t & 3), lane i therefore receives
-  // V[R0 + j][C0 + i] for j = 0..3: four consecutive keys of its own column.
-  // Two such reads (R0 and R0 + 4) give the eight keys of one operand.
+  // p = 2^(s*c2 - m) for every score, rounded to T for the second product;
+  // returns this half-wave's fp32 sum of the tile's p.
+  template <int NB>
+  __device__ static __forceinline__ float softmax_p(const f32x16 (&s)[NB], float c2, float m_sub,
+                                                    PRegs<NB>& p) {
+    float tile_sum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(s[nb][r], c2, -m_sub));
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p.f[nb][half][e] = static_cast<T>(x[half * 8 + e]);
+      }
+      tile_sum += tree_sum16(x);
+    }
+    return tile_sum;
+  }
+
+  // O^T += V^T P^T.  p.f[nb][half] holds the weights of keys
+  // 32nb + 16h + 8half .. +8 for this lane's row (the B operand of one
+  // k-step).  The A operand needs V[key .. key+7][d] (eight keys, one column
+  // d = the lane's li) -- a transposed access.  ds_read_b64_tr_b16 serves it:
+  // within each group of 16 lanes, lane i receives element (i & 3) of the
+  // 64-bit words read by lanes 4j + (i >> 2), j = 0..3.  If lane t of the
+  // group points at row R0 + t/4, column C0 + 4(t & 3), lane i therefore
+  // receives V[R0 + j][C0 + i] for j = 0..3: four consecutive keys of its
+  // own column.  Two such reads (R0 and R0 + 4) give the eight keys of one
+  // operand.
   template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const T* v_tile, const f32x16 (&p)[NB], int lane,
+  __device__ static __forceinline__ void pv(const T* v_tile, const PRegs<NB>& p, int lane,
                                             f32x16 (&acc)[DB]) {
     using s16x4 = short __attribute__((ext_vector_type(4)));
     const int t = lane & 15;
@@ -161,9 +209,6 @@ struct Path16 {
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        frag pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = static_cast<T>(p[nb][half * 8 + e]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           s16x4 w[2];
@@ -177,7 +222,7 @@ struct Path16 {
           }
           frag vf;
           __builtin_memcpy(&vf, w, sizeof(vf));
-          acc[db] = Mma16<T>::mma(vf, pf, acc[db]);
+          acc[db] = Mma16<T>::mma(vf, p.f[nb][half], acc[db]);
         }
       }
     }
@@ -187,11 +232,14 @@ struct Path16 {
 // fp32: one 32x32x2 product per 2 elements of the contraction; P stays fp32.
 template <int D>
 struct Path32 {
-  static constexpr int kElemsPerChunk = 4;
   static constexpr int kChunks = D / 4;
   static constexpr int kGroups = D / 8;  // groups of 4 k-steps = 8 dims
   struct QRegs {
     f32x4 f[kGroups];
+  };
+  template <int NB>
+  struct PRegs {
+    f32x16 f[NB];
   };
 
   // k-step 4g + e covers dims 8g + e (lanes 0..31) and 8g + 4 + e (32..63).
@@ -212,7 +260,7 @@ struct Path32 {
         const int r = nb * 32 + key_of(li);
         const int ch = 2 * g + lh;
         const f32x4 a = *reinterpret_cast<const f32x4*>(
-            k_tile + r * D + ((ch ^ chunk_swizzle<kChunks>(r)) * kElemsPerChunk));
+            k_tile + r * D + ((ch ^ chunk_swizzle<kChunks>(r)) * 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           s[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q.f[g][e], s[nb], 0, 0, 0);
@@ -224,10 +272,27 @@ struct Path32 {
   // V rows are stored unswizzled; each lane reads single fp32 elements.
   __device__ static __forceinline__ int v_swizzle(int) { return 0; }
 
+  template <int NB>
+  __device__ static __forceinline__ float softmax_p(const f32x16 (&s)[NB], float c2, float m_sub,
+                                                    PRegs<NB>& p) {
+    float tile_sum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = __builtin_amdgcn_exp2f(fmaf(s[nb][r], c2, -m_sub));
+        p.f[nb][r] = x[r];
+      }
+      tile_sum += tree_sum16(x);
+    }
+    return tile_sum;
+  }
+
   // O^T += V^T P^T with one key per k-step: lane (i, h) supplies p[nb][r]
   // (key 32nb + 16h + r) and V[32nb + 16h + r][32db + i].
   template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const float* v_tile, const f32x16 (&p)[NB], int lane,
+  __device__ static __forceinline__ void pv(const float* v_tile, const PRegs<NB>& p, int lane,
                                             f32x16 (&acc)[DB]) {
     const int li = lane & 31;
     const int lh = lane >> 5;
@@ -238,7 +303,7 @@ struct Path32 {
         const float* vrow = v_tile + (nb * 32 + lh * 16 + r) * D + li;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[db * 32], p[nb][r], acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[db * 32], p.f[nb][r], acc[db], 0, 0, 0);
         }
       }
     }
@@ -252,6 +317,65 @@ struct PathFor {
 template <int D>
 struct PathFor<float, D> {
   using type = Path32<D>;
+};
+
+// ---------------------------------------------------------------------------
+// Tile copies: buffer loads straight into LDS
+// ---------------------------------------------------------------------------
+// buffer_load_dwordx4 ... lds writes lane L's 16 bytes to (wave-uniform LDS
+// base + 16 L): one instruction fills 1 KiB of LDS from 64 independent
+// source offsets.  A K or V tile is BN rows of D elements and each wave
+// issues its share of the tile's 1 KiB blocks.  The swizzled LDS layout
+// comes from choosing, for LDS position p of row r, the source chunk
+// p ^ swizzle(r).  The buffer descriptor starts at the tile's first row and
+// covers only the rows that exist, so rows past the sequence read back as
+// zeros with no bounds arithmetic.  Source offsets are 32-bit: the host
+// limits row strides accordingly.
+
+template <typename T, int D, int BN, int NW>
+struct TileCopy {
+  static constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
+  static constexpr int kRowsPerInst = 1024 / kRowBytes;
+  static constexpr int kInstPerTile = BN * kRowBytes / 1024;
+  static_assert(kInstPerTile % NW == 0, "tile copy must split evenly over the waves");
+  static constexpr int kInstPerWave = kInstPerTile / NW;
+  static constexpr int kChunks = kRowBytes / 16;
+
+  uint32_t voff[kInstPerWave];
+
+  // Source offsets of this lane's chunks; Path supplies the row swizzle of K
+  // (for_v false) or of V (for_v true).
+  template <typename Path, bool for_v>
+  __device__ __forceinline__ void init(int wave, int lane, int64_t row_bytes) {
+    const int lr = lane / kChunks;
+    const int lp = lane % kChunks;
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const int r = (wave * kInstPerWave + i) * kRowsPerInst + lr;
+      const int swz = for_v ? Path::v_swizzle(r) : chunk_swizzle<Path::kChunks>(r);
+      voff[i] = static_cast<uint32_t>(r * row_bytes) + static_cast<uint32_t>((lp ^ swz) << 4);
+    }
+  }
+
+  // Rows [0, valid_rows) of the tile starting at `tile` land in `lds_tile`.
+  __device__ __forceinline__ void issue(const char* tile, int64_t valid_rows, int64_t row_bytes,
+                                        T* lds_tile, int wave) const {
+    // hipcc's host (x86) pass parses this body too but has no buffer-resource
+    // type; left visible there, it stops the host pass from emitting the
+    // launch stubs of later kernel instantiations.
+#if defined(__HIP_DEVICE_COMPILE__)
+    int64_t bytes = valid_rows * row_bytes;
+    bytes = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tile), 0, static_cast<int>(static_cast<uint32_t>(bytes)), kBufferFlags);
+    char* lds = reinterpret_cast<char*>(lds_tile) + wave * kInstPerWave * 1024;
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds + i * 1024), 16, voff[i],
+                                               0, 0, 0);
+    }
+#endif
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -326,19 +450,20 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 template <typename T, int D, int NW, int BN, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   using Path = typename PathFor<T, D>::type;
+  using Copy = TileCopy<T, D, BN, NW>;
+  using PRegs = typename Path::template PRegs<BN / 32>;
   constexpr int BM = NW * 32;
-  constexpr int NT = NW * 64;
-  constexpr int EPC = Path::kElemsPerChunk;
-  constexpr int NCH = Path::kChunks;
-  constexpr int TILE_CHUNKS = BN * NCH;
-  static_assert(TILE_CHUNKS % NT == 0, "tile copy must split evenly over the workgroup");
-  constexpr int CPT = TILE_CHUNKS / NT;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
-  using chunk_t = f32x4;  // 16 bytes
 
-  __shared__ __attribute__((aligned(16))) T k_lds[2][BN * D];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][BN * D];
+  // Four separate LDS arrays (not one [2][...] array): each gets its own
+  // alias scope, so the compiler can see that fragment reads of one buffer do
+  // not depend on the buffer loads still landing in the other one, and need
+  // not wait for them.
+  __shared__ __attribute__((aligned(1024))) T k_lds0[BN * D];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[BN * D];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[BN * D];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[BN * D];
 
   int z, h, m;
   decode_tile(a.m_tiles, a.num_heads, z, h, m);
@@ -354,10 +479,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const T* qp = static_cast<const T*>(a.q) + sr.b * a.q_sb + h * a.q_sh +
                 static_cast<int64_t>(sr.q_start) * a.q_ss;
-  const T* kp = static_cast<const T*>(a.k) + sr.b * a.k_sb + h * a.k_sh +
-                static_cast<int64_t>(sr.k_start) * a.k_ss;
-  const T* vp = static_cast<const T*>(a.v) + sr.b * a.v_sb + h * a.v_sh +
-                static_cast<int64_t>(sr.k_start) * a.v_ss;
+  const char* kp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.k) + sr.b * a.k_sb + h * a.k_sh +
+      static_cast<int64_t>(sr.k_start) * a.k_ss);
+  const char* vp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.v) + sr.b * a.v_sb + h * a.v_sh +
+      static_cast<int64_t>(sr.k_start) * a.v_ss);
   T* op = static_cast<T*>(a.o) + sr.b * a.o_sb + h * a.o_sh +
           static_cast<int64_t>(sr.q_start) * a.o_ss;
   float* lsep = a.lse + sr.b * a.lse_sb + h * a.lse_sh + sr.q_start;
@@ -365,115 +492,126 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   const int row0 = m0 + wave * 32;  // first query row of this wave
   const int qi = row0 + li;         // this lane's query row
   const bool row_ok = qi < sr.len_q;
-  const bool wave_active = row0 < sr.len_q;
-  const int wave_last_row = min(row0 + 31, sr.len_q - 1);
-
-  typename Path::QRegs qr;
-  Path::load_q(qp + static_cast<int64_t>(qi) * a.q_ss, row_ok, lh, qr);
 
   int kend = sr.len_k;
   if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, sr.len_q));
   const int n_tiles = (kend + BN - 1) / BN;
+
+  const int64_t k_row_bytes = a.k_ss * static_cast<int64_t>(sizeof(T));
+  const int64_t v_row_bytes = a.v_ss * static_cast<int64_t>(sizeof(T));
+  Copy kcopy, vcopy;
+  kcopy.template init<Path, false>(wave, lane, k_row_bytes);
+  vcopy.template init<Path, true>(wave, lane, v_row_bytes);
+  // Tile t lives in buffer t & 1.  Every call below names its buffers
+  // directly (the loop is unrolled by two), so after inlining each LDS access
+  // refers to a known array.
+  auto issue_k = [&](int t, T* buf) {
+    const int j0 = t * BN;
+    kcopy.issue(kp + j0 * k_row_bytes, sr.len_k - j0, k_row_bytes, buf, wave);
+  };
+  auto issue_v = [&](int t, T* buf) {
+    const int j0 = t * BN;
+    vcopy.issue(vp + j0 * v_row_bytes, sr.len_k - j0, v_row_bytes, buf, wave);
+  };
+
+  typename Path::QRegs qr;
+  Path::load_q(qp + static_cast<int64_t>(qi) * a.q_ss, row_ok, lh, qr);
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = kNegInf;  // running max of scale*log2(e)*s, this row
   float l_run = 0.f;      // running sum of this half-wave's weights
-
-  chunk_t k_stage[CPT], v_stage[CPT];
-  auto global_load = [&](int j0) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int id = c * NT + tid;
-      const int r = id / NCH;
-      const int ch = id % NCH;
-      const int key = j0 + r;
-      if (key < sr.len_k) {
-        k_stage[c] = *reinterpret_cast<const chunk_t*>(kp + static_cast<int64_t>(key) * a.k_ss + ch * EPC);
-        v_stage[c] = *reinterpret_cast<const chunk_t*>(vp + static_cast<int64_t>(key) * a.v_ss + ch * EPC);
-      } else {
-        k_stage[c] = chunk_t{};
-        v_stage[c] = chunk_t{};
-      }
-    }
-  };
-  auto lds_store = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int id = c * NT + tid;
-      const int r = id / NCH;
-      const int ch = id % NCH;
-      *reinterpret_cast<chunk_t*>(&k_lds[buf][r * D + (ch ^ chunk_swizzle<NCH>(r)) * EPC]) = k_stage[c];
-      *reinterpret_cast<chunk_t*>(&v_lds[buf][r * D + (ch ^ Path::v_swizzle(r)) * EPC]) = v_stage[c];
-    }
-  };
-
-  if (n_tiles > 0) {
-    global_load(0);
-    lds_store(0);
-  }
-  __syncthreads();
-
+  float alpha = 1.f;      // pending rescale of acc and l (when rescale is set)
+  bool rescale = false;
   const float c2 = a.scale_log2;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+
+  // Scores of tile t (masked where needed) into s; k_tile holds K(t).
+  auto scores = [&](int t, const T* k_tile, f32x16 (&s)[NB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+    Path::template qk<NB>(k_tile, qr, li, lh, s);
     const int j0 = t * BN;
-    if (t + 1 < n_tiles) global_load(j0 + BN);
-
-    const bool skip = !wave_active || (CAUSAL && j0 > wave_last_row);
-    if (!skip) {
-      f32x16 s[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-      Path::template qk<NB>(k_lds[buf], qr, li, lh, s);
-
-      const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0);
-      if (need_mask) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + nb * 32 + lh * 16 + r;
-            const bool ok = key < sr.len_k && (!CAUSAL || key <= qi);
-            if (!ok) s[nb][r] = kNegInf;
-          }
-        }
-      }
-
-      float mx = kNegInf;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
-      }
-      mx = max_across_halves(mx) * c2;  // scale > 0, so max commutes with it
-
-      const bool grow = mx > m_run + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
-
+    const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0);
+    if (need_mask) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[nb][r], c2, -m_sub));
-          s[nb][r] = p;
-          l_run += p;
+          const int key = j0 + nb * 32 + lh * 16 + r;
+          const bool ok = key < sr.len_k && (!CAUSAL || key <= qi);
+          if (!ok) s[nb][r] = kNegInf;
         }
       }
-      Path::template pv<NB, DB>(v_lds[buf], s, lane, acc);
+    }
+  };
+  // Fold the row max of s into m_run; a growth beyond the threshold in any
+  // row of the wave schedules a rescale of acc and l.
+  auto update_max = [&](const f32x16 (&s)[NB]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+    }
+    mx = max_across_halves(mx) * c2;  // scale > 0, so max commutes with it
+    const bool grow = mx > m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      rescale = true;
+      m_run = m_new;
+    }
+  };
+
+  f32x16 s[NB];
+  if (n_tiles > 0) {
+    issue_k(0, k_lds0);
+    issue_v(0, v_lds0);
+    if (n_tiles > 1) issue_k(1, k_lds1);
+    wait_vmem();
+    __syncthreads();
+    scores(0, k_lds0, s);
+    update_max(s);
+    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
+  }
+
+  // One pipeline step for tile t: (k_cur, v_cur) are the buffers of parity
+  // t & 1 (K(t+2) and V(t) live there), (k_nxt, v_nxt) the other parity
+  // (K(t+1) and V(t+1)).
+  auto step = [&](int t, T* k_cur, T* v_cur, T* k_nxt, T* v_nxt) {
+    const bool has_next = t + 1 < n_tiles;
+    if (t + 2 < n_tiles) issue_k(t + 2, k_cur);
+    if (has_next) issue_v(t + 1, v_nxt);
+
+    if (rescale) {  // the max grew at tile t: bring acc and l to the new base
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      rescale = false;
+    }
+    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+
+    // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
+    PRegs p;
+    l_run += Path::template softmax_p<NB>(s, c2, m_sub, p);
+    f32x16 s_next[NB];
+    if (has_next) scores(t + 1, k_nxt, s_next);
+
+    // Phase B: O += P(t) V(t) (MFMA) || row max of tile t+1 (VALU).
+    Path::template pv<NB, DB>(v_cur, p, lane, acc);
+    if (has_next) {
+      update_max(s_next);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
     }
 
-    if (t + 1 < n_tiles) lds_store(buf ^ 1);
+    wait_vmem();
     __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (t + 1 < n_tiles) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.

@@ -101,10 +101,11 @@ def _dense(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(lse=None), 1), (dict(dtype=7), 2), (dict(D=96), 3), (dict(D=256), 3),
     (dict(B=-1), 4), (dict(Sk=-3), 4), (dict(qs=_st(1024, 512, 64, 2)), 5),
-    (dict(ks=_st(1024, -512, 64, 1)), 5), (dict(vs=_st(1024, 512, 60, 1)), 6),
+    (dict(ks=_st(1024, -512, 64, 1)), 5), (dict(vs=_st(1024, 512, 68, 1)), 6),
     (dict(o=DUMMY + 8), 6), (dict(scale=0.0), 9), (dict(scale=float("nan")), 9),
     (dict(scale=-1.0), 9), (dict(scale=float("inf")), 9),
     (dict(qs=_st(2 ** 61, 512, 64, 1), B=8), 5),
+    (dict(ks=_st(1024, 512, 32, 1)), 5), (dict(vs=_st(2 ** 26, 2 ** 25, 2 ** 24, 1)), 5),
 ])
 def test_dense_validation(kw, status):
     assert _dense(**kw) == status
