@@ -3,11 +3,11 @@
 // One workgroup computes block_m = 32 * waves query rows of one
 // (batch or sequence, head); each wavefront owns 32 rows.  The workgroup
 // walks the key axis in tiles of block_n keys.  K and V tiles go from HBM
-// straight into LDS with buffer loads (double-buffered, no register
+// straight into LDS with buffer loads (two or three LDS stages, no register
 // staging, rows past the sequence read back as zeros).  Every wave keeps its
 // Q rows in VGPRs for the whole loop, multiplies them against the K tile on
-// the matrix cores, folds the tile into a running max and running sum
-// (online softmax) and accumulates P.V on the matrix cores.  The score
+// the matrix cores, folds the tile into a running reference max and running
+// sum (online softmax) and accumulates P.V on the matrix cores.  The score
 // matrix never leaves registers.  This is the forward pass behind the
 // scaled-dot-product attention node of nvFuser issue #2278 "Investigate a
 // new SDPA IR node", with the variable-length modes of AOTriton PR #31 "Add
@@ -20,15 +20,20 @@
 // max, the row sum and the per-row rescale of O are in-lane, apart from one
 // v_permlane32_swap to combine the two half-waves (lanes l and l ^ 32 share
 // a row).  The accumulator of S^T therefore feeds the second product as its
-// B operand directly.  Accumulator register r of lane l holds row
-// rho = 8*(r/4) + 4*(l/32) + r%4; K rows are loaded in the order
-// key_of(rho) = 16*(l/32) + r so that each half-wave holds 16 consecutive
-// keys of its query row.
+// B operand directly.  Accumulator register r of lane l holds key
+// 8*(r/4) + 4*(l/32) + r%4 of its 32-key block.
 //
-// Software pipeline.  Iteration t turns the scores of tile t into
-// probabilities (VALU) while the matrix cores compute the scores of tile
-// t+1, then accumulates P(t).V(t) (matrix cores) while the VALU takes the row
-// max of tile t+1.  Tile t+2's K and tile t+1's V are in flight meanwhile.
+// LDS layout.  Tiles are row-major [key][dim] with padded rows, chosen for
+// gfx950's 64 banks of 4 bytes: the 16 consecutive K rows that one 128-bit
+// fragment read touches land in 16 distinct 16-byte bank groups, and the 4
+// V rows of one transposing read land in 4 distinct 64-byte bank blocks.
+// Padding (not an XOR swizzle) keeps every fragment address "one per-lane
+// base + an immediate offset", which saves dozens of address registers.
+//
+// Software pipeline.  Step t turns the scores of tile t into probabilities
+// (VALU) while the matrix cores compute the scores of tile t+1, then
+// accumulates P(t).V(t) on the matrix cores.  Later tiles' K and V are in
+// flight meanwhile.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -45,28 +50,23 @@ using lds_void_ptr = __attribute__((address_space(3))) void*;
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
-// O and l are rescaled only when a row max grows by more than this many
-// powers of two (a wave-uniform decision); until then exponents are taken
-// against the stale max, so p <= 2^8 and the fp32 sums stay exact enough.
-constexpr float kRescaleLog2 = 8.0f;
+// Exponents are taken against a stale reference max as long as each lane's
+// sum of a tile's weights stays at or below this bound (so no weight exceeds
+// it); a larger sum (a wave-uniform decision) triggers an exact max and a
+// rescale.
+constexpr float kSumLimit = 4096.0f;
 // Fourth dword of a raw buffer descriptor on gfx9 (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
 
-// Key index (within a 32-key block) loaded into accumulator row rho.
-__device__ __forceinline__ int key_of(int rho) {
-  return ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3);
-}
-
-// XOR swizzle of the 16-byte chunks of a K row in LDS, chosen so that the
-// 128-bit fragment reads of key_of() rows hit distinct banks.
-template <int NCH>
-__device__ __forceinline__ int chunk_swizzle(int r) {
-  if constexpr (NCH == 8) {
-    return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r >> 4) & 1) << 2);
-  } else {
-    return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3);
-  }
-}
+// LDS row strides (bytes) of K and V tiles for element size ES and head
+// dim D.  K: 16 bytes of padding per row shifts consecutive rows by one
+// 16-byte bank group.  V (16-bit): 64 bytes shift consecutive rows by a
+// quarter of the 256-byte bank cycle.  V (fp32): 32 bytes put rows r and
+// r+4, which one fp32 read pairs, in opposite halves of the banks.
+template <int ES, int D>
+constexpr int k_lds_row_bytes() { return D * ES + 16; }
+template <int ES, int D>
+constexpr int v_lds_row_bytes() { return ES == 2 ? D * ES + 64 : D * ES + 32; }
 
 __device__ __forceinline__ float max_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -79,6 +79,14 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory
+// loads are still in flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_allow() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
 
 // ---------------------------------------------------------------------------
 // Matrix-core paths.  Each provides: Q fragments held in registers, the
@@ -120,7 +128,6 @@ __device__ __forceinline__ float tree_sum16(const float (&x)[16]) {
 // bf16 / fp16: one 32x32x16 product per 16 elements of the contraction.
 template <typename T, int D>
 struct Path16 {
-  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
   static constexpr int kQFrags = D / 16;
   using frag = typename Mma16<T>::frag;
   struct QRegs {
@@ -139,35 +146,70 @@ struct Path16 {
     }
   }
 
+  static constexpr int kRowK = k_lds_row_bytes<2, D>();
+  static constexpr int kRowV = v_lds_row_bytes<2, D>();
+
+  // A operand of k-step ks: lane (rho, h) reads K[32nb + rho][16ks + 8h ..+8]
+  // -- rho is the lane's li, so the address is a per-lane base plus an
+  // immediate.
   template <int NB>
   __device__ static __forceinline__ void qk(const T* k_tile, const QRegs& q, int li, int lh,
                                             f32x16 (&s)[NB]) {
+    const char* base = reinterpret_cast<const char*>(k_tile) + li * kRowK + lh * 16;
 #pragma unroll
     for (int ks = 0; ks < kQFrags; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int r = nb * 32 + key_of(li);
-        const int ch = 2 * ks + lh;
-        const frag a = *reinterpret_cast<const frag*>(
-            k_tile + r * D + ((ch ^ chunk_swizzle<kChunks>(r)) * 8));
+        const frag a = *reinterpret_cast<const frag*>(base + nb * 32 * kRowK + ks * 32);
         s[nb] = Mma16<T>::mma(a, q.f[ks], s[nb]);
       }
     }
   }
 
-  // V rows keep their 16-byte chunks XOR-swizzled too, so that the
-  // transposing reads in pv() (4 rows x 32 bytes per 16 lanes) hit distinct
-  // banks.
-  __device__ static __forceinline__ int v_swizzle(int r) {
-    if constexpr (kChunks == 16) {
-      return (r & 3) << 2;
-    } else {
-      return ((r >> 1) & 1) << 2;
+  // An empty asm statement that takes the P fragments as operands: the
+  // compiler must have computed them at this point (it would otherwise sink
+  // the softmax past the masking branch that follows, next to its use).
+  template <int NB>
+  __device__ static __forceinline__ void pin(PRegs<NB>& p) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) asm volatile("" : "+v"(p.f[nb][half]));
+    }
+  }
+
+  // Scheduling requests for the two pipeline phases (sched_group_barrier
+  // masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU).  Phase A: keep a few K
+  // fragment reads ahead, then one MFMA, one read and a share of the softmax
+  // VALU work.  Phase B: two transposing V reads and a little VALU per MFMA.
+  template <int NB>
+  __device__ static __forceinline__ void interleave_qk() {
+    constexpr int n_mfma = NB * kQFrags;
+    constexpr int valu_per = (NB * 16 * 3 + n_mfma - 1) / n_mfma;
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int i = 0; i < n_mfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, valu_per, 0);
+    }
+  }
+  template <int NB, int DB>
+  __device__ static __forceinline__ void interleave_pv() {
+    constexpr int n_mfma = NB * 2 * DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < n_mfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
 
   // p = 2^(s*c2 - m) for every score, rounded to T for the second product;
-  // returns this half-wave's fp32 sum of the tile's p.
+  // returns this lane's fp32 sum of the unrounded p.  (A sum of the rounded
+  // weights would be cheaper -- v_dot2_f32_bf16 against (1, 1) -- but for rows
+  // that see only a few keys its rounding error reaches 2^-9 of l, which the
+  // logsumexp output cannot afford.)
   template <int NB>
   __device__ static __forceinline__ float softmax_p(const f32x16 (&s)[NB], float c2, float m_sub,
                                                     PRegs<NB>& p) {
@@ -187,24 +229,25 @@ struct Path16 {
     return tile_sum;
   }
 
-  // O^T += V^T P^T.  p.f[nb][half] holds the weights of keys
-  // 32nb + 16h + 8half .. +8 for this lane's row (the B operand of one
-  // k-step).  The A operand needs V[key .. key+7][d] (eight keys, one column
-  // d = the lane's li) -- a transposed access.  ds_read_b64_tr_b16 serves it:
-  // within each group of 16 lanes, lane i receives element (i & 3) of the
-  // 64-bit words read by lanes 4j + (i >> 2), j = 0..3.  If lane t of the
-  // group points at row R0 + t/4, column C0 + 4(t & 3), lane i therefore
-  // receives V[R0 + j][C0 + i] for j = 0..3: four consecutive keys of its
-  // own column.  Two such reads (R0 and R0 + 4) give the eight keys of one
-  // operand.
+  // O^T += V^T P^T.  Register r of lane (i, h) holds the weight of key
+  // 32nb + 8(r/4) + 4h + r%4, so k-step (nb, half) -- registers 8half..+8 --
+  // covers keys 32nb + 16half + {4h..4h+3, 8+4h..8+4h+3}, and its A operand
+  // needs V at those eight keys in the lane's column d = li: a transposed
+  // access.  ds_read_b64_tr_b16 serves it: within each group of 16 lanes,
+  // lane i receives element (i & 3) of the 64-bit words read by lanes
+  // 4j + (i >> 2), j = 0..3.  If lane t of the group points at row
+  // R0 + t/4, column C0 + 4(t & 3), lane i therefore receives V[R0 + j][C0 + i]
+  // for j = 0..3: four consecutive keys of its own column.  Two such reads
+  // (R0 = 32nb + 16half + 4h and R0 + 8) give the eight keys of one operand.
   template <int NB, int DB>
   __device__ static __forceinline__ void pv(const T* v_tile, const PRegs<NB>& p, int lane,
                                             f32x16 (&acc)[DB]) {
     using s16x4 = short __attribute__((ext_vector_type(4)));
     const int t = lane & 15;
     const int grp = lane >> 4;
-    const int row_lane = (grp >> 1) * 16 + (t >> 2);    // + 32nb + 8half + 4sub
-    const int col_lane = (grp & 1) * 16 + 4 * (t & 3);  // + 32db
+    const int row_lane = (grp >> 1) * 4 + (t >> 2);
+    const int col_lane = (grp & 1) * 16 + 4 * (t & 3);
+    const char* base = reinterpret_cast<const char*>(v_tile) + row_lane * kRowV + col_lane * 2;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -214,9 +257,7 @@ struct Path16 {
           s16x4 w[2];
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            const int row = nb * 32 + half * 8 + sub * 4 + row_lane;
-            const int col = db * 32 + col_lane;
-            const T* src = v_tile + row * D + (((col >> 3) ^ v_swizzle(row)) << 3) + (col & 7);
+            const char* src = base + (nb * 32 + half * 16 + sub * 8) * kRowV + db * 64;
             w[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(src));
           }
@@ -232,7 +273,6 @@ struct Path16 {
 // fp32: one 32x32x2 product per 2 elements of the contraction; P stays fp32.
 template <int D>
 struct Path32 {
-  static constexpr int kChunks = D / 4;
   static constexpr int kGroups = D / 8;  // groups of 4 k-steps = 8 dims
   struct QRegs {
     f32x4 f[kGroups];
@@ -250,17 +290,18 @@ struct Path32 {
     }
   }
 
+  static constexpr int kRowK = k_lds_row_bytes<4, D>();
+  static constexpr int kRowV = v_lds_row_bytes<4, D>();
+
   template <int NB>
   __device__ static __forceinline__ void qk(const float* k_tile, const QRegs& q, int li, int lh,
                                             f32x16 (&s)[NB]) {
+    const char* base = reinterpret_cast<const char*>(k_tile) + li * kRowK + lh * 16;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int r = nb * 32 + key_of(li);
-        const int ch = 2 * g + lh;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(
-            k_tile + r * D + ((ch ^ chunk_swizzle<kChunks>(r)) * 4));
+        const f32x4 a = *reinterpret_cast<const f32x4*>(base + nb * 32 * kRowK + g * 32);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           s[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q.f[g][e], s[nb], 0, 0, 0);
@@ -269,8 +310,14 @@ struct Path32 {
     }
   }
 
-  // V rows are stored unswizzled; each lane reads single fp32 elements.
-  __device__ static __forceinline__ int v_swizzle(int) { return 0; }
+  template <int NB>
+  __device__ static __forceinline__ void pin(PRegs<NB>&) {}
+
+  // fp32 is a correctness path: no scheduling requests.
+  template <int NB>
+  __device__ static __forceinline__ void interleave_qk() {}
+  template <int NB, int DB>
+  __device__ static __forceinline__ void interleave_pv() {}
 
   template <int NB>
   __device__ static __forceinline__ float softmax_p(const f32x16 (&s)[NB], float c2, float m_sub,
@@ -290,20 +337,22 @@ struct Path32 {
   }
 
   // O^T += V^T P^T with one key per k-step: lane (i, h) supplies p[nb][r]
-  // (key 32nb + 16h + r) and V[32nb + 16h + r][32db + i].
+  // (key 32nb + 8(r/4) + 4h + r%4) and V at that key in column 32db + i.
   template <int NB, int DB>
   __device__ static __forceinline__ void pv(const float* v_tile, const PRegs<NB>& p, int lane,
                                             f32x16 (&acc)[DB]) {
     const int li = lane & 31;
     const int lh = lane >> 5;
+    const char* base = reinterpret_cast<const char*>(v_tile) + lh * 4 * kRowV + li * 4;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float* vrow = v_tile + (nb * 32 + lh * 16 + r) * D + li;
+        const char* vrow = base + (nb * 32 + 8 * (r >> 2) + (r & 3)) * kRowV;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[db * 32], p.f[nb][r], acc[db], 0, 0, 0);
+          const float vv = *reinterpret_cast<const float*>(vrow + db * 128);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p.f[nb][r], acc[db], 0, 0, 0);
         }
       }
     }
@@ -323,56 +372,53 @@ struct PathFor<float, D> {
 // Tile copies: buffer loads straight into LDS
 // ---------------------------------------------------------------------------
 // buffer_load_dwordx4 ... lds writes lane L's 16 bytes to (wave-uniform LDS
-// base + 16 L): one instruction fills 1 KiB of LDS from 64 independent
-// source offsets.  A K or V tile is BN rows of D elements and each wave
-// issues its share of the tile's 1 KiB blocks.  The swizzled LDS layout
-// comes from choosing, for LDS position p of row r, the source chunk
-// p ^ swizzle(r).  The buffer descriptor starts at the tile's first row and
-// covers only the rows that exist, so rows past the sequence read back as
-// zeros with no bounds arithmetic.  Source offsets are 32-bit: the host
-// limits row strides accordingly.
+// base + 16 L): one instruction fills a 1 KiB block of LDS from 64
+// independent source offsets.  A tile of BN rows at LDS row stride ROW
+// occupies BN * ROW bytes; every wave issues the same number of blocks
+// (the last ones may lie past the tile, inside the array).  A lane whose
+// 16 bytes fall on row padding, or past the tile, gets an offset outside
+// the descriptor's range and writes zeros.  The descriptor starts at the
+// tile's first row and covers only the rows that exist, so rows past the
+// sequence read back as zeros too, with no bounds arithmetic in the loop.
+// Source offsets are 32-bit: the host limits row strides accordingly.
 
-template <typename T, int D, int BN, int NW>
+template <typename T, int D, int BN, int NW, int ROW>
 struct TileCopy {
-  static constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
-  static constexpr int kRowsPerInst = 1024 / kRowBytes;
-  static constexpr int kInstPerTile = BN * kRowBytes / 1024;
-  static_assert(kInstPerTile % NW == 0, "tile copy must split evenly over the waves");
-  static constexpr int kInstPerWave = kInstPerTile / NW;
-  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kDataBytes = D * static_cast<int>(sizeof(T));  // payload per row
+  static constexpr int kBlocks = (BN * ROW + 1023) / 1024;
+  static constexpr int kInstPerWave = (kBlocks + NW - 1) / NW;
+  static constexpr int kArrayBytes = kInstPerWave * NW * 1024;  // LDS array size per tile
+  static constexpr uint32_t kNowhere = 0x80000000u;  // past any descriptor range
 
   uint32_t voff[kInstPerWave];
 
-  // Source offsets of this lane's chunks; Path supplies the row swizzle of K
-  // (for_v false) or of V (for_v true).
-  template <typename Path, bool for_v>
   __device__ __forceinline__ void init(int wave, int lane, int64_t row_bytes) {
-    const int lr = lane / kChunks;
-    const int lp = lane % kChunks;
 #pragma unroll
     for (int i = 0; i < kInstPerWave; ++i) {
-      const int r = (wave * kInstPerWave + i) * kRowsPerInst + lr;
-      const int swz = for_v ? Path::v_swizzle(r) : chunk_swizzle<Path::kChunks>(r);
-      voff[i] = static_cast<uint32_t>(r * row_bytes) + static_cast<uint32_t>((lp ^ swz) << 4);
+      const int pos = (i * NW + wave) * 1024 + lane * 16;
+      const int r = pos / ROW;
+      const int col = pos % ROW;
+      const bool data = r < BN && col < kDataBytes;
+      voff[i] = data ? static_cast<uint32_t>(r * row_bytes) + static_cast<uint32_t>(col) : kNowhere;
     }
   }
 
   // Rows [0, valid_rows) of the tile starting at `tile` land in `lds_tile`.
-  __device__ __forceinline__ void issue(const char* tile, int64_t valid_rows, int64_t row_bytes,
+  __device__ __forceinline__ void issue(const char* tile, int valid_rows, int64_t row_bytes,
                                         T* lds_tile, int wave) const {
     // hipcc's host (x86) pass parses this body too but has no buffer-resource
     // type; left visible there, it stops the host pass from emitting the
     // launch stubs of later kernel instantiations.
 #if defined(__HIP_DEVICE_COMPILE__)
-    int64_t bytes = valid_rows * row_bytes;
-    bytes = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+    const int rows = valid_rows < 0 ? 0 : (valid_rows > BN ? BN : valid_rows);
+    const uint32_t bytes = static_cast<uint32_t>(rows * row_bytes);  // <= 2^30
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(tile), 0, static_cast<int>(static_cast<uint32_t>(bytes)), kBufferFlags);
-    char* lds = reinterpret_cast<char*>(lds_tile) + wave * kInstPerWave * 1024;
+        const_cast<char*>(tile), 0, static_cast<int>(bytes), kBufferFlags);
+    char* lds = reinterpret_cast<char*>(lds_tile);
 #pragma unroll
     for (int i = 0; i < kInstPerWave; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds + i * 1024), 16, voff[i],
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_void_ptr)(lds + (i * NW + wave) * 1024), 16, voff[i], 0, 0, 0);
     }
 #endif
   }
@@ -447,23 +493,36 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 // The kernel
 // ---------------------------------------------------------------------------
 
-template <typename T, int D, int NW, int BN, int MODE, bool CAUSAL>
+// STAGES LDS buffers each for K and V tiles (2 or 3).  With 3, a tile load
+// issued at step t is first needed at step t+2, so it has two steps of
+// compute to hide its latency behind.
+template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
+  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
   using Path = typename PathFor<T, D>::type;
-  using Copy = TileCopy<T, D, BN, NW>;
+  using KCopy = TileCopy<T, D, BN, NW, Path::kRowK>;
+  using VCopy = TileCopy<T, D, BN, NW, Path::kRowV>;
   using PRegs = typename Path::template PRegs<BN / 32>;
   constexpr int BM = NW * 32;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
+  constexpr int kKElems = KCopy::kArrayBytes / static_cast<int>(sizeof(T));
+  constexpr int kVElems = VCopy::kArrayBytes / static_cast<int>(sizeof(T));
+  // Loads one step issues per wave; with three stages they may still be in
+  // flight when the step ends.
+  constexpr int kLoadsPerStep = KCopy::kInstPerWave + VCopy::kInstPerWave;
+  constexpr int kInFlightAtStepEnd = (STAGES - 2) * kLoadsPerStep;
 
-  // Four separate LDS arrays (not one [2][...] array): each gets its own
-  // alias scope, so the compiler can see that fragment reads of one buffer do
-  // not depend on the buffer loads still landing in the other one, and need
-  // not wait for them.
-  __shared__ __attribute__((aligned(1024))) T k_lds0[BN * D];
-  __shared__ __attribute__((aligned(1024))) T k_lds1[BN * D];
-  __shared__ __attribute__((aligned(1024))) T v_lds0[BN * D];
-  __shared__ __attribute__((aligned(1024))) T v_lds1[BN * D];
+  // Separate LDS arrays per buffer (not one [STAGES][...] array): each gets
+  // its own alias scope, so the compiler can see that fragment reads of one
+  // buffer do not depend on the buffer loads still landing in another, and
+  // need not wait for them.
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds2[STAGES > 2 ? kKElems : 8];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds2[STAGES > 2 ? kVElems : 8];
 
   int z, h, m;
   decode_tile(a.m_tiles, a.num_heads, z, h, m);
@@ -499,19 +558,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const int64_t k_row_bytes = a.k_ss * static_cast<int64_t>(sizeof(T));
   const int64_t v_row_bytes = a.v_ss * static_cast<int64_t>(sizeof(T));
-  Copy kcopy, vcopy;
-  kcopy.template init<Path, false>(wave, lane, k_row_bytes);
-  vcopy.template init<Path, true>(wave, lane, v_row_bytes);
-  // Tile t lives in buffer t & 1.  Every call below names its buffers
-  // directly (the loop is unrolled by two), so after inlining each LDS access
-  // refers to a known array.
-  auto issue_k = [&](int t, T* buf) {
+  KCopy kcopy;
+  VCopy vcopy;
+  kcopy.init(wave, lane, k_row_bytes);
+  vcopy.init(wave, lane, v_row_bytes);
+  // Tile t lives in buffer t % STAGES.  Every call below names its buffers
+  // directly (the loop is unrolled by STAGES), so after inlining each LDS
+  // access refers to a known array.  Rows at or past `end` are not fetched
+  // (they read back as zeros); a load past the last tile fetches nothing.
+  auto issue_k = [&](int t, T* buf, int end) {
     const int j0 = t * BN;
-    kcopy.issue(kp + j0 * k_row_bytes, sr.len_k - j0, k_row_bytes, buf, wave);
+    kcopy.issue(kp + j0 * k_row_bytes, end - j0, k_row_bytes, buf, wave);
   };
-  auto issue_v = [&](int t, T* buf) {
+  auto issue_v = [&](int t, T* buf, int end) {
     const int j0 = t * BN;
-    vcopy.issue(vp + j0 * v_row_bytes, sr.len_k - j0, v_row_bytes, buf, wave);
+    vcopy.issue(vp + j0 * v_row_bytes, end - j0, v_row_bytes, buf, wave);
   };
 
   typename Path::QRegs qr;
@@ -520,17 +581,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;  // running max of scale*log2(e)*s, this row
+  float m_run = kNegInf;  // reference (stale) max of scale*log2(e)*s, this row
   float l_run = 0.f;      // running sum of this half-wave's weights
-  float alpha = 1.f;      // pending rescale of acc and l (when rescale is set)
-  bool rescale = false;
   const float c2 = a.scale_log2;
 
-  // Scores of tile t (masked where needed) into s; k_tile holds K(t).
-  auto scores = [&](int t, const T* k_tile, f32x16 (&s)[NB]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-    Path::template qk<NB>(k_tile, qr, li, lh, s);
+  // Masks the scores of tile t where keys run past the sequence or, under
+  // the causal mask, past the lane's row (only tail and diagonal tiles).
+  auto mask_tile = [&](int t, f32x16 (&s)[NB]) {
     const int j0 = t * BN;
     const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0);
     if (need_mask) {
@@ -538,80 +595,144 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + nb * 32 + lh * 16 + r;
+          const int key = j0 + nb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
           const bool ok = key < sr.len_k && (!CAUSAL || key <= qi);
           if (!ok) s[nb][r] = kNegInf;
         }
       }
     }
   };
-  // Fold the row max of s into m_run; a growth beyond the threshold in any
-  // row of the wave schedules a rescale of acc and l.
-  auto update_max = [&](const f32x16 (&s)[NB]) {
+  // Row max of a score tile in scaled log2 units (scale > 0, so the max
+  // commutes with the scaling).
+  auto tile_max = [&](const f32x16 (&s)[NB]) {
     float mx = kNegInf;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
     }
-    mx = max_across_halves(mx) * c2;  // scale > 0, so max commutes with it
-    const bool grow = mx > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      rescale = true;
+    return max_across_halves(mx) * c2;
+  };
+  // Probabilities of score tile s against the running reference m_run,
+  // into p; returns this lane's share of the tile's row sum.  The reference
+  // only has to keep every p bounded, not to equal the row max: while a
+  // tile's sums stay <= 2^12 (so every p <= 2^12) nothing else is done.
+  // Otherwise -- and on the first tile a row sees -- the exact row max is
+  // taken, acc and l are rescaled to it, and p is recomputed (p <= 1).  The
+  // result is unchanged: O = acc / l and LSE = m + log2 l for any m.
+  auto probabilities = [&](const f32x16 (&s)[NB], PRegs& p) {
+    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+    float tile_sum = Path::template softmax_p<NB>(s, c2, m_sub, p);
+    const bool redo = !(tile_sum <= kSumLimit) || m_run == kNegInf;
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      const float m_new = fmaxf(m_run, tile_max(s));
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       m_run = m_new;
+      tile_sum = Path::template softmax_p<NB>(s, c2, (m_run == kNegInf) ? 0.f : m_run, p);
     }
+    return tile_sum;
   };
 
   f32x16 s[NB];
   if (n_tiles > 0) {
-    issue_k(0, k_lds0);
-    issue_v(0, v_lds0);
-    if (n_tiles > 1) issue_k(1, k_lds1);
+    issue_k(0, k_lds0, kend);
+    issue_k(1, k_lds1, 1 < n_tiles ? kend : 0);
+    issue_v(0, v_lds0, kend);
+    if constexpr (STAGES > 2) {
+      issue_k(2, k_lds2, 2 < n_tiles ? kend : 0);
+      issue_v(1, v_lds1, 1 < n_tiles ? kend : 0);
+    }
     wait_vmem();
     __syncthreads();
-    scores(0, k_lds0, s);
-    update_max(s);
-    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+    Path::template qk<NB>(k_lds0, qr, li, lh, s);
+    mask_tile(0, s);
+    __syncthreads();  // every wave is done with K(0) before K(STAGES) replaces it
   }
 
-  // One pipeline step for tile t: (k_cur, v_cur) are the buffers of parity
-  // t & 1 (K(t+2) and V(t) live there), (k_nxt, v_nxt) the other parity
-  // (K(t+1) and V(t+1)).
-  auto step = [&](int t, T* k_cur, T* v_cur, T* k_nxt, T* v_nxt) {
-    const bool has_next = t + 1 < n_tiles;
-    if (t + 2 < n_tiles) issue_k(t + 2, k_cur);
-    if (has_next) issue_v(t + 1, v_nxt);
-
-    if (rescale) {  // the max grew at tile t: bring acc and l to the new base
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      rescale = false;
-    }
-    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+  // Pipeline step for tile t when tile t+1 exists.  k_cur holds K(t) (done
+  // with; K(t+STAGES) is loaded into it), k_nxt holds K(t+1), v_cur holds V(t)
+  // and v_pre receives V(t+STAGES-1).  Phase A is straight-line code, so the
+  // scheduler can interleave the softmax VALU work with the next tile's
+  // score MFMAs.
+  auto step = [&](int t, T* k_cur, T* k_nxt, T* v_cur, T* v_pre) {
+    issue_k(t + STAGES, k_cur, t + STAGES < n_tiles ? kend : 0);
+    issue_v(t + STAGES - 1, v_pre, t + STAGES - 1 < n_tiles ? kend : 0);
 
     // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
     PRegs p;
-    l_run += Path::template softmax_p<NB>(s, c2, m_sub, p);
     f32x16 s_next[NB];
-    if (has_next) scores(t + 1, k_nxt, s_next);
-
-    // Phase B: O += P(t) V(t) (MFMA) || row max of tile t+1 (VALU).
-    Path::template pv<NB, DB>(v_cur, p, lane, acc);
-    if (has_next) {
-      update_max(s_next);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
+    for (int nb = 0; nb < NB; ++nb) s_next[nb] = f32x16{};
+    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+    float tile_sum = Path::template softmax_p<NB>(s, c2, m_sub, p);
+    Path::template qk<NB>(k_nxt, qr, li, lh, s_next);
+    Path::pin(p);  // P is computed here, beside the MFMAs, not after the branch
+    Path::template interleave_qk<NB>();
+    const bool redo = !(tile_sum <= kSumLimit) || m_run == kNegInf;
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {  // rare: see probabilities()
+      const float m_new = fmaxf(m_run, tile_max(s));
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+      tile_sum = Path::template softmax_p<NB>(s, c2, (m_run == kNegInf) ? 0.f : m_run, p);
     }
+    l_run += tile_sum;
+    mask_tile(t + 1, s_next);
 
-    wait_vmem();
+    // Phase B: O += P(t) V(t) on the matrix cores.
+    Path::template pv<NB, DB>(v_cur, p, lane, acc);
+    Path::template interleave_pv<NB, DB>();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
+
+    // K(t+2) and V(t+1) -- issued one step earlier with three stages, in
+    // this step with two -- must have landed before the next step.
+    wait_vmem_allow<kInFlightAtStepEnd>();
     __syncthreads();
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, k_lds0, v_lds0, k_lds1, v_lds1);
-    if (t + 1 < n_tiles) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  // The last tile: probabilities and P.V only.
+  auto last_step = [&](const T* v_cur) {
+    PRegs p;
+    l_run += probabilities(s, p);
+    Path::template pv<NB, DB>(v_cur, p, lane, acc);
+  };
+
+  int t = 0;
+  if constexpr (STAGES == 2) {
+    for (; t + 2 < n_tiles; t += 2) {  // both steps have a next tile
+      step(t, k_lds0, k_lds1, v_lds0, v_lds1);
+      step(t + 1, k_lds1, k_lds0, v_lds1, v_lds0);
+    }
+    if (n_tiles - t == 2) {
+      step(t, k_lds0, k_lds1, v_lds0, v_lds1);
+      last_step(v_lds1);
+    } else if (n_tiles - t == 1) {
+      last_step(v_lds0);
+    }
+  } else {
+    for (; t + 3 < n_tiles; t += 3) {  // all three steps have a next tile
+      step(t, k_lds0, k_lds1, v_lds0, v_lds2);
+      step(t + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+      step(t + 2, k_lds2, k_lds0, v_lds2, v_lds1);
+    }
+    const int rest = n_tiles - t;
+    if (rest == 3) {
+      step(t, k_lds0, k_lds1, v_lds0, v_lds2);
+      step(t + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+      last_step(v_lds2);
+    } else if (rest == 2) {
+      step(t, k_lds0, k_lds1, v_lds0, v_lds2);
+      last_step(v_lds1);
+    } else if (rest == 1) {
+      last_step(v_lds0);
+    }
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
@@ -654,8 +775,8 @@ template <typename T, int D, int MODE, bool CAUSAL>
 int launch_typed(const FwdArgs& a, hipStream_t stream) {
   constexpr TableEntry e = table_entry<T, D>();
   const uint32_t grid = static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, MODE, CAUSAL>), dim3(grid),
-                     dim3(e.waves * 64), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL>),
+                     dim3(grid), dim3(e.waves * 64), 0, stream, a);
   return static_cast<int>(hipGetLastError());
 }
 
