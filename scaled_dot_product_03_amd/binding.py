@@ -53,11 +53,16 @@ _stride = ctypes.POINTER(ctypes.c_int64)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the shared library once and declare its signatures."""
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the shared library once and declare its signatures.
+
+    The default is the in-tree build; SDPA03_LIBRARY names another build of
+    the same library (the dispatch-table sweep uses it for its candidates).
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SDPA03_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is not built; build it with `python -m scaled_dot_product_03_amd.build` "

@@ -497,7 +497,8 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 // issued at step t is first needed at step t+2, so it has two steps of
 // compute to hide its latency behind.
 template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_lds1, T* k_lds2,
+                                              T* v_lds0, T* v_lds1, T* v_lds2) {
   static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
   using Path = typename PathFor<T, D>::type;
   using KCopy = TileCopy<T, D, BN, NW, Path::kRowK>;
@@ -506,23 +507,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = NW * 32;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
-  constexpr int kKElems = KCopy::kArrayBytes / static_cast<int>(sizeof(T));
-  constexpr int kVElems = VCopy::kArrayBytes / static_cast<int>(sizeof(T));
   // Loads one step issues per wave; with three stages they may still be in
   // flight when the step ends.
   constexpr int kLoadsPerStep = KCopy::kInstPerWave + VCopy::kInstPerWave;
   constexpr int kInFlightAtStepEnd = (STAGES - 2) * kLoadsPerStep;
-
-  // Separate LDS arrays per buffer (not one [STAGES][...] array): each gets
-  // its own alias scope, so the compiler can see that fragment reads of one
-  // buffer do not depend on the buffer loads still landing in another, and
-  // need not wait for them.
-  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
-  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
-  __shared__ __attribute__((aligned(1024))) T k_lds2[STAGES > 2 ? kKElems : 8];
-  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds2[STAGES > 2 ? kVElems : 8];
 
   int z, h, m;
   decode_tile(a.m_tiles, a.num_heads, z, h, m);
@@ -704,35 +692,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     Path::template pv<NB, DB>(v_cur, p, lane, acc);
   };
 
-  int t = 0;
-  if constexpr (STAGES == 2) {
-    for (; t + 2 < n_tiles; t += 2) {  // both steps have a next tile
-      step(t, k_lds0, k_lds1, v_lds0, v_lds1);
-      step(t + 1, k_lds1, k_lds0, v_lds1, v_lds0);
+  // Each step body exists once (unrolled by STAGES so that every step names
+  // its buffers at compile time); the loop leaves as soon as the next tile
+  // would be the last one, and the last tile's V buffer is picked at run time
+  // (the last step issues no loads, so nothing can be in flight into it).
+  if (n_tiles > 0) {
+    for (int t = 0;; t += STAGES) {
+      if (t + 1 >= n_tiles) break;
+      step(t, k_lds0, k_lds1, v_lds0, STAGES == 2 ? v_lds1 : v_lds2);
+      if (t + 2 >= n_tiles) break;
+      if constexpr (STAGES == 2) {
+        step(t + 1, k_lds1, k_lds0, v_lds1, v_lds0);
+      } else {
+        step(t + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+        if (t + 3 >= n_tiles) break;
+        step(t + 2, k_lds2, k_lds0, v_lds2, v_lds1);
+      }
     }
-    if (n_tiles - t == 2) {
-      step(t, k_lds0, k_lds1, v_lds0, v_lds1);
-      last_step(v_lds1);
-    } else if (n_tiles - t == 1) {
-      last_step(v_lds0);
-    }
-  } else {
-    for (; t + 3 < n_tiles; t += 3) {  // all three steps have a next tile
-      step(t, k_lds0, k_lds1, v_lds0, v_lds2);
-      step(t + 1, k_lds1, k_lds2, v_lds1, v_lds0);
-      step(t + 2, k_lds2, k_lds0, v_lds2, v_lds1);
-    }
-    const int rest = n_tiles - t;
-    if (rest == 3) {
-      step(t, k_lds0, k_lds1, v_lds0, v_lds2);
-      step(t + 1, k_lds1, k_lds2, v_lds1, v_lds0);
-      last_step(v_lds2);
-    } else if (rest == 2) {
-      step(t, k_lds0, k_lds1, v_lds0, v_lds2);
-      last_step(v_lds1);
-    } else if (rest == 1) {
-      last_step(v_lds0);
-    }
+    const int last = (n_tiles - 1) % STAGES;
+    last_step(last == 0 ? v_lds0 : (last == 1 ? v_lds1 : v_lds2));
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
@@ -760,6 +738,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     if (lh == 0) {
       lsep[qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
     }
+  }
+}
+
+// The kernel: declares the LDS buffers its stage count needs and runs the
+// body.  Separate LDS arrays per buffer (not one [STAGES][...] array): each
+// gets its own alias scope, so the compiler can see that fragment reads of
+// one buffer do not depend on the buffer loads still landing in another,
+// and need not wait for them.
+template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
+  using Path = typename PathFor<T, D>::type;
+  constexpr int kKElems = TileCopy<T, D, BN, NW, Path::kRowK>::kArrayBytes / static_cast<int>(sizeof(T));
+  constexpr int kVElems = TileCopy<T, D, BN, NW, Path::kRowV>::kArrayBytes / static_cast<int>(sizeof(T));
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  if constexpr (STAGES > 2) {
+    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds2, v_lds0, v_lds1,
+                                                      v_lds2);
+  } else {
+    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds0, v_lds0, v_lds1,
+                                                      v_lds0);
   }
 }
 
