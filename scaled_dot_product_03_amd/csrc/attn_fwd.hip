@@ -412,8 +412,21 @@ struct TileCopy {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int rows = valid_rows < 0 ? 0 : (valid_rows > BN ? BN : valid_rows);
     const uint32_t bytes = static_cast<uint32_t>(rows * row_bytes);  // <= 2^30
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(tile), 0, static_cast<int>(bytes), kBufferFlags);
+    // Every input of the descriptor is wave-uniform; saying so explicitly
+    // keeps the descriptor in SGPRs.  (Left in VGPRs, the compiler wraps each
+    // buffer load in a loop over the distinct descriptor values of the wave.)
+    // readfirstlane returns int: keep both halves unsigned 32-bit before
+    // widening, or a low half with bit 31 set would sign-extend into the
+    // high half of the address.
+    const uint64_t addr = reinterpret_cast<uint64_t>(tile);
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr >> 32))));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr))));
+    const uint64_t base = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, nrec, kBufferFlags);
     char* lds = reinterpret_cast<char*>(lds_tile);
 #pragma unroll
     for (int i = 0; i < kInstPerWave; ++i) {
@@ -520,7 +533,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile-copy addresses scalar
   const int li = lane & 31;
   const int lh = lane >> 5;
 
