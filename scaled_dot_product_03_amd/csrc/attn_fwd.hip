@@ -80,6 +80,22 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Workgroup barrier for LDS hand-offs.  __syncthreads() (and any release
+// fence covering LDS) waits for every outstanding vector-memory load first
+// (vmcnt(0)), because a buffer load into LDS counts as an LDS write -- which
+// would drain tile loads that are meant to stay in flight across the barrier.
+// Here each wave waits for its own tile loads explicitly (wait_vmem_allow)
+// before it arrives; the barrier itself waits only for the wave's LDS reads
+// (so no later load can overwrite a buffer still being read), and the memory
+// clobber and the scheduling barriers keep the compiler from moving LDS
+// accesses -- or any other instruction -- across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory
 // loads are still in flight (they complete in issue order).
 template <int N>
@@ -197,6 +213,20 @@ struct Path16 {
   template <int NB, int DB>
   __device__ static __forceinline__ void interleave_pv() {
     constexpr int n_mfma = NB * 2 * DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < n_mfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+
+  // One C interval of the ping-pong schedule: the scores of the next tile
+  // and P.V of the current one, both on the matrix cores; keep a few LDS
+  // reads ahead of the products.
+  template <int NB, int DB>
+  __device__ static __forceinline__ void interleave_c() {
+    constexpr int n_mfma = NB * kQFrags + NB * 2 * DB;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < n_mfma; ++i) {
@@ -435,6 +465,45 @@ struct TileCopy {
     }
 #endif
   }
+
+  // The same copy written as inline assembly.  The compiler neither moves
+  // these loads nor counts them, so it inserts no waits of its own for them
+  // (its tracking of which LDS buffer a load writes is lost across the
+  // ping-pong loop and would make it drain every load in flight); the caller
+  // waits with explicit vmcnt counts, and must have no compiler-issued
+  // vector-memory load outstanding that it relies on the compiler to wait
+  // for.  The memory clobber keeps LDS reads of earlier code before the
+  // loads.  s_nop 4 covers the wait states between a VALU write of a
+  // descriptor SGPR (readfirstlane) and its use by a vector-memory
+  // instruction; s_nop 0 those between writing M0 and an LDS load.
+  __device__ __forceinline__ void issue_untracked(const char* tile, int valid_rows,
+                                                  int64_t row_bytes, T* lds_tile, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using i32x4 = int __attribute__((ext_vector_type(4)));
+    const int rows = valid_rows < 0 ? 0 : (valid_rows > BN ? BN : valid_rows);
+    const uint32_t bytes = static_cast<uint32_t>(rows * row_bytes);  // <= 2^30
+    const uint64_t addr = reinterpret_cast<uint64_t>(tile);
+    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr >> 32)));
+    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr)));
+    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    // Raw descriptor: base (48 bits, stride 0), num_records, format/flags.
+    const i32x4 rsrc = {lo, hi & 0xFFFF, nrec, kBufferFlags};
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_ptr)(lds_tile);  // LDS byte address
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+          static_cast<int>(lds + static_cast<uint32_t>((i * NW + wave) * 1024))));
+      asm volatile(
+          "s_nop 4\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %0, %2, 0 offen lds"
+          :
+          : "v"(voff[i]), "s"(m0v), "s"(rsrc)
+          : "memory", "m0");
+    }
+#endif
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -647,12 +716,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
       issue_v(1, v_lds1, 1 < n_tiles ? kend : 0);
     }
     wait_vmem();
-    __syncthreads();
+    barrier_lds();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
     Path::template qk<NB>(k_lds0, qr, li, lh, s);
     mask_tile(0, s);
-    __syncthreads();  // every wave is done with K(0) before K(STAGES) replaces it
+    barrier_lds();  // every wave is done with K(0) before K(STAGES) replaces it
   }
 
   // Pipeline step for tile t when tile t+1 exists.  k_cur holds K(t) (done
@@ -696,7 +765,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
     // K(t+2) and V(t+1) -- issued one step earlier with three stages, in
     // this step with two -- must have landed before the next step.
     wait_vmem_allow<kInFlightAtStepEnd>();
-    __syncthreads();
+    barrier_lds();
   };
   // The last tile: probabilities and P.V only.
   auto last_step = [&](const T* v_cur) {
@@ -754,6 +823,267 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong schedule (16-bit inputs)
+// ---------------------------------------------------------------------------
+// Eight waves in two groups of four: waves w and w + 4 run on the same SIMD,
+// so every SIMD holds one wave of each group.  A wave alternates two kinds
+// of interval: C(n) -- matrix-core work: scores of tile n+1 (K(n+1) Q^T) and
+// O += P(n) V(n) -- and S(n) -- vector work: mask and probabilities of tile
+// n.  Group 1 runs one interval behind group 0, and every interval ends at a
+// workgroup barrier, so on each SIMD one wave's softmax always runs beside
+// the other wave's matrix products.
+//
+// With global interval j (group 0 runs its local interval u at j = u, group
+// 1 at j = u + 1; u = 0 is the first tile's scores, then S(n) at u = 2n+1
+// and C(n) at u = 2n+2), K(n) is read at j = 2n and 2n+1, V(n) at j = 2n+2
+// and 2n+3.  Tiles rotate through STAGES buffers (tile n in buffer
+// n % STAGES).  At the start of C(n) each wave issues its share of K(n +
+// STAGES) into K(n)'s buffer and of V(n + STAGES - 1) into V(n - 1)'s: the
+// last readers of both finished by global interval 2n+1, and C(n) starts at
+// j >= 2n+2.  At the end of C(n) each wave waits until only the loads it
+// issued in the last STAGES - 2 C intervals are in flight, so a tile issued
+// in C(n) has landed after C(n + STAGES - 2) -- before its first reader at
+// j = 2(n + STAGES) (K) or 2(n + STAGES - 1) + 2 (V).
+template <typename T, int D, int BN, int STAGES, int MODE, bool CAUSAL>
+__device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_lds0, T* k_lds1,
+                                                       T* k_lds2, T* v_lds0, T* v_lds1,
+                                                       T* v_lds2) {
+  static_assert(sizeof(T) == 2, "the ping-pong schedule serves 16-bit inputs");
+  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  constexpr int NW = 8;
+  using Path = Path16<T, D>;
+  using KCopy = TileCopy<T, D, BN, NW, Path::kRowK>;
+  using VCopy = TileCopy<T, D, BN, NW, Path::kRowV>;
+  using PRegs = typename Path::template PRegs<BN / 32>;
+  constexpr int BM = NW * 32;
+  constexpr int NB = BN / 32;
+  constexpr int DB = D / 32;
+  constexpr int kLoadsPerTile = KCopy::kInstPerWave + VCopy::kInstPerWave;
+  constexpr int kInFlight = (STAGES - 2) * kLoadsPerTile;
+
+  int z, h, m;
+  decode_tile(a.m_tiles, a.num_heads, z, h, m);
+  const SeqRange sr = seq_range<MODE>(a, z);
+  const int m0 = m * BM;
+  if (m0 >= sr.len_q) return;  // uniform over the workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const T* qp = static_cast<const T*>(a.q) + sr.b * a.q_sb + h * a.q_sh +
+                static_cast<int64_t>(sr.q_start) * a.q_ss;
+  const char* kp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.k) + sr.b * a.k_sb + h * a.k_sh +
+      static_cast<int64_t>(sr.k_start) * a.k_ss);
+  const char* vp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.v) + sr.b * a.v_sb + h * a.v_sh +
+      static_cast<int64_t>(sr.k_start) * a.v_ss);
+  T* op = static_cast<T*>(a.o) + sr.b * a.o_sb + h * a.o_sh +
+          static_cast<int64_t>(sr.q_start) * a.o_ss;
+  float* lsep = a.lse + sr.b * a.lse_sb + h * a.lse_sh + sr.q_start;
+
+  const int row0 = m0 + wave * 32;
+  const int qi = row0 + li;
+  const bool row_ok = qi < sr.len_q;
+
+  int kend = sr.len_k;
+  if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, sr.len_q));
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  const int64_t k_row_bytes = a.k_ss * static_cast<int64_t>(sizeof(T));
+  const int64_t v_row_bytes = a.v_ss * static_cast<int64_t>(sizeof(T));
+  KCopy kcopy;
+  VCopy vcopy;
+  kcopy.init(wave, lane, k_row_bytes);
+  vcopy.init(wave, lane, v_row_bytes);
+  auto issue_k = [&](int t, T* buf) {
+    const int j0 = t * BN;
+    kcopy.issue_untracked(kp + j0 * k_row_bytes, t < n_tiles ? kend - j0 : 0, k_row_bytes, buf,
+                          wave);
+  };
+  auto issue_v = [&](int t, T* buf) {
+    const int j0 = t * BN;
+    vcopy.issue_untracked(vp + j0 * v_row_bytes, t < n_tiles ? kend - j0 : 0, v_row_bytes, buf,
+                          wave);
+  };
+
+  typename Path::QRegs qr;
+  Path::load_q(qp + static_cast<int64_t>(qi) * a.q_ss, row_ok, lh, qr);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  // Same masking and lazy-reference softmax as the single-group schedule.
+  auto mask_tile = [&](int t, f32x16 (&s)[NB]) {
+    const int j0 = t * BN;
+    const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0);
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + nb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool ok = key < sr.len_k && (!CAUSAL || key <= qi);
+          if (!ok) s[nb][r] = kNegInf;
+        }
+      }
+    }
+  };
+  auto tile_max = [&](const f32x16 (&s)[NB]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+    }
+    return max_across_halves(mx) * c2;
+  };
+  auto probabilities = [&](const f32x16 (&s)[NB], PRegs& p) {
+    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+    float tile_sum = Path::template softmax_p<NB>(s, c2, m_sub, p);
+    const bool redo = !(tile_sum <= kSumLimit) || m_run == kNegInf;
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      const float m_new = fmaxf(m_run, tile_max(s));
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+      tile_sum = Path::template softmax_p<NB>(s, c2, (m_run == kNegInf) ? 0.f : m_run, p);
+    }
+    return tile_sum;
+  };
+
+  f32x16 s[NB];
+  PRegs p;
+  if (n_tiles > 0) {
+    // Prologue: Q (loaded above) and K(0) land before the first barrier;
+    // K(i) and V(i-1), i < STAGES, stay in flight behind the first scores.
+    // (Q's loads are the compiler's: the full wait settles them before any
+    // untracked tile load is issued.)
+    issue_k(0, k_lds0);
+    wait_vmem();
+    barrier_lds();
+    issue_k(1, k_lds1);
+    issue_v(0, v_lds0);
+    if constexpr (STAGES > 2) {
+      issue_k(2, k_lds2);
+      issue_v(1, v_lds1);
+    }
+    if (group == 1) barrier_lds();  // group 1 sits out global interval 0
+
+    // u = 0: scores of tile 0.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+    Path::template qk<NB>(k_lds0, qr, li, lh, s);
+    wait_vmem_allow<kInFlight>();  // K(1) and V(0) have landed
+    barrier_lds();
+
+    // S(n): vector work on tile n's scores.
+    auto s_interval = [&](int n) {
+      mask_tile(n, s);
+      l_run += probabilities(s, p);
+      barrier_lds();
+    };
+    // C(n) for n + 1 < n_tiles.  k_cur: K(n)'s buffer (receives K(n+STAGES));
+    // k_nxt: K(n+1); v_cur: V(n); v_pre: receives V(n+STAGES-1).
+    // The loads are issued unconditionally (tiles past the end fetch zero
+    // rows into buffers nobody reads again): a branch around them would make
+    // the compiler lose track of which buffer each load writes and wait for
+    // all of them before the first fragment read.
+    auto c_interval = [&](int n, T* k_cur, T* k_nxt, T* v_cur, T* v_pre) {
+      issue_k(n + STAGES, k_cur);
+      issue_v(n + STAGES - 1, v_pre);
+      f32x16 s_next[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s_next[nb] = f32x16{};
+      Path::template qk<NB>(k_nxt, qr, li, lh, s_next);
+      Path::template pv<NB, DB>(v_cur, p, lane, acc);
+      Path::template interleave_c<NB, DB>();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
+      wait_vmem_allow<kInFlight>();
+      barrier_lds();
+    };
+
+    for (int n = 0;; n += STAGES) {
+      if (n + 1 >= n_tiles) break;
+      s_interval(n);
+      c_interval(n, k_lds0, k_lds1, v_lds0, STAGES == 2 ? v_lds1 : v_lds2);
+      if (n + 2 >= n_tiles) break;
+      s_interval(n + 1);
+      if constexpr (STAGES == 2) {
+        c_interval(n + 1, k_lds1, k_lds0, v_lds1, v_lds0);
+      } else {
+        c_interval(n + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+        if (n + 3 >= n_tiles) break;
+        s_interval(n + 2);
+        c_interval(n + 2, k_lds2, k_lds0, v_lds2, v_lds1);
+      }
+    }
+    // Last tile: S(T-1), then C(T-1) = P.V only.  Group 1's last interval is
+    // the workgroup's last, so it ends without a barrier (every wave passes
+    // the same number of barriers).
+    s_interval(n_tiles - 1);
+    const int last = (n_tiles - 1) % STAGES;
+    const T* v_last = last == 0 ? v_lds0 : (last == 1 ? v_lds1 : v_lds2);
+    Path::template pv<NB, DB>(v_last, p, lane, acc);
+    wait_vmem();
+    if (group == 0) barrier_lds();
+  }
+
+  // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
+  const float l_tot = sum_across_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    T* orow = op + static_cast<int64_t>(qi) * a.o_ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        T out4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out4[e] = static_cast<T>(acc[db][4 * g + e] * inv);
+        uint2 packed;
+        __builtin_memcpy(&packed, out4, 8);
+        *reinterpret_cast<uint2*>(orow + db * 32 + g * 8 + lh * 4) = packed;
+      }
+    }
+    if (lh == 0) {
+      lsep[qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+template <typename T, int D, int BN, int STAGES, int MODE, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_fwd_pingpong_kernel(FwdArgs a) {
+  using Path = Path16<T, D>;
+  constexpr int kKElems = TileCopy<T, D, BN, 8, Path::kRowK>::kArrayBytes / 2;
+  constexpr int kVElems = TileCopy<T, D, BN, 8, Path::kRowV>::kArrayBytes / 2;
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  if constexpr (STAGES > 2) {
+    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+    attn_fwd_pingpong_body<T, D, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds2, v_lds0,
+                                                           v_lds1, v_lds2);
+  } else {
+    attn_fwd_pingpong_body<T, D, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds0, v_lds0,
+                                                           v_lds1, v_lds0);
+  }
+}
+
 // The kernel: declares the LDS buffers its stage count needs and runs the
 // body.  Separate LDS arrays per buffer (not one [STAGES][...] array): each
 // gets its own alias scope, so the compiler can see that fragment reads of
@@ -791,8 +1121,14 @@ template <typename T, int D, int MODE, bool CAUSAL>
 int launch_typed(const FwdArgs& a, hipStream_t stream) {
   constexpr TableEntry e = table_entry<T, D>();
   const uint32_t grid = static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL>),
-                     dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  if constexpr (e.pingpong != 0) {
+    static_assert(e.waves == 8 && sizeof(T) == 2, "ping-pong: 8 waves, 16-bit inputs");
+    hipLaunchKernelGGL((attn_fwd_pingpong_kernel<T, D, e.block_n, e.stages, MODE, CAUSAL>),
+                       dim3(grid), dim3(512), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  }
   return static_cast<int>(hipGetLastError());
 }
 

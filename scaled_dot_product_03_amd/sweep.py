@@ -1,7 +1,8 @@
 """Offline sweep that writes the compiled-in dispatch table.
 
 For every problem class (dtype, head_dim) a set of candidate kernel shapes
-(waves per workgroup, keys per tile, LDS stages) is compiled into its own
+(waves per workgroup, keys per tile, LDS stages, schedule: 0 single group,
+1 ping-pong of two wave groups) is compiled into its own
 build of libsdpa03.so.  A candidate counts only if its build has no register
 spills, keeps two waves per SIMD, and then passes the GPU parity tests
 (tests/test_gpu_parity.py, run against that build); only then is it timed
@@ -31,12 +32,12 @@ RESULTS = os.path.join(SWEEP_DIR, "results.json")
 TABLE = os.path.join(CSRC, "dispatch_table.inc")
 DTYPE_CODES = {"fp32": 0, "fp16": 1, "bf16": 2}
 
-# Candidate (waves, block_n, stages) per class.
+# Candidate (waves, block_n, stages, pingpong) per class.
 CANDIDATES = {
-    ("bf16", 128): [(4, 64, 2), (8, 64, 2), (8, 64, 3), (4, 32, 2), (4, 32, 3), (8, 32, 3)],
-    ("fp16", 128): [(4, 64, 2), (8, 64, 2), (8, 64, 3)],
-    ("fp16", 64): [(4, 64, 2), (4, 64, 3), (8, 64, 2), (8, 64, 3), (4, 32, 3)],
-    ("bf16", 64): [(4, 64, 2), (4, 64, 3), (8, 64, 3)],
+    ("bf16", 128): [(4, 64, 2, 0), (4, 32, 3, 0), (8, 64, 2, 0), (8, 64, 3, 0), (8, 32, 3, 0),
+                    (8, 64, 3, 1), (8, 128, 2, 1)],
+    ("fp16", 64): [(4, 64, 2, 0), (4, 64, 3, 0), (4, 32, 3, 0), (8, 64, 3, 0), (8, 64, 3, 1),
+                   (8, 128, 2, 1)],
 }
 
 # Timed workloads per class: (workload name from inputs.WORKLOADS, weight).
@@ -47,8 +48,14 @@ TIMED = {
 }
 
 
+def _cand4(cand):
+    """Candidates recorded before the schedule field existed are single-group."""
+    return tuple(cand) + (0,) * (4 - len(cand))
+
+
 def _name(cls, cand):
-    return f"{cls[0]}_d{cls[1]}_w{cand[0]}_n{cand[1]}_s{cand[2]}"
+    w, n, st, pp = _cand4(cand)
+    return f"{cls[0]}_d{cls[1]}_w{w}_n{n}_s{st}" + ("_pp" if pp else "")
 
 
 def _lib_path(cls, cand):
@@ -64,7 +71,9 @@ def _resources(cls, cand):
            "-Rpass-analysis=kernel-resource-usage", *defs]
     out = subprocess.run(cmd, capture_output=True, text=True).stderr
     dt_tag = {"bf16": "DF16b", "fp16": "DF16_", "fp32": "f"}[cls[0]]
-    want = f"attn_fwd_kernelI{dt_tag}Li{cls[1]}ELi{cand[0]}ELi{cand[1]}ELi{cand[2]}E"
+    w, n, st, pp = _cand4(cand)
+    want = (f"attn_fwd_pingpong_kernelI{dt_tag}Li{cls[1]}ELi{n}ELi{st}E" if pp else
+            f"attn_fwd_kernelI{dt_tag}Li{cls[1]}ELi{w}ELi{n}ELi{st}E")
     vg, sp, occ, cur = 0, 0, 99, None
     for line in out.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
@@ -86,16 +95,20 @@ def _resources(cls, cand):
 
 
 def _defines(cls, cand):
+    w, n, st, pp = _cand4(cand)
     return [f"-DSDPA03_SWEEP_DTYPE={DTYPE_CODES[cls[0]]}", f"-DSDPA03_SWEEP_HEAD_DIM={cls[1]}",
-            f"-DSDPA03_SWEEP_WAVES={cand[0]}", f"-DSDPA03_SWEEP_BLOCK_N={cand[1]}",
-            f"-DSDPA03_SWEEP_STAGES={cand[2]}"]
+            f"-DSDPA03_SWEEP_WAVES={w}", f"-DSDPA03_SWEEP_BLOCK_N={n}",
+            f"-DSDPA03_SWEEP_STAGES={st}", f"-DSDPA03_SWEEP_PINGPONG={pp}"]
 
 
-def build():
+def build(only=None):
+    """Compile the candidates (those whose name contains one of `only`, if given)."""
     os.makedirs(SWEEP_DIR, exist_ok=True)
     plan = []
     for cls, cands in CANDIDATES.items():
         for cand in cands:
+            if only and not any(o in _name(cls, cand) for o in only):
+                continue
             vg, sp, occ = _resources(cls, cand)
             ok = sp == 0 and occ >= 2
             print(f"{_name(cls, cand):28s} vgpr={vg} spill={sp} waves/simd={occ} "
@@ -169,7 +182,7 @@ def run():
         built = json.load(f)
     results = []
     for b in built:
-        cls, cand = (b["dtype"], b["head_dim"]), tuple(b["cand"])
+        cls, cand = (b["dtype"], b["head_dim"]), _cand4(b["cand"])
         if cls not in TIMED:
             continue
         lib = _lib_path(cls, cand)
@@ -212,9 +225,9 @@ def write(results_path=RESULTS, table_path=TABLE):
         cls = (r["dtype"], r["head_dim"])
         total = sum(sum(v) for v in r["ms"].values())
         if cls not in best or total < best[cls][0]:
-            best[cls] = (total, tuple(r["cand"]), r["ms"])
-    fallback = {("bf16", 128): (4, 64, 2), ("fp16", 128): (4, 64, 2),
-                ("bf16", 64): (4, 64, 3), ("fp16", 64): (4, 64, 3)}
+            best[cls] = (total, _cand4(r["cand"]), r["ms"])
+    fallback = {("bf16", 128): (4, 64, 2, 0), ("fp16", 128): (4, 64, 2, 0),
+                ("bf16", 64): (4, 64, 3, 0), ("fp16", 64): (4, 64, 3, 0)}
     pick = {cls: (best[cls][1] if cls in best else fallback[cls]) for cls in fallback}
     # classes without their own timed workload follow the timed class of the same head_dim
     if ("bf16", 128) in best:
@@ -223,15 +236,16 @@ def write(results_path=RESULTS, table_path=TABLE):
         pick[("bf16", 64)] = best[("fp16", 64)][1]
     lines = ["  // BEGIN TABLE (generated)"]
     for cls, (total, cand, ms) in sorted(best.items()):
-        lines.append(f"  // {cls[0]} d{cls[1]}: (waves, block_n, stages) = {cand}; "
+        lines.append(f"  // {cls[0]} d{cls[1]}: (waves, block_n, stages, pingpong) = {cand}; "
                      f"sum of timed workloads {total:.3f} ms")
-    lines += ["  if constexpr (sizeof(T) == 4) {", "    return TableEntry{4, 32, 2};"]
+    lines += ["  if constexpr (sizeof(T) == 4) {", "    return TableEntry{4, 32, 2, 0};"]
     for dt in ("bf16", "fp16"):
         for d in (128, 64):
-            w, n, s = pick[(dt, d)]
+            w, n, st, pp = pick[(dt, d)]
             cond = (f"dtype_code<T>() == {'DT_BF16' if dt == 'bf16' else 'DT_F16'} && D == {d}")
-            lines += [f"  }} else if constexpr ({cond}) {{", f"    return TableEntry{{{w}, {n}, {s}}};"]
-    lines += ["  } else {", "    return TableEntry{4, 64, 2};", "  }", "  // END TABLE"]
+            lines += [f"  }} else if constexpr ({cond}) {{",
+                      f"    return TableEntry{{{w}, {n}, {st}, {pp}}};"]
+    lines += ["  } else {", "    return TableEntry{4, 64, 2, 0};", "  }", "  // END TABLE"]
     text = open(table_path).read()
     text = re.sub(r"  // BEGIN TABLE \(generated\).*  // END TABLE", "\n".join(lines), text,
                   flags=re.S)
@@ -242,4 +256,7 @@ def write(results_path=RESULTS, table_path=TABLE):
 
 
 if __name__ == "__main__":
-    {"build": build, "run": run, "write": write}[sys.argv[1]]()
+    if sys.argv[1] == "build":
+        build(sys.argv[2:] or None)
+    else:
+        {"run": run, "write": write}[sys.argv[1]]()
