@@ -88,7 +88,8 @@ typedef enum {
   SDPA_ERR_BATCH = 7,     /* compact varlen called with B != 1 */
   SDPA_ERR_SEQLEN = 8,    /* bad sequence-length arguments or cu_seqlens contents */
   SDPA_ERR_SCALE = 9,     /* scale is not finite and positive */
-  SDPA_ERR_HIP = 10       /* the HIP runtime rejected the launch */
+  SDPA_ERR_HIP = 10,      /* the HIP runtime rejected the launch */
+  SDPA_ERR_WORKSPACE = 11 /* split forward: workspace NULL, misaligned or too small */
 } sdpa_status;
 
 /* Static text for a status code (never NULL). */
@@ -161,6 +162,55 @@ sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, 
                                    const int64_t q_stride[4], const int64_t k_stride[4],
                                    const int64_t v_stride[4], const int64_t o_stride[4],
                                    float scale, int32_t causal, void* hip_stream);
+
+/*
+ * Key-parallel ("split") dense forward for few query rows against many keys.
+ * Triton issue #2267 (opening comment) counts differing numbers of queries
+ * and keys among the use cases; with, say, 512 queries against 8192 keys a
+ * grid of one workgroup per query tile leaves most of the 256 compute units
+ * idle.  Here the key axis of every query tile is cut into num_splits
+ * contiguous ranges of whole key tiles.  Each range is computed by its own
+ * workgroup into a partial output normalised over the range's keys, kept in
+ * fp32, plus the range's logsumexp; a second kernel then merges the ranges
+ * row by row:
+ *
+ *     LSE = log sum_s exp(LSE_s),    O = sum_s exp(LSE_s - LSE) * O_s.
+ *
+ * The result is attn_fwd's O and LSE up to fp32 rounding order: the
+ * logsumexp that the forward returns for the backward pass (nvFuser issue
+ * #2278, on what to stash) is exactly what makes the ranges mergeable.
+ *
+ * Arguments as attn_fwd, plus:
+ *  - num_splits: number of key ranges.  <= 0 lets the library choose (about
+ *    two workgroups per compute unit of a 256-CU MI355X, and at least four
+ *    key tiles per range); a request above the number of key tiles is cut
+ *    to it.  sdpa_fwd_splitk_plan reports the value a call will use.
+ *  - workspace: DEVICE memory of at least the workspace_bytes that
+ *    sdpa_fwd_splitk_plan reports for the same dtype, sizes and num_splits,
+ *    16-byte aligned and owned by the caller.  Its contents on entry do not
+ *    matter; on return they are scratch.  Calls in flight at the same time
+ *    must not share a workspace.
+ * Returns SDPA_ERR_WORKSPACE for a NULL (when bytes are needed), misaligned
+ * or too small workspace.  Empty problems return SDPA_OK without launching.
+ */
+sdpa_status attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                            sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                            int32_t seqlen_k, int32_t head_dim,
+                            const int64_t q_stride[4], const int64_t k_stride[4],
+                            const int64_t v_stride[4], const int64_t o_stride[4],
+                            float scale, int32_t causal, int32_t num_splits, void* workspace,
+                            uint64_t workspace_bytes, void* hip_stream);
+
+/*
+ * The split count attn_fwd_splitk will use for these sizes and request
+ * (num_splits <= 0: the library's choice) and the workspace bytes it needs:
+ * num_splits_used * B * H * seqlen_q * (head_dim + 1) * 4 plus alignment
+ * padding.  Either output pointer may be NULL.  Errors: SDPA_ERR_DTYPE,
+ * SDPA_ERR_HEAD_DIM, SDPA_ERR_SHAPE (negative or too large sizes).
+ */
+sdpa_status sdpa_fwd_splitk_plan(sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                                 int32_t seqlen_k, int32_t head_dim, int32_t num_splits,
+                                 int32_t* num_splits_used, uint64_t* workspace_bytes);
 
 /*
  * Host-side check of a HOST copy of a cu_seqlens array of n + 1 entries:

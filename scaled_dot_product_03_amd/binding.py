@@ -24,7 +24,7 @@ _BAD_DTYPE = 99  # lets the library report SDPA_ERR_DTYPE itself
 STATUS_NAMES = {
     0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_DTYPE", 3: "SDPA_ERR_HEAD_DIM",
     4: "SDPA_ERR_SHAPE", 5: "SDPA_ERR_STRIDE", 6: "SDPA_ERR_ALIGN", 7: "SDPA_ERR_BATCH",
-    8: "SDPA_ERR_SEQLEN", 9: "SDPA_ERR_SCALE", 10: "SDPA_ERR_HIP",
+    8: "SDPA_ERR_SEQLEN", 9: "SDPA_ERR_SCALE", 10: "SDPA_ERR_HIP", 11: "SDPA_ERR_WORKSPACE",
 }
 
 EXPORTED = (
@@ -32,6 +32,8 @@ EXPORTED = (
     "attn_fwd",
     "attn_fwd_compact_varlen",
     "attn_fwd_padded_varlen",
+    "attn_fwd_splitk",
+    "sdpa_fwd_splitk_plan",
     "sdpa_check_cu_seqlens_host",
     "sdpa_kernel_config",
 )
@@ -80,6 +82,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_padded_varlen.restype = ctypes.c_int
     lib.attn_fwd_padded_varlen.argtypes = (
         [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p] + common_tail)
+    lib.attn_fwd_splitk.restype = ctypes.c_int
+    lib.attn_fwd_splitk.argtypes = (
+        [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _stride, _stride, _stride,
+         _stride, ctypes.c_float, _i32, _i32, _p, ctypes.c_uint64, _p])
+    lib.sdpa_fwd_splitk_plan.restype = ctypes.c_int
+    lib.sdpa_fwd_splitk_plan.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32, _i32p,
+                                         ctypes.POINTER(ctypes.c_uint64)]
     lib.sdpa_check_cu_seqlens_host.restype = ctypes.c_int
     lib.sdpa_check_cu_seqlens_host.argtypes = [_i32p, _i32, _i32, _i32]
     lib.sdpa_kernel_config.restype = ctypes.c_int
@@ -149,6 +158,47 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
         _dtype_code(q), B, H, Sq, Sk, D,
         _strides(q), _strides(k), _strides(v), _strides(o),
         _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    return o, lse
+
+
+def splitk_plan(dtype: torch.dtype, B: int, H: int, seqlen_q: int, seqlen_k: int, head_dim: int,
+                num_splits: int = 0):
+    """(splits used, workspace bytes) of a split forward with these sizes."""
+    lib = load_library()
+    used, nbytes = ctypes.c_int32(), ctypes.c_uint64()
+    _check(lib.sdpa_fwd_splitk_plan(_DTYPE_CODES.get(dtype, _BAD_DTYPE), B, H, seqlen_q, seqlen_k,
+                                    head_dim, int(num_splits), ctypes.byref(used),
+                                    ctypes.byref(nbytes)))
+    return used.value, nbytes.value
+
+
+def attn_fwd_splitk(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None,
+                    workspace=None):
+    """Key-parallel dense forward (same results as attn_fwd).
+
+    q: (B,H,Sq,D), k/v: (B,H,Sk,D).  num_splits <= 0 lets the library pick.
+    The workspace (a uint8 device tensor) is allocated here unless given.
+    Returns (o, lse (B,H,Sq) fp32).
+    """
+    lib = load_library()
+    _require_gpu(q, k, v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    _, nbytes = splitk_plan(q.dtype, B, H, Sq, Sk, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.attn_fwd_splitk(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        _dtype_code(q), B, H, Sq, Sk, D,
+        _strides(q), _strides(k), _strides(v), _strides(o),
+        _scale(scale, D), int(bool(causal)), int(num_splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return o, lse
 
 

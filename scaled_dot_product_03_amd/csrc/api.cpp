@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/sdpa03.h"
 #include "fwd_args.h"
 
@@ -79,6 +81,104 @@ void set_strides(const int64_t* s, int64_t& sb, int64_t& sh, int64_t& ss) {
   ss = s[2];
 }
 
+// Argument checks and kernel arguments of a dense call (attn_fwd and the
+// split forward).  *empty is set when there is no query row to produce.
+sdpa_status dense_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                       sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q, int32_t seqlen_k,
+                       int32_t head_dim, const int64_t q_stride[4], const int64_t k_stride[4],
+                       const int64_t v_stride[4], const int64_t o_stride[4], float scale,
+                       FwdArgs* a, bool* empty) {
+  *empty = false;
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H * seqlen_q == 0) {
+    *empty = true;
+    return SDPA_OK;
+  }
+  if ((st = check_pointers(q, k, v, o, lse, seqlen_k)) != SDPA_OK) return st;
+  const int es = elem_size(dtype);
+  const View vq{q, {B, H, seqlen_q, head_dim}, q_stride};
+  const View vk{k, {B, H, seqlen_k, head_dim}, k_stride};
+  const View vv{v, {B, H, seqlen_k, head_dim}, v_stride};
+  const View vo{o, {B, H, seqlen_q, head_dim}, o_stride};
+  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
+      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
+    return st;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+
+  *a = FwdArgs{};
+  a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
+  a->cu_q = nullptr; a->cu_k = nullptr;
+  set_strides(q_stride, a->q_sb, a->q_sh, a->q_ss);
+  set_strides(k_stride, a->k_sb, a->k_sh, a->k_ss);
+  set_strides(v_stride, a->v_sb, a->v_sh, a->v_ss);
+  set_strides(o_stride, a->o_sb, a->o_sh, a->o_ss);
+  a->lse_sh = seqlen_q;
+  a->lse_sb = static_cast<int64_t>(H) * seqlen_q;
+  a->seqlen_q = seqlen_q;
+  a->seqlen_k = seqlen_k;
+  a->total_q = seqlen_q;
+  a->total_k = seqlen_k;
+  a->num_heads = H;
+  a->num_z = B;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->num_splits = 1;
+  return SDPA_OK;
+}
+
+// Key ranges of a split forward and the workspace they need.  The library
+// aims at two workgroups per compute unit of a 256-CU MI355X and at least
+// kMinTilesPerSplit key tiles per range; the key tiles are then dealt out
+// evenly (every range but possibly the last gets split_tiles tiles).
+constexpr int64_t kSplitTargetWorkgroups = 512;
+constexpr int64_t kMinTilesPerSplit = 4;
+constexpr int64_t kMaxSplits = 256;
+
+struct SplitPlan {
+  int32_t splits;
+  int32_t split_tiles;
+  int32_t m_tiles;
+  int64_t rows;       // B * H * seqlen_q
+  uint64_t o_bytes;   // partial outputs, padded to 256 bytes
+  uint64_t bytes;     // o_bytes + partial logsumexps
+};
+
+sdpa_status split_plan(int dtype, int32_t B, int32_t H, int32_t seqlen_q, int32_t seqlen_k,
+                       int32_t head_dim, int32_t request, SplitPlan* p) {
+  if (!dtype_ok(dtype)) return SDPA_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return SDPA_ERR_HEAD_DIM;
+  if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
+  sdpa03::KernelConfig cfg;
+  if (!sdpa03::split_kernel_config(dtype, head_dim, &cfg)) return SDPA_ERR_HEAD_DIM;
+  const int64_t key_tiles = (static_cast<int64_t>(seqlen_k) + cfg.block_n - 1) / cfg.block_n;
+  const int64_t m_tiles = (static_cast<int64_t>(seqlen_q) + cfg.block_m - 1) / cfg.block_m;
+  const int64_t base = m_tiles * H * B;
+  int64_t splits;
+  if (request <= 0) {
+    splits = base > 0 ? (kSplitTargetWorkgroups + base - 1) / base : 1;
+    splits = std::min(splits, std::max<int64_t>(1, key_tiles / kMinTilesPerSplit));
+  } else {
+    splits = std::min<int64_t>(request, std::max<int64_t>(1, key_tiles));
+  }
+  splits = std::max<int64_t>(1, std::min(splits, kMaxSplits));
+  int64_t split_tiles = 1;
+  if (key_tiles > 0) {
+    split_tiles = (key_tiles + splits - 1) / splits;
+    splits = (key_tiles + split_tiles - 1) / split_tiles;  // no range left empty
+  }
+  const int64_t rows = static_cast<int64_t>(B) * H * seqlen_q;
+  if (rows > (int64_t(1) << 40) / (splits * (head_dim + 1))) return SDPA_ERR_SHAPE;
+  if (base * splits > kMaxGrid) return SDPA_ERR_SHAPE;
+  p->splits = static_cast<int32_t>(splits);
+  p->split_tiles = static_cast<int32_t>(split_tiles);
+  p->m_tiles = static_cast<int32_t>(m_tiles);
+  p->rows = rows;
+  p->o_bytes = (static_cast<uint64_t>(splits * rows * head_dim) * 4 + 255) / 256 * 256;
+  p->bytes = p->o_bytes + static_cast<uint64_t>(splits * rows) * 4;
+  return SDPA_OK;
+}
+
 sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, int mode,
                               int32_t causal, void* stream) {
   sdpa03::KernelConfig cfg;
@@ -109,6 +209,8 @@ const char* sdpa_status_string(sdpa_status status) {
     case SDPA_ERR_SEQLEN: return "invalid sequence-length arguments";
     case SDPA_ERR_SCALE: return "scale must be finite and positive";
     case SDPA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case SDPA_ERR_WORKSPACE:
+      return "split forward workspace is NULL, not 16-byte aligned or smaller than the plan";
   }
   return "unknown status";
 }
@@ -143,38 +245,65 @@ sdpa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int32_t seqlen_k, int32_t head_dim, const int64_t q_stride[4],
                      const int64_t k_stride[4], const int64_t v_stride[4],
                      const int64_t o_stride[4], float scale, int32_t causal, void* hip_stream) {
-  sdpa_status st = check_common(dtype, head_dim, scale);
-  if (st != SDPA_OK) return st;
-  if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H * seqlen_q == 0) return SDPA_OK;
-  if ((st = check_pointers(q, k, v, o, lse, seqlen_k)) != SDPA_OK) return st;
-  const int es = elem_size(dtype);
-  const View vq{q, {B, H, seqlen_q, head_dim}, q_stride};
-  const View vk{k, {B, H, seqlen_k, head_dim}, k_stride};
-  const View vv{v, {B, H, seqlen_k, head_dim}, v_stride};
-  const View vo{o, {B, H, seqlen_q, head_dim}, o_stride};
-  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
-      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
-    return st;
-  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
-
-  FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.cu_q = nullptr; a.cu_k = nullptr;
-  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
-  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
-  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
-  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
-  a.lse_sh = seqlen_q;
-  a.lse_sb = static_cast<int64_t>(H) * seqlen_q;
-  a.seqlen_q = seqlen_q;
-  a.seqlen_k = seqlen_k;
-  a.total_q = seqlen_q;
-  a.total_k = seqlen_k;
-  a.num_heads = H;
-  a.num_z = B;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  FwdArgs a;
+  bool empty;
+  const sdpa_status st = dense_args(q, k, v, o, lse, dtype, B, H, seqlen_q, seqlen_k, head_dim,
+                                    q_stride, k_stride, v_stride, o_stride, scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
   return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_DENSE, causal, hip_stream);
+}
+
+sdpa_status sdpa_fwd_splitk_plan(sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                                 int32_t seqlen_k, int32_t head_dim, int32_t num_splits,
+                                 int32_t* num_splits_used, uint64_t* workspace_bytes) {
+  SplitPlan p;
+  const sdpa_status st = split_plan(dtype, B, H, seqlen_q, seqlen_k, head_dim, num_splits, &p);
+  if (st != SDPA_OK) return st;
+  if (num_splits_used) *num_splits_used = p.splits;
+  if (workspace_bytes) *workspace_bytes = p.bytes;
+  return SDPA_OK;
+}
+
+sdpa_status attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                            sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                            int32_t seqlen_k, int32_t head_dim, const int64_t q_stride[4],
+                            const int64_t k_stride[4], const int64_t v_stride[4],
+                            const int64_t o_stride[4], float scale, int32_t causal,
+                            int32_t num_splits, void* workspace, uint64_t workspace_bytes,
+                            void* hip_stream) {
+  FwdArgs a;
+  bool empty;
+  sdpa_status st = dense_args(q, k, v, o, lse, dtype, B, H, seqlen_q, seqlen_k, head_dim,
+                              q_stride, k_stride, v_stride, o_stride, scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
+  SplitPlan p;
+  if ((st = split_plan(dtype, B, H, seqlen_q, seqlen_k, head_dim, num_splits, &p)) != SDPA_OK)
+    return st;
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 ||
+      workspace_bytes < p.bytes)
+    return SDPA_ERR_WORKSPACE;
+  a.m_tiles = p.m_tiles;
+  a.num_splits = p.splits;
+  a.split_tiles = p.split_tiles;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.o_bytes);
+  a.ws_rows = p.rows;
+  sdpa03::MergeArgs mg{};
+  mg.ws_o = a.ws_o;
+  mg.ws_lse = a.ws_lse;
+  mg.o = o;
+  mg.lse = lse;
+  mg.o_sb = a.o_sb;
+  mg.o_sh = a.o_sh;
+  mg.o_ss = a.o_ss;
+  mg.lse_sb = a.lse_sb;
+  mg.lse_sh = a.lse_sh;
+  mg.ws_rows = p.rows;
+  mg.num_heads = H;
+  mg.seqlen_q = seqlen_q;
+  mg.num_splits = p.splits;
+  const int err = sdpa03::launch_attn_fwd_split(a, mg, dtype, head_dim, causal != 0, hip_stream);
+  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
 }
 
 sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v, void* o,
@@ -225,6 +354,7 @@ sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v,
   a.num_heads = H;
   a.num_z = num_seqs;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_splits = 1;
   return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_COMPACT, causal, hip_stream);
 }
 
@@ -271,6 +401,7 @@ sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, 
   a.num_heads = H;
   a.num_z = B;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_splits = 1;
   return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_PADDED, causal, hip_stream);
 }
 

@@ -514,14 +514,23 @@ struct TileCopy {
 // each XCD runs a contiguous range of logical tiles (whole heads, sharing
 // that XCD's L2), and within a head start with the last query tile (the
 // heaviest one under a causal mask).
-__device__ __forceinline__ void decode_tile(int m_tiles, int num_heads, int& z, int& h, int& m) {
+// In a split forward the splits of one head follow each other, so the
+// workgroups that read one key range of a head share an XCD too.
+template <bool SPLIT>
+__device__ __forceinline__ void decode_tile(int m_tiles, int num_heads, int num_splits, int& z,
+                                            int& h, int& m, int& split) {
   const uint32_t n = blockIdx.x;
   const uint32_t per_xcd = gridDim.x >> 3;
   uint32_t logical = n;
   if (n < (per_xcd << 3)) logical = (n & 7u) * per_xcd + (n >> 3);
   const uint32_t mt = logical % static_cast<uint32_t>(m_tiles);
-  const uint32_t rest = logical / static_cast<uint32_t>(m_tiles);
+  uint32_t rest = logical / static_cast<uint32_t>(m_tiles);
   m = m_tiles - 1 - static_cast<int>(mt);
+  split = 0;
+  if constexpr (SPLIT) {
+    split = static_cast<int>(rest % static_cast<uint32_t>(num_splits));
+    rest /= static_cast<uint32_t>(num_splits);
+  }
   h = static_cast<int>(rest % static_cast<uint32_t>(num_heads));
   z = static_cast<int>(rest / static_cast<uint32_t>(num_heads));
 }
@@ -578,10 +587,14 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 // STAGES LDS buffers each for K and V tiles (2 or 3).  With 3, a tile load
 // issued at step t is first needed at step t+2, so it has two steps of
 // compute to hide its latency behind.
-template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL>
+// SPLIT: key-parallel dense forward.  The workgroup covers the key tiles of
+// its split only and writes a normalised fp32 partial output and its
+// logsumexp to the workspace; a second kernel merges the splits.
+template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_lds1, T* k_lds2,
                                               T* v_lds0, T* v_lds1, T* v_lds2) {
   static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  static_assert(!SPLIT || MODE == MODE_DENSE, "the split forward serves the dense mode");
   using Path = typename PathFor<T, D>::type;
   using KCopy = TileCopy<T, D, BN, NW, Path::kRowK>;
   using VCopy = TileCopy<T, D, BN, NW, Path::kRowV>;
@@ -594,8 +607,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   constexpr int kLoadsPerStep = KCopy::kInstPerWave + VCopy::kInstPerWave;
   constexpr int kInFlightAtStepEnd = (STAGES - 2) * kLoadsPerStep;
 
-  int z, h, m;
-  decode_tile(a.m_tiles, a.num_heads, z, h, m);
+  int z, h, m, split;
+  decode_tile<SPLIT>(a.m_tiles, a.num_heads, a.num_splits, z, h, m, split);
   const SeqRange sr = seq_range<MODE>(a, z);
   const int m0 = m * BM;
   if (m0 >= sr.len_q) return;  // uniform over the workgroup
@@ -624,7 +637,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
 
   int kend = sr.len_k;
   if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, sr.len_q));
-  const int n_tiles = (kend + BN - 1) / BN;
+  // Key tiles [tile0, tile0 + n_tiles): all of them, or this split's share
+  // (possibly none: an empty split still writes its partial result).
+  int tile0 = 0;
+  int n_tiles = (kend + BN - 1) / BN;
+  if constexpr (SPLIT) {
+    tile0 = split * a.split_tiles;
+    n_tiles = max(0, min(n_tiles - tile0, a.split_tiles));
+  }
 
   const int64_t k_row_bytes = a.k_ss * static_cast<int64_t>(sizeof(T));
   const int64_t v_row_bytes = a.v_ss * static_cast<int64_t>(sizeof(T));
@@ -637,11 +657,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   // access refers to a known array.  Rows at or past `end` are not fetched
   // (they read back as zeros); a load past the last tile fetches nothing.
   auto issue_k = [&](int t, T* buf, int end) {
-    const int j0 = t * BN;
+    const int j0 = (tile0 + t) * BN;
     kcopy.issue(kp + j0 * k_row_bytes, end - j0, k_row_bytes, buf, wave);
   };
   auto issue_v = [&](int t, T* buf, int end) {
-    const int j0 = t * BN;
+    const int j0 = (tile0 + t) * BN;
     vcopy.issue(vp + j0 * v_row_bytes, end - j0, v_row_bytes, buf, wave);
   };
 
@@ -658,7 +678,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   // Masks the scores of tile t where keys run past the sequence or, under
   // the causal mask, past the lane's row (only tail and diagonal tiles).
   auto mask_tile = [&](int t, f32x16 (&s)[NB]) {
-    const int j0 = t * BN;
+    const int j0 = (tile0 + t) * BN;
     const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0);
     if (need_mask) {
 #pragma unroll
@@ -798,6 +818,24 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
   const float l_tot = sum_across_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if constexpr (SPLIT) {
+    if (row_ok) {
+      const int64_t row = (static_cast<int64_t>(split) * a.num_z + z) * a.num_heads * sr.len_q +
+                          static_cast<int64_t>(h) * sr.len_q + qi;
+      float* wrow = a.ws_o + row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          *reinterpret_cast<f32x4*>(wrow + db * 32 + g * 8 + lh * 4) =
+              f32x4{acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
+                    acc[db][4 * g + 3] * inv};
+        }
+      }
+      if (lh == 0) a.ws_lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   if (row_ok) {
     T* orow = op + static_cast<int64_t>(qi) * a.o_ss;
 #pragma unroll
@@ -862,8 +900,8 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
   constexpr int kLoadsPerTile = KCopy::kInstPerWave + VCopy::kInstPerWave;
   constexpr int kInFlight = (STAGES - 2) * kLoadsPerTile;
 
-  int z, h, m;
-  decode_tile(a.m_tiles, a.num_heads, z, h, m);
+  int z, h, m, split;
+  decode_tile<false>(a.m_tiles, a.num_heads, 1, z, h, m, split);
   const SeqRange sr = seq_range<MODE>(a, z);
   const int m0 = m * BM;
   if (m0 >= sr.len_q) return;  // uniform over the workgroup
@@ -1089,7 +1127,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pingpong_kernel(FwdArgs a) {
 // gets its own alias scope, so the compiler can see that fragment reads of
 // one buffer do not depend on the buffer loads still landing in another,
 // and need not wait for them.
-template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL>
+template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   using Path = typename PathFor<T, D>::type;
   constexpr int kKElems = TileCopy<T, D, BN, NW, Path::kRowK>::kArrayBytes / static_cast<int>(sizeof(T));
@@ -1101,12 +1139,62 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   if constexpr (STAGES > 2) {
     __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
     __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
-    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds2, v_lds0, v_lds1,
-                                                      v_lds2);
+    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL, SPLIT>(a, k_lds0, k_lds1, k_lds2, v_lds0,
+                                                             v_lds1, v_lds2);
   } else {
-    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds0, v_lds0, v_lds1,
-                                                      v_lds0);
+    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL, SPLIT>(a, k_lds0, k_lds1, k_lds0, v_lds0,
+                                                             v_lds1, v_lds0);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of a split forward
+// ---------------------------------------------------------------------------
+// Split s of a row holds O_s (normalised over its own keys) and LSE_s.  The
+// row's result is LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE)
+// O_s: each O_s is a softmax-weighted mean over its keys, and exp(LSE_s) is
+// the total weight of those keys.  A split that saw no key has LSE_s = -inf
+// and weight 0; a row with no key at all gets O = 0 and LSE = -inf.  One
+// thread per (row, 4 consecutive dims); the work is a few bytes of traffic
+// per output element, bounded by HBM.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeArgs a) {
+  constexpr int kChunks = D / 4;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid / kChunks;
+  if (row >= a.ws_rows) return;
+  const int c = static_cast<int>(gid % kChunks);
+  float m = kNegInf;
+  for (int sp = 0; sp < a.num_splits; ++sp) m = fmaxf(m, a.ws_lse[sp * a.ws_rows + row]);
+  float w_sum = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m != kNegInf) {
+    for (int sp = 0; sp < a.num_splits; ++sp) {
+      const int64_t r = sp * a.ws_rows + row;
+      const float w = expf(a.ws_lse[r] - m);
+      const f32x4 part = *reinterpret_cast<const f32x4*>(a.ws_o + r * D + 4 * c);
+      w_sum += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, part[e], acc[e]);
+    }
+  }
+  const float inv = w_sum > 0.f ? 1.f / w_sum : 0.f;
+  const int64_t i = row % a.seqlen_q;
+  const int64_t zh = row / a.seqlen_q;
+  const int64_t h = zh % a.num_heads;
+  const int64_t z = zh / a.num_heads;
+  T* dst = static_cast<T*>(a.o) + z * a.o_sb + h * a.o_sh + i * a.o_ss + 4 * c;
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  } else {
+    T out4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out4[e] = static_cast<T>(acc[e] * inv);
+    uint2 packed;
+    __builtin_memcpy(&packed, out4, 8);
+    *reinterpret_cast<uint2*>(dst) = packed;
+  }
+  if (c == 0) a.lse[z * a.lse_sb + h * a.lse_sh + i] = m == kNegInf ? kNegInf : m + logf(w_sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,9 +1214,24 @@ int launch_typed(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_fwd_pingpong_kernel<T, D, e.block_n, e.stages, MODE, CAUSAL>),
                        dim3(grid), dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL>),
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL, false>),
                        dim3(grid), dim3(e.waves * 64), 0, stream, a);
   }
+  return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, int D, bool CAUSAL>
+int launch_split_typed(const FwdArgs& a, const MergeArgs& mg, hipStream_t stream) {
+  constexpr TableEntry e = split_entry<T, D>();
+  const uint32_t grid =
+      static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z * static_cast<uint32_t>(a.num_splits);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE_DENSE, CAUSAL, true>),
+                     dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  int err = static_cast<int>(hipGetLastError());
+  if (err != 0) return err;
+  const int64_t threads = mg.ws_rows * (D / 4);
+  hipLaunchKernelGGL((attn_fwd_merge_kernel<T, D>), dim3(static_cast<uint32_t>((threads + 255) / 256)),
+                     dim3(256), 0, stream, mg);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1166,6 +1269,38 @@ bool kernel_config(int dtype, int head_dim, bool causal, int mode, KernelConfig*
   cfg->block_n = e.block_n;
   cfg->waves = e.waves;
   return true;
+}
+
+bool split_kernel_config(int dtype, int head_dim, KernelConfig* cfg) {
+  if (head_dim != 64 && head_dim != 128) return false;
+  TableEntry e;
+  switch (dtype) {
+    case DT_F32: e = head_dim == 64 ? split_entry<float, 64>() : split_entry<float, 128>(); break;
+    case DT_F16: e = head_dim == 64 ? split_entry<_Float16, 64>() : split_entry<_Float16, 128>(); break;
+    case DT_BF16: e = head_dim == 64 ? split_entry<__bf16, 64>() : split_entry<__bf16, 128>(); break;
+    default: return false;
+  }
+  cfg->block_m = e.waves * 32;
+  cfg->block_n = e.block_n;
+  cfg->waves = e.waves;
+  return true;
+}
+
+int launch_attn_fwd_split(const FwdArgs& a, const MergeArgs& mg, int dtype, int head_dim,
+                          bool causal, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto by_dim = [&](auto tag) {
+    using T = decltype(tag);
+    if (head_dim == 64) {
+      return causal ? launch_split_typed<T, 64, true>(a, mg, s) : launch_split_typed<T, 64, false>(a, mg, s);
+    }
+    return causal ? launch_split_typed<T, 128, true>(a, mg, s) : launch_split_typed<T, 128, false>(a, mg, s);
+  };
+  switch (dtype) {
+    case DT_F32: return by_dim(float{});
+    case DT_F16: return by_dim(_Float16{});
+    default: return by_dim(__bf16{});
+  }
 }
 
 int launch_attn_fwd(const FwdArgs& a, int dtype, int head_dim, int mode, bool causal, void* stream) {

@@ -31,6 +31,29 @@ struct FwdArgs {
   int32_t num_z;      // batches (dense, padded) or sequences (compact)
   int32_t m_tiles;    // ceil(seqlen_q / block_m)
   float scale_log2;   // scale * log2(e): scores go straight into exp2
+  // Key-parallel (split) dense forward only: split s of a query tile covers
+  // key tiles [s * split_tiles, (s + 1) * split_tiles) and writes its
+  // normalised fp32 partial output and its logsumexp to the workspace.
+  int32_t num_splits;     // 1 outside split mode
+  int32_t split_tiles;
+  float* ws_o;            // [split][z][h][row][head_dim]
+  float* ws_lse;          // [split][z][h][row]
+  int64_t ws_rows;        // rows per split: num_z * num_heads * seqlen_q
+};
+
+// Arguments of the kernel that merges the partial results of a split
+// forward into O and LSE.
+struct MergeArgs {
+  const float* ws_o;
+  const float* ws_lse;
+  void* o;
+  float* lse;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t lse_sb, lse_sh;
+  int64_t ws_rows;
+  int32_t num_heads;
+  int32_t seqlen_q;
+  int32_t num_splits;
 };
 
 // One compiled kernel shape.
@@ -43,9 +66,17 @@ struct KernelConfig {
 // Picks the compiled kernel for a problem class; false if unsupported.
 bool kernel_config(int dtype, int head_dim, bool causal, int mode, KernelConfig* cfg);
 
+// The kernel shape of the split dense forward for (dtype, head_dim).
+bool split_kernel_config(int dtype, int head_dim, KernelConfig* cfg);
+
 // Launches the forward on `stream` (a hipStream_t).  Returns the HIP error
 // code of the launch (0 on success).  Arguments are assumed validated.
 int launch_attn_fwd(const FwdArgs& args, int dtype, int head_dim, int mode, bool causal,
                     void* stream);
+
+// Split dense forward: the partial kernel (grid m_tiles * heads * batches *
+// splits), then the merge kernel, both on `stream`.
+int launch_attn_fwd_split(const FwdArgs& args, const MergeArgs& merge, int dtype, int head_dim,
+                          bool causal, void* stream);
 
 }  // namespace sdpa03

@@ -36,7 +36,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fwd_compact_varlen", "attn_fwd_padded_varlen", "sdpa_status_string"):
+    for n in ("attn_fwd", "attn_fwd_compact_varlen", "attn_fwd_padded_varlen", "attn_fwd_splitk",
+              "sdpa_fwd_splitk_plan", "sdpa_status_string"):
         assert n in names
     assert set(names) == set(binding.EXPORTED)
 
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = binding.load_library()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = lib.sdpa_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.sdpa_status_string(123).decode() == "unknown status"
@@ -149,3 +150,58 @@ def test_padded_validation(kw, status):
     r = lib.attn_fwd_padded_varlen(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, a["dtype"], a["B"], 2, 32,
                                    32, 64, a["cu_q"], a["cu_k"], st, st, st, st, 0.125, 0, None)
     assert r == status
+
+
+# --- split (key-parallel) forward: plan and validation ----------------------
+
+def test_splitk_plan():
+    bf, f16 = torch.bfloat16, torch.float16
+    # 512 queries x 8192 keys, fp16 D64: 4 query tiles x 32 heads x 2 batches = 256
+    # workgroups; the library aims at 512, so two ranges of 64 key tiles each
+    used, nbytes = binding.splitk_plan(f16, 2, 32, 512, 8192, 64)
+    rows = 2 * 32 * 512
+    assert used == 2
+    assert nbytes == 2 * rows * 64 * 4 + 2 * rows * 4
+    # a request is cut to the key tiles and then dealt out without empty ranges
+    _, bn, _ = binding.kernel_config(bf, 128)
+    tiles = lambda sk: -(-sk // bn)
+    assert binding.splitk_plan(bf, 1, 1, 64, 100, 128, 1000)[0] == tiles(100)
+    assert binding.splitk_plan(bf, 1, 1, 64, 10 * bn, 128, 4)[0] == 4   # 3+3+3+1 tiles
+    assert binding.splitk_plan(bf, 1, 1, 64, 10 * bn, 128, 6)[0] == 5   # 2 tiles each
+    assert binding.splitk_plan(bf, 1, 1, 64, 0, 128, 8)[0] == 1
+    # enough query tiles already: no split by default
+    assert binding.splitk_plan(bf, 4, 16, 2048, 2048, 128)[0] == 1
+    # the workspace grows with the split count and head_dim + 1 floats per row
+    u, nb = binding.splitk_plan(bf, 1, 2, 100, 64 * bn, 64, 8)
+    assert u == 8 and nb >= 8 * 200 * 65 * 4
+    for bad in [dict(dtype=torch.float64), dict(D=96), dict(B=-1)]:
+        a = dict(dtype=bf, B=1, H=1, D=64)
+        a.update(bad)
+        with pytest.raises(binding.SdpaError):
+            binding.splitk_plan(a["dtype"], a["B"], 1, 10, 10, a["D"])
+
+
+def _splitk(**kw):
+    lib = binding.load_library()
+    a = dict(q=DUMMY, k=DUMMY, v=DUMMY, o=DUMMY, lse=DUMMY, dtype=2, B=1, H=2, Sq=8, Sk=512,
+             D=64, scale=0.125, splits=4, ws=DUMMY, ws_bytes=1 << 30)
+    a.update(kw)
+    st = _st(1024 * 64, 512 * 64, 64, 1)
+    return lib.attn_fwd_splitk(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dtype"], a["B"],
+                               a["H"], a["Sq"], a["Sk"], a["D"], st, st, st, st, a["scale"], 0,
+                               a["splits"], a["ws"], a["ws_bytes"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), 11), (dict(ws=DUMMY + 8), 11), (dict(ws_bytes=64), 11),
+    (dict(q=None), 1), (dict(D=32), 3), (dict(dtype=5), 2), (dict(scale=0.0), 9),
+    (dict(Sk=-1), 4),
+])
+def test_splitk_validation(kw, status):
+    assert _splitk(**kw) == status
+
+
+@no_gpu
+def test_splitk_empty_problem_is_ok_without_launch():
+    assert _splitk(q=None, ws=None, Sq=0) == 0
