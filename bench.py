@@ -9,9 +9,11 @@ non-causal forward followed by the causal forward (both masks of that
 workload), inputs resident in HBM.  FLOPs are 4*Sq*Sk*D*H*B per forward,
 halved for causal.  The line also carries the compact varlen THD workload
 (16 sequences, lengths U{1..4096} from seed 4, H=16, D=128, bf16, causal)
-timed the same way, a roofline record for the dominant kernel (the
-non-causal forward, timed per launch with HIP events on the stream it runs
-on) and the float64 CPU oracle timed on a bounded sample of the same
+and the fp16 B=2, H=32, Sq=512, Sk=8192, D=64 workload (through attn_fwd
+and through the key-parallel attn_fwd_splitk) timed the same way, a
+roofline record for the dominant kernel (the
+non-causal forward, timed with HIP events on the stream it runs on around the
+block of its back-to-back launches) and the float64 CPU oracle timed on a bounded sample of the same
 workload.
 
 Prints ONE JSON line on stdout.
@@ -126,6 +128,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (a kernel of "
                          "known HBM traffic, for scaling counter readings)")
@@ -155,15 +158,15 @@ def main():
     f_nc = dense_flops(B, H, Sq, Sk, D, False)
     f_c = dense_flops(B, H, Sq, Sk, D, True)
 
-    def step(events=None):
-        if events is not None:
-            events[0].record(stream)
+    def fwd_noncausal():
         binding.attn_fwd(q, k, v, scale=x.scale, causal=False, out=o, lse=lse)
-        if events is not None:
-            events[1].record(stream)
+
+    def fwd_causal():
         binding.attn_fwd(q, k, v, scale=x.scale, causal=True, out=o, lse=lse)
-        if events is not None:
-            events[2].record(stream)
+
+    def step():
+        fwd_noncausal()
+        fwd_causal()
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -180,33 +183,51 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The timed region runs the K steps' non-causal forwards back to back, then
+    # their causal forwards, with HIP events on the launch stream only at the
+    # three block boundaries: per-launch events would add each launch's
+    # dispatch latency to the kernel average.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        fwd_noncausal()
+    ev[1].record(stream)
+    for _ in range(args.steps):
+        fwd_causal()
+    ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    nc_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    c_ms = [e[1].elapsed_time(e[2]) for e in evs]
     log(f"timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step")
 
     ms_per_step = wall * 1e3 / args.steps
     value = (f_nc + f_c) / (ms_per_step * 1e-3) / 1e12
-    nc_avg = float(np.mean(nc_ms))
-    c_avg = float(np.mean(c_ms))
+    nc_avg = ev[0].elapsed_time(ev[1]) / args.steps
+    c_avg = ev[1].elapsed_time(ev[2]) / args.steps
     achieved = f_nc / (nc_avg * 1e-3) / 1e12
     traffic = traffic_from_profiles("dense_bf16_b4h16s2048d128_noncausal")
 
     breakdown = {
-        "noncausal": {"flops": f_nc, "avg_ms": nc_avg, "median_ms": float(np.median(nc_ms)),
-                      "min_ms": float(np.min(nc_ms)), "tflops": achieved,
+        "noncausal": {"flops": f_nc, "avg_ms": nc_avg, "tflops": achieved,
                       "pct_mfma_peak": 100 * achieved / PEAK_BF16_TFLOPS},
-        "causal": {"flops": f_c, "avg_ms": c_avg, "median_ms": float(np.median(c_ms)),
-                   "min_ms": float(np.min(c_ms)),
-                   "tflops": f_c / (c_avg * 1e-3) / 1e12,
+        "causal": {"flops": f_c, "avg_ms": c_avg, "tflops": f_c / (c_avg * 1e-3) / 1e12,
                    "pct_mfma_peak": 100 * f_c / (c_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
+
+    def block_ms(call):
+        """Average ms of `call` over args.steps back-to-back calls (after warmup),
+        from two HIP events on the launch stream."""
+        for _ in range(args.warmup):
+            call()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        for _ in range(args.steps):
+            call()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / args.steps
 
     if not args.no_varlen:
         vx = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
@@ -216,25 +237,38 @@ def main():
         maxlen = int(max(lengths))
         vo = torch.empty_like(vq)
         vlse = torch.empty((1, vq.shape[1], vq.shape[0]), dtype=torch.float32, device=dev)
-        for _ in range(args.warmup):
-            binding.attn_fwd_compact_varlen(vq, vk, vv, cu, cu, maxlen, maxlen, scale=vx.scale,
-                                            causal=True, out=vo, lse=vlse)
-        ve = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            ve[i][0].record(stream)
-            binding.attn_fwd_compact_varlen(vq, vk, vv, cu, cu, maxlen, maxlen, scale=vx.scale,
-                                            causal=True, out=vo, lse=vlse)
-            ve[i][1].record(stream)
-        torch.cuda.synchronize()
-        v_ms = [a.elapsed_time(b) for a, b in ve]
+        v_avg = block_ms(lambda: binding.attn_fwd_compact_varlen(
+            vq, vk, vv, cu, cu, maxlen, maxlen, scale=vx.scale, causal=True, out=vo, lse=vlse))
         vf = varlen_flops(lengths, vq.shape[1], vq.shape[2], True)
         breakdown["varlen_thd_causal"] = {
             "workload": "thd_bf16_16seq_len1to4096_h16d128_causal (seed 4, T=%d)" % vq.shape[0],
-            "flops": vf, "avg_ms": float(np.mean(v_ms)), "median_ms": float(np.median(v_ms)),
-            "tflops": vf / (np.mean(v_ms) * 1e-3) / 1e12,
-            "pct_mfma_peak": 100 * vf / (np.mean(v_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            "flops": vf, "avg_ms": v_avg, "tflops": vf / (v_avg * 1e-3) / 1e12,
+            "pct_mfma_peak": 100 * vf / (v_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del vq, vk, vv, vo, vlse
+
+    if not args.no_splitk:
+        sx = inputs.workload("dense_fp16_b2h32sq512sk8192d64")
+        sq, sk, sv = sx.q.to(dev), sx.k.to(dev), sx.v.to(dev)
+        sB, sH, sSq, sD = sq.shape
+        sSk = sk.shape[2]
+        splits, nbytes = binding.splitk_plan(sq.dtype, sB, sH, sSq, sSk, sD)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        so = torch.empty_like(sq)
+        slse = torch.empty((sB, sH, sSq), dtype=torch.float32, device=dev)
+        calls = {
+            "attn_fwd": lambda: binding.attn_fwd(sq, sk, sv, scale=sx.scale, out=so, lse=slse),
+            "attn_fwd_splitk": lambda: binding.attn_fwd_splitk(sq, sk, sv, scale=sx.scale, out=so,
+                                                               lse=slse, workspace=ws),
+        }
+        sf = dense_flops(sB, sH, sSq, sSk, sD, False)
+        entry = {"workload": "dense_fp16_b2h32sq512sk8192d64 (seed 3), non-causal",
+                 "flops": sf, "splits": splits}
+        for name, call in calls.items():
+            s_avg = block_ms(call)
+            entry[name] = {"avg_ms": s_avg, "tflops": sf / (s_avg * 1e-3) / 1e12,
+                           "pct_mfma_peak": 100 * sf / (s_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        breakdown["dense_fp16_sq512_sk8192"] = entry
+        del sq, sk, sv, so, slse, ws
 
     bm, bn, waves = binding.kernel_config(torch.bfloat16, D)
     record = {
