@@ -510,16 +510,41 @@ struct TileCopy {
 // Tile bookkeeping
 // ---------------------------------------------------------------------------
 
-// Workgroups are dealt round-robin to the 8 XCDs.  Remap the launch index so
-// each XCD runs a contiguous range of logical tiles (whole heads, sharing
-// that XCD's L2), and within a head start with the last query tile (the
-// heaviest one under a causal mask).
-// In a split forward the splits of one head follow each other, so the
-// workgroups that read one key range of a head share an XCD too.
-template <bool SPLIT>
-__device__ __forceinline__ void decode_tile(int m_tiles, int num_heads, int num_splits, int& z,
-                                            int& h, int& m, int& split) {
+// Workgroups are dealt round-robin to the 8 XCDs, in launch order.
+//
+// Without a causal mask every query tile costs the same: the launch index
+// is remapped so each XCD runs a contiguous range of logical tiles (whole
+// heads, sharing that XCD's L2).  In a split forward the splits of one head
+// follow each other, so the workgroups that read one key range of a head
+// share an XCD too.
+//
+// Under a causal mask query tile m costs m + 1 key tiles.  Heaviest-first
+// within each head still leaves long tiles starting late (a model of 64
+// workgroup slots puts the makespan at 1.5 times the average load); here the
+// launch index runs over (batch, head[, split]) fastest and over query tiles
+// from the last one down, so all the heaviest tiles start first.  Consecutive
+// launch indices walk the heads and land on consecutive XCDs, so every XCD
+// gets the same mix of tile costs, and with a multiple of 8 (batch, head)
+// groups each head stays on one XCD.
+template <bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void decode_tile(int m_tiles, int num_heads, int num_z, int num_splits,
+                                            int& z, int& h, int& m, int& split) {
   const uint32_t n = blockIdx.x;
+  if constexpr (CAUSAL) {
+    const uint32_t per_split = static_cast<uint32_t>(num_heads) * static_cast<uint32_t>(num_z);
+    const uint32_t groups = SPLIT ? per_split * static_cast<uint32_t>(num_splits) : per_split;
+    const uint32_t g = n % groups;
+    m = m_tiles - 1 - static_cast<int>(n / groups);
+    uint32_t rest = g;
+    split = 0;
+    if constexpr (SPLIT) {
+      split = static_cast<int>(rest % static_cast<uint32_t>(num_splits));
+      rest /= static_cast<uint32_t>(num_splits);
+    }
+    h = static_cast<int>(rest % static_cast<uint32_t>(num_heads));
+    z = static_cast<int>(rest / static_cast<uint32_t>(num_heads));
+    return;
+  }
   const uint32_t per_xcd = gridDim.x >> 3;
   uint32_t logical = n;
   if (n < (per_xcd << 3)) logical = (n & 7u) * per_xcd + (n >> 3);
@@ -608,7 +633,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   constexpr int kInFlightAtStepEnd = (STAGES - 2) * kLoadsPerStep;
 
   int z, h, m, split;
-  decode_tile<SPLIT>(a.m_tiles, a.num_heads, a.num_splits, z, h, m, split);
+  decode_tile<CAUSAL, SPLIT>(a.m_tiles, a.num_heads, a.num_z, a.num_splits, z, h, m, split);
   const SeqRange sr = seq_range<MODE>(a, z);
   const int m0 = m * BM;
   if (m0 >= sr.len_q) return;  // uniform over the workgroup
@@ -901,7 +926,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
   constexpr int kInFlight = (STAGES - 2) * kLoadsPerTile;
 
   int z, h, m, split;
-  decode_tile<false>(a.m_tiles, a.num_heads, 1, z, h, m, split);
+  decode_tile<CAUSAL, false>(a.m_tiles, a.num_heads, a.num_z, 1, z, h, m, split);
   const SeqRange sr = seq_range<MODE>(a, z);
   const int m0 = m * BM;
   if (m0 >= sr.len_q) return;  // uniform over the workgroup
