@@ -201,3 +201,133 @@ def sdpa_padded_varlen(q, k, v, cu_q, cu_k, scale, causal):
             out[b, h, : lq[b]] = o_bh
             lse[b, h, : lq[b]] = lse_bh
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+# The nvFuser issue #2278 (Priya2698's meeting summary) needs an SdpaOpBwd node
+# next to the forward one, and AOTriton PR #31 (opening comment) pairs every
+# varlen forward API with a backward one.  The backward of the definition
+# above, for an upstream gradient dO of O (the loss is sum(dO * O)), is the
+# plain chain rule through O = P V, the row softmax P = softmax(S) over the
+# allowed keys, and S = scale * Q K^T:
+#
+#     dV      = P^T dO
+#     dP      = dO V^T
+#     delta_i = sum_j P_ij dP_ij  (= sum_d dO_id O_id)
+#     dS      = P * (dP - delta[:, None])        (0 where not allowed)
+#     dQ      = scale * dS K
+#     dK      = scale * dS^T Q
+#
+# A row with no allowed key has P = 0 and contributes nothing.
+
+__all__ += [
+    "attention_head_bwd",
+    "sdpa_dense_bwd",
+    "sdpa_compact_varlen_bwd",
+    "sdpa_padded_varlen_bwd",
+]
+
+
+def attention_head_bwd(q, k, v, do, scale, causal):
+    """Gradients of one (sequence, head) in float64.
+
+    q: (Lq, D), k: (Lk, D), v: (Lk, Dv), do: (Lq, Dv).  Returns
+    ``(dQ, dK, dV)`` shaped like q, k and v.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    lq, lk = q.shape[0], k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if lq == 0 or lk == 0:
+        return dq, dk, dv
+    # The forward's normalised weights P, step by step as in attention_head.
+    s = float(scale) * (q @ k.T)
+    allowed = np.ones((lq, lk), dtype=bool)
+    if causal:
+        allowed = np.arange(lk)[None, :] <= np.arange(lq)[:, None]
+    has_key = allowed.any(axis=1)
+    s_masked = np.where(allowed, s, -np.inf)
+    m = np.where(has_key, s_masked.max(axis=1), 0.0)
+    p = np.where(allowed, np.exp(s_masked - m[:, None]), 0.0)
+    l = np.where(has_key, p.sum(axis=1), 1.0)
+    p = p / l[:, None]
+    # Chain rule, one library matmul per product.
+    dv = p.T @ do
+    dp = do @ v.T
+    delta = (p * dp).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv
+
+
+def sdpa_dense_bwd(q, k, v, do, scale, causal, heads=None):
+    """Dense BHSD backward: returns (dQ, dK, dV) shaped like q, k, v.
+
+    ``heads`` optionally restricts the work to a list of (b, h) pairs; the
+    other entries are left as NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    b_, h_ = q.shape[:2]
+    pairs = [(b, h) for b in range(b_) for h in range(h_)] if heads is None else heads
+    for b, h in pairs:
+        dq[b, h], dk[b, h], dv[b, h] = attention_head_bwd(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                          scale, causal)
+    return dq, dk, dv
+
+
+def sdpa_compact_varlen_bwd(q, k, v, do, cu_q, cu_k, scale, causal):
+    """Compact varlen backward over packed THD tokens (q, do: (Tq,H,D); k, v:
+    (Tk,H,D)).  Tokens outside every sequence get zero gradients."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    lengths_from_cu(cu_q, q.shape[0])
+    lengths_from_cu(cu_k, k.shape[0])
+    if cu_q.size != cu_k.size:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same sequence count")
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for z in range(cu_q.size - 1):
+        qs, qe = cu_q[z], cu_q[z + 1]
+        ks, ke = cu_k[z], cu_k[z + 1]
+        for h in range(q.shape[1]):
+            g = attention_head_bwd(q[qs:qe, h], k[ks:ke, h], v[ks:ke, h], do[qs:qe, h], scale,
+                                   causal)
+            dq[qs:qe, h], dk[ks:ke, h], dv[ks:ke, h] = g
+    return dq, dk, dv
+
+
+def sdpa_padded_varlen_bwd(q, k, v, do, cu_q, cu_k, scale, causal):
+    """Padded varlen backward over rank-4 slabs; rows and keys past a batch's
+    true length get zero gradients (they do not affect any output)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    lq = lengths_from_cu(cu_q)
+    lk = lengths_from_cu(cu_k)
+    b_, h_ = q.shape[:2]
+    if lq.size != b_ or lk.size != b_:
+        raise ValueError("padded varlen needs B+1 cu_seqlens entries")
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(b_):
+        for h in range(h_):
+            g = attention_head_bwd(q[b, h, : lq[b]], k[b, h, : lk[b]], v[b, h, : lk[b]],
+                                   do[b, h, : lq[b]], scale, causal)
+            dq[b, h, : lq[b]], dk[b, h, : lk[b]], dv[b, h, : lk[b]] = g
+    return dq, dk, dv
