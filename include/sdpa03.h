@@ -213,6 +213,46 @@ sdpa_status sdpa_fwd_splitk_plan(sdpa_dtype dtype, int32_t B, int32_t H, int32_t
                                  int32_t* num_splits_used, uint64_t* workspace_bytes);
 
 /*
+ * Dense backward (bf16 and fp16).  The nvFuser issue #2278 pairs the forward
+ * SDPA node with an SdpaOpBwd node; AOTriton PR #31 pairs each forward API
+ * with a backward one.  Given the forward's inputs q, k, v, its outputs o
+ * and lse (as attn_fwd returns them, lse contiguous (B, H, seqlen_q) fp32)
+ * and the gradient dout of o, it writes the gradients of
+ * loss = sum(dout * o):
+ *
+ *     P = softmax over allowed keys of scale * q k^T   (rebuilt from lse)
+ *     dv = P^T dout,   dS = P * (dout v^T - rowsum(dout * o)),
+ *     dq = scale * dS k,   dk = scale * dS^T q.
+ *
+ * dq, dk and dv have the shapes and strides of q, k and v; dout has its own
+ * strides.  Same mask convention as attn_fwd.  Every row of dq, dk and dv is
+ * written (zeros where no allowed pair contributes); the results are
+ * deterministic (no atomics).
+ *
+ * workspace: DEVICE memory of at least sdpa_bwd_workspace_bytes(B, H,
+ * seqlen_q) bytes, 16-byte aligned, caller-owned scratch (it holds
+ * rowsum(dout * o) and lse * log2(e) per query row).  Calls in flight at the
+ * same time must not share it.
+ * Errors as attn_fwd; SDPA_ERR_DTYPE for fp32 (not supported by the
+ * backward); SDPA_ERR_WORKSPACE for a NULL, misaligned or small workspace.
+ */
+sdpa_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                     int32_t seqlen_k, int32_t head_dim,
+                     const int64_t q_stride[4], const int64_t k_stride[4],
+                     const int64_t v_stride[4], const int64_t o_stride[4],
+                     const int64_t dout_stride[4], float scale, int32_t causal,
+                     void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/*
+ * Workspace bytes attn_bwd needs: 2 * B * H * roundup(seqlen_q, 64) * 4.
+ * SDPA_ERR_SHAPE for negative sizes.
+ */
+sdpa_status sdpa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t seqlen_q,
+                                     uint64_t* workspace_bytes);
+
+/*
  * Host-side check of a HOST copy of a cu_seqlens array of n + 1 entries:
  * starts at 0, non-decreasing, last entry <= total, every length <=
  * max_len.  Returns SDPA_OK or SDPA_ERR_SEQLEN (SDPA_ERR_NULL for NULL).

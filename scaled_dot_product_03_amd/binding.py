@@ -34,6 +34,8 @@ EXPORTED = (
     "attn_fwd_padded_varlen",
     "attn_fwd_splitk",
     "sdpa_fwd_splitk_plan",
+    "attn_bwd",
+    "sdpa_bwd_workspace_bytes",
     "sdpa_check_cu_seqlens_host",
     "sdpa_kernel_config",
 )
@@ -89,6 +91,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sdpa_fwd_splitk_plan.restype = ctypes.c_int
     lib.sdpa_fwd_splitk_plan.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32, _i32p,
                                          ctypes.POINTER(ctypes.c_uint64)]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = (
+        [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
+         _stride, _stride, _stride, _stride, _stride, ctypes.c_float, _i32, _p, ctypes.c_uint64,
+         _p])
+    lib.sdpa_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.sdpa_bwd_workspace_bytes.argtypes = [_i32, _i32, _i32, ctypes.POINTER(ctypes.c_uint64)]
     lib.sdpa_check_cu_seqlens_host.restype = ctypes.c_int
     lib.sdpa_check_cu_seqlens_host.argtypes = [_i32p, _i32, _i32, _i32]
     lib.sdpa_kernel_config.restype = ctypes.c_int
@@ -200,6 +209,46 @@ def attn_fwd_splitk(q, k, v, scale=None, causal=False, num_splits=0, out=None, l
         _scale(scale, D), int(bool(causal)), int(num_splits), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return o, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, seqlen_q: int) -> int:
+    """Workspace bytes attn_bwd needs for these sizes."""
+    nbytes = ctypes.c_uint64()
+    _check(load_library().sdpa_bwd_workspace_bytes(B, H, seqlen_q, ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Dense backward (bf16/fp16).  q: (B,H,Sq,D), k/v: (B,H,Sk,D), o/dout like q,
+    lse (B,H,Sq) fp32 as attn_fwd returns them.  Returns (dq, dk, dv) shaped
+    and strided like q, k, v (allocated with empty_like unless given)."""
+    lib = load_library()
+    _require_gpu(q, k, v, o, dout, lse)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o, dout")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous (B, H, Sq) float32 tensor")
+    if len({t.dtype for t in (q, k, v, o, dout)}) != 1:
+        raise ValueError("q, k, v, o and dout must share one dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for g, t in ((dq, q), (dk, k), (dv, v)):
+        if g.stride() != t.stride() or g.shape != t.shape:
+            raise ValueError("dq, dk, dv must have the shapes and strides of q, k, v")
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, Sq), 1), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib.attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_code(q), B, H, Sq, Sk, D,
+        _strides(q), _strides(k), _strides(v), _strides(o), _strides(dout),
+        _scale(scale, D), int(bool(causal)), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
+    return dq, dk, dv
 
 
 def _device_cu(cu, device, total, max_len, check):

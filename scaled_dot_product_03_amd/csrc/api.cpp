@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include "../../include/sdpa03.h"
+#include "bwd_args.h"
 #include "fwd_args.h"
 
 namespace {
@@ -213,6 +214,84 @@ const char* sdpa_status_string(sdpa_status status) {
       return "split forward workspace is NULL, not 16-byte aligned or smaller than the plan";
   }
   return "unknown status";
+}
+
+sdpa_status sdpa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t seqlen_q,
+                                     uint64_t* workspace_bytes) {
+  if (B < 0 || H < 0 || seqlen_q < 0) return SDPA_ERR_SHAPE;
+  if (workspace_bytes) {
+    *workspace_bytes = 2ull * static_cast<uint64_t>(B) * static_cast<uint64_t>(H) *
+                       static_cast<uint64_t>(sdpa03::bwd_ws_rows_pad(seqlen_q)) * 4ull;
+  }
+  return SDPA_OK;
+}
+
+sdpa_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q,
+                     int32_t seqlen_k, int32_t head_dim, const int64_t q_stride[4],
+                     const int64_t k_stride[4], const int64_t v_stride[4],
+                     const int64_t o_stride[4], const int64_t dout_stride[4], float scale,
+                     int32_t causal, void* workspace, uint64_t workspace_bytes,
+                     void* hip_stream) {
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (dtype == SDPA_F32) return SDPA_ERR_DTYPE;
+  if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H == 0 || (seqlen_q == 0 && seqlen_k == 0)) return SDPA_OK;
+  // Query side (q, o, dout, lse, dq) is needed when there are query rows; key
+  // side (k, v, dk, dv) when there are keys.
+  if (seqlen_q > 0 && (!q || !o || !dout || !lse || !dq)) return SDPA_ERR_NULL;
+  if (seqlen_k > 0 && (!k || !v || !dk || !dv)) return SDPA_ERR_NULL;
+  if (seqlen_q > 0 && seqlen_k > 0 && (!q || !k)) return SDPA_ERR_NULL;
+  const int es = elem_size(dtype);
+  const View views[] = {
+      {q, {B, H, seqlen_q, head_dim}, q_stride},     {dq, {B, H, seqlen_q, head_dim}, q_stride},
+      {o, {B, H, seqlen_q, head_dim}, o_stride},     {dout, {B, H, seqlen_q, head_dim}, dout_stride},
+      {k, {B, H, seqlen_k, head_dim}, k_stride},     {dk, {B, H, seqlen_k, head_dim}, k_stride},
+      {v, {B, H, seqlen_k, head_dim}, v_stride},     {dv, {B, H, seqlen_k, head_dim}, v_stride},
+  };
+  for (int i = 0; i < 8; ++i) {
+    const bool key_side = i >= 4;
+    if ((key_side ? seqlen_k : seqlen_q) == 0) continue;
+    if ((st = check_view(views[i], es, true)) != SDPA_OK) return st;
+  }
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+  const int64_t pad = sdpa03::bwd_ws_rows_pad(seqlen_q);
+  const uint64_t need = 2ull * static_cast<uint64_t>(B) * H * pad * 4ull;
+  if (seqlen_q > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 ||
+                       workspace_bytes < need))
+    return SDPA_ERR_WORKSPACE;
+  const int64_t q_tiles = (static_cast<int64_t>(seqlen_q) + sdpa03::kBwdDqRows - 1) / sdpa03::kBwdDqRows;
+  const int64_t k_tiles = (static_cast<int64_t>(seqlen_k) + sdpa03::kBwdDkvKeys - 1) / sdpa03::kBwdDkvKeys;
+  const int64_t groups = static_cast<int64_t>(B) * H;
+  if (q_tiles * groups > kMaxGrid || k_tiles * groups > kMaxGrid ||
+      groups * pad > (int64_t(1) << 40))
+    return SDPA_ERR_SHAPE;
+
+  sdpa03::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.ws_delta = static_cast<float*>(workspace);
+  a.ws_lse2 = seqlen_q > 0 ? static_cast<float*>(workspace) + groups * pad : nullptr;
+  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
+  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
+  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
+  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
+  set_strides(dout_stride, a.do_sb, a.do_sh, a.do_ss);
+  a.lse_sh = seqlen_q;
+  a.lse_sb = static_cast<int64_t>(H) * seqlen_q;
+  a.seqlen_q = seqlen_q;
+  a.seqlen_k = seqlen_k;
+  a.num_heads = H;
+  a.num_z = B;
+  a.ws_rows_pad = static_cast<int32_t>(pad);
+  a.q_tiles = static_cast<int32_t>(q_tiles);
+  a.k_tiles = static_cast<int32_t>(k_tiles);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int err = sdpa03::launch_attn_bwd(a, dtype, head_dim, causal != 0, hip_stream);
+  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
 }
 
 sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t total,

@@ -1,0 +1,528 @@
+// Flash-attention backward kernels for CDNA4 (gfx950), bf16 and fp16 inputs.
+//
+// The backward of O = softmax(scale * Q K^T) V recomputes the softmax weights
+// from the per-row logsumexp that the forward returns -- the one number per
+// row that nvFuser issue #2278 "Investigate a new SDPA IR node" leaves the
+// forward to stash for its SdpaOpBwd node -- and never writes the score
+// matrix to memory.  With c = scale:
+//
+//   delta_i = sum_d dO_id O_id                          (prep kernel)
+//   P_ij    = exp(c q_i . k_j - LSE_i), 0 where masked
+//   dP_ij   = dO_i . v_j
+//   dS_ij   = P_ij (dP_ij - delta_i)
+//   dQ_i    = c sum_j dS_ij k_j                          (dQ kernel)
+//   dK_j    = c sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i (dK/dV kernel)
+//
+// P and dS are recomputed twice, once per query tile (dQ, a lane owns a query
+// row) and once per key tile (dK and dV, a lane owns a key), so every
+// gradient row is summed inside one workgroup: no atomics, deterministic.
+//
+// Register layout, as in the forward: in a 32x32 MFMA accumulator lane l
+// holds column l % 32 and register r holds row 8 (r / 4) + 4 (l / 32) + r % 4.
+//  - dQ kernel: S^T = K Q^T and dP^T = V dO^T (K and V tiles in LDS as A
+//    operands, the wave's Q and dO rows in registers as B operands) put one
+//    query row per lane; dQ^T += K^T dS^T reads K transposed.
+//  - dK/dV kernel: S = Q K^T and dP = dO V^T (Q and dO tiles in LDS, the
+//    wave's K and V rows in registers) put one key per lane;
+//    dV^T += dO^T P and dK^T += Q^T dS read dO and Q transposed.
+// In both, the rounded P or dS accumulator is directly the B operand of the
+// transposed product, exactly as P is in the forward's P V.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_common.h"
+#include "bwd_args.h"
+
+namespace sdpa03 {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS row stride (bytes) of a tile that is read both as 16-row MFMA operands
+// (ds_read_b128: the 16 rows of one pass must start in distinct 16-byte bank
+// groups of gfx950's 256-byte bank cycle) and transposed (ds_read_b64_tr_b16:
+// the 4 rows of one 32-lane pass must start in distinct 64-byte blocks).  An
+// odd multiple of 16 satisfies the first; D * 2 + 80 also satisfies the
+// second: consecutive rows start 0, 80, 160, 240 (D = 128) or 0, 208, 160,
+// 112 (D = 64) bytes into the cycle.
+template <int D>
+constexpr int dual_row_bytes() { return D * 2 + 80; }
+// Tiles read only as 16-row MFMA operands.
+template <int D>
+constexpr int plain_row_bytes() { return D * 2 + 16; }
+
+template <typename T>
+using frag_t = typename Mma16<T>::frag;
+
+// Scheduling requests for one block of N_MFMA products fed by N_READ LDS
+// fragment reads (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read):
+// a few reads ahead, then one product and its share of reads.  Without them
+// the compiler issues every read of the block first and runs out of
+// registers.
+template <int N_MFMA, int N_READ>
+__device__ __forceinline__ void interleave_reads() {
+  constexpr int per = (N_READ + N_MFMA - 1) / N_MFMA;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * per, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+  }
+}
+
+// c[nb] += A B for nb < NB.  A: rows 32 nb .. 32 nb + 31 of an LDS tile with
+// row stride ROW bytes, 16 dims per k-step (lane (rho, h) reads the 16 bytes
+// at dims 16 ks + 8 h of row 32 nb + rho).  B: the wave's own rows, one
+// fragment per k-step, in registers.
+template <typename T, int D, int ROW, int NB>
+__device__ __forceinline__ void tile_rows_x_regs(const T* tile, const frag_t<T> (&b)[D / 16],
+                                                 int li, int lh, f32x16 (&c)[NB]) {
+  const char* base = reinterpret_cast<const char*>(tile) + li * ROW + lh * 16;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const frag_t<T> a = *reinterpret_cast<const frag_t<T>*>(base + nb * 32 * ROW + ks * 32);
+      c[nb] = Mma16<T>::mma(a, b[ks], c[nb]);
+    }
+  }
+}
+
+// acc[db] += X^T W.  X: an LDS tile of NB * 32 rows (row stride ROW bytes)
+// read transposed; W: the rounded fragments of NB 32-row accumulators over
+// those rows, register r of lane (i, h) holding row 8 (r / 4) + 4 h + r % 4.
+// k-step (nb, half) -- registers 8 half .. 8 half + 7 -- covers rows
+// 32 nb + 16 half + {4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3}.  Within each
+// group of 16 lanes, ds_read_b64_tr_b16 gives lane i element (i & 3) of the
+// 64-bit words read by lanes 4 j + (i >> 2); with lane t pointing at row
+// R0 + t / 4, column C0 + 4 (t & 3), lane i receives X[R0 + j][C0 + i] for
+// j = 0..3.  Two reads (R0 = 32 nb + 16 half + 4 h and R0 + 8) give the eight
+// rows of one operand.
+template <typename T, int ROW, int NB, int DB>
+__device__ __forceinline__ void tile_tr_x_frags(const T* tile, const frag_t<T> (&w)[NB][2],
+                                                int lane, f32x16 (&acc)[DB]) {
+  using s16x4 = short __attribute__((ext_vector_type(4)));
+  const int t = lane & 15;
+  const int grp = lane >> 4;
+  const int row_lane = (grp >> 1) * 4 + (t >> 2);
+  const int col_lane = (grp & 1) * 16 + 4 * (t & 3);
+  const char* base = reinterpret_cast<const char*>(tile) + row_lane * ROW + col_lane * 2;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        s16x4 x[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const char* src = base + (nb * 32 + half * 16 + sub * 8) * ROW + db * 64;
+          x[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(src));
+        }
+        frag_t<T> xf;
+        __builtin_memcpy(&xf, x, sizeof(xf));
+        acc[db] = Mma16<T>::mma(xf, w[nb][half], acc[db]);
+      }
+    }
+  }
+}
+
+// The wave's own 32 rows as MFMA B-operand fragments: lane (i, h) holds the
+// 8 elements at dims 16 ks + 8 h of row i (zeros for rows past the end).
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frags(const T* row, bool ok, int lh,
+                                               frag_t<T> (&f)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    f[ks] = ok ? *reinterpret_cast<const frag_t<T>*>(row + 16 * ks + 8 * lh) : frag_t<T>{};
+  }
+}
+
+// Stores a 32 x D accumulator whose lane owns one output row (register r of
+// block db holds dims 32 db + 8 (r / 4) + 4 h + r % 4), times `mul`.
+template <typename T, int DB>
+__device__ __forceinline__ void store_row(T* row, const f32x16 (&acc)[DB], float mul, int lh) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      T out4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out4[e] = static_cast<T>(acc[db][4 * g + e] * mul);
+      uint2 packed;
+      __builtin_memcpy(&packed, out4, 8);
+      *reinterpret_cast<uint2*>(row + db * 32 + g * 8 + lh * 4) = packed;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prep: delta = rowsum(dO * O) and LSE * log2(e), one thread per workspace
+// row.  Padding rows (past seqlen_q) get delta = 0 and +inf, so that any
+// weight computed from them is exactly 0.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(a.num_z) * a.num_heads * a.ws_rows_pad;
+  if (gid >= rows) return;
+  const int64_t i = gid % a.ws_rows_pad;
+  const int64_t zh = gid / a.ws_rows_pad;
+  if (i >= a.seqlen_q) {
+    a.ws_delta[gid] = 0.f;
+    a.ws_lse2[gid] = __builtin_huge_valf();
+    return;
+  }
+  const int64_t h = zh % a.num_heads;
+  const int64_t z = zh / a.num_heads;
+  const T* orow = static_cast<const T*>(a.o) + z * a.o_sb + h * a.o_sh + i * a.o_ss;
+  const T* drow = static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh + i * a.do_ss;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const frag_t<T> ov = *reinterpret_cast<const frag_t<T>*>(orow + 8 * c);
+    const frag_t<T> dv = *reinterpret_cast<const frag_t<T>*>(drow + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(ov[e]), static_cast<float>(dv[e]), acc);
+  }
+  const int64_t w = zh * a.ws_rows_pad + i;
+  a.ws_delta[w] = acc;
+  a.ws_lse2[w] = a.lse[z * a.lse_sb + h * a.lse_sh + i] * kLog2e;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 256 query rows of one (batch, head); 8 waves of 32
+// rows; key tiles of 64 stream through two LDS stages.
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = kBwdDqRows / 32;
+  constexpr int BM = kBwdDqRows;
+  constexpr int BN = 64;
+  constexpr int NB = BN / 32;
+  constexpr int DB = D / 32;
+  constexpr int kRowK = dual_row_bytes<D>();
+  constexpr int kRowV = plain_row_bytes<D>();
+  using KCopy = TileCopy<T, D, BN, NW, kRowK>;
+  using VCopy = TileCopy<T, D, BN, NW, kRowV>;
+  using frag = frag_t<T>;
+  __shared__ __attribute__((aligned(1024))) T k_lds0[KCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[KCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[VCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[VCopy::kArrayBytes / 2];
+
+  // Under the causal mask the last query tiles cost the most: they go first.
+  const uint32_t n = blockIdx.x;
+  const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
+  int m;
+  uint32_t g;
+  if constexpr (CAUSAL) {
+    g = n % groups;
+    m = a.q_tiles - 1 - static_cast<int>(n / groups);
+  } else {
+    m = static_cast<int>(n % static_cast<uint32_t>(a.q_tiles));
+    g = n / static_cast<uint32_t>(a.q_tiles);
+  }
+  const int h = static_cast<int>(g % static_cast<uint32_t>(a.num_heads));
+  const int z = static_cast<int>(g / static_cast<uint32_t>(a.num_heads));
+  const int m0 = m * BM;
+  if (m0 >= a.seqlen_q) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+  const int row0 = m0 + wave * 32;
+  const int qi = row0 + li;
+  const bool row_ok = qi < a.seqlen_q;
+
+  const T* qrow = static_cast<const T*>(a.q) + z * a.q_sb + h * a.q_sh + static_cast<int64_t>(qi) * a.q_ss;
+  const T* drow = static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh + static_cast<int64_t>(qi) * a.do_ss;
+  const char* kp = reinterpret_cast<const char*>(static_cast<const T*>(a.k) + z * a.k_sb + h * a.k_sh);
+  const char* vp = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + z * a.v_sb + h * a.v_sh);
+  const int64_t k_row_bytes = a.k_ss * static_cast<int64_t>(sizeof(T));
+  const int64_t v_row_bytes = a.v_ss * static_cast<int64_t>(sizeof(T));
+
+  frag qf[D / 16];
+  frag df[D / 16];
+  load_row_frags<T, D>(qrow, row_ok, lh, qf);
+  load_row_frags<T, D>(drow, row_ok, lh, df);
+  const int64_t wrow = static_cast<int64_t>(g) * a.ws_rows_pad + qi;
+  const float lse2 = row_ok ? a.ws_lse2[wrow] : 0.f;
+  const float delta = row_ok ? a.ws_delta[wrow] : 0.f;
+  const float c2 = a.scale_log2;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  int kend = a.seqlen_k;
+  if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, a.seqlen_q));
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  KCopy kcopy;
+  VCopy vcopy;
+  kcopy.init(wave, lane, k_row_bytes);
+  vcopy.init(wave, lane, v_row_bytes);
+  auto issue = [&](int t, T* kb, T* vb) {
+    const int j0 = t * BN;
+    const int rows = t < n_tiles ? kend - j0 : 0;
+    kcopy.issue(kp + j0 * k_row_bytes, rows, k_row_bytes, kb, wave);
+    vcopy.issue(vp + j0 * v_row_bytes, rows, v_row_bytes, vb, wave);
+  };
+
+  // Tile t, one 32-key block at a time (it keeps the live softmax state to
+  // one block): scores, weights, dP, dS, then dQ^T += K^T dS^T.
+  auto compute = [&](int t, const T* kc, const T* vc) {
+#pragma nounroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int j0 = t * BN + nb * 32;
+      const T* kb = kc + nb * 32 * kRowK / static_cast<int>(sizeof(T));
+      const T* vb = vc + nb * 32 * kRowV / static_cast<int>(sizeof(T));
+      f32x16 st[1] = {f32x16{}};
+      tile_rows_x_regs<T, D, kRowK, 1>(kb, qf, li, lh, st);
+      f32x16 dpt[1] = {f32x16{}};
+      tile_rows_x_regs<T, D, kRowV, 1>(vb, df, li, lh, dpt);
+      const bool need_mask = (j0 + 32 > a.seqlen_k) || (CAUSAL && j0 + 31 > row0);
+      frag w[1][2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(st[0][r], c2, -lse2));
+        if (need_mask) {
+          const int key = j0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (!(key < a.seqlen_k && (!CAUSAL || key <= qi))) p = 0.f;
+        }
+        w[0][r >> 3][r & 7] = static_cast<T>(p * (dpt[0][r] - delta));
+      }
+      tile_tr_x_frags<T, kRowK, 1, DB>(kb, w, lane, acc);
+      // S^T and dP^T: 2 * D/16 products over as many reads; dQ: 2 * DB
+      // products over 4 * DB transposing reads.
+      interleave_reads<2 * (D / 16) + 2 * DB, 2 * (D / 16) + 4 * DB>();
+    }
+  };
+
+  if (n_tiles > 0) {
+    issue(0, k_lds0, v_lds0);
+    wait_vmem();
+    barrier_lds();
+    // Step t computes tile t from one buffer while tile t + 1 loads into the
+    // other (free: its last readers passed the barrier ending step t - 1).
+    for (int t = 0;; t += 2) {
+      issue(t + 1, k_lds1, v_lds1);
+      compute(t, k_lds0, v_lds0);
+      wait_vmem();
+      barrier_lds();
+      if (t + 1 >= n_tiles) break;
+      issue(t + 2, k_lds0, v_lds0);
+      compute(t + 1, k_lds1, v_lds1);
+      wait_vmem();
+      barrier_lds();
+      if (t + 2 >= n_tiles) break;
+    }
+  }
+
+  if (row_ok) {
+    T* dqrow = static_cast<T*>(a.dq) + z * a.q_sb + h * a.q_sh + static_cast<int64_t>(qi) * a.q_ss;
+    store_row<T, DB>(dqrow, acc, a.scale, lh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: one workgroup per 128 keys of one (batch, head); 4 waves of 32
+// keys; query tiles of 64 rows (Q and dO) stream through two LDS stages.
+// With D = 128 the wave's K and V rows and both accumulators take more than
+// half a SIMD's registers: one wave per SIMD.
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = kBwdDkvKeys / 32;
+  constexpr int BQ = 64;
+  constexpr int NB = BQ / 32;
+  constexpr int DB = D / 32;
+  constexpr int kRow = dual_row_bytes<D>();
+  using QCopy = TileCopy<T, D, BQ, NW, kRow>;
+  using frag = frag_t<T>;
+  __shared__ __attribute__((aligned(1024))) T q_lds0[QCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) T q_lds1[QCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) T d_lds0[QCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) T d_lds1[QCopy::kArrayBytes / 2];
+
+  // Under the causal mask the first key tiles cost the most: they go first.
+  const uint32_t n = blockIdx.x;
+  const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
+  int kt;
+  uint32_t g;
+  if constexpr (CAUSAL) {
+    g = n % groups;
+    kt = static_cast<int>(n / groups);
+  } else {
+    kt = static_cast<int>(n % static_cast<uint32_t>(a.k_tiles));
+    g = n / static_cast<uint32_t>(a.k_tiles);
+  }
+  const int h = static_cast<int>(g % static_cast<uint32_t>(a.num_heads));
+  const int z = static_cast<int>(g / static_cast<uint32_t>(a.num_heads));
+  const int n0 = kt * kBwdDkvKeys;
+  if (n0 >= a.seqlen_k) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+  const int key0 = n0 + wave * 32;  // first key of this wave
+  const int kj = key0 + li;         // this lane's key
+  const bool key_ok = kj < a.seqlen_k;
+
+  const T* krow = static_cast<const T*>(a.k) + z * a.k_sb + h * a.k_sh + static_cast<int64_t>(kj) * a.k_ss;
+  const T* vrow = static_cast<const T*>(a.v) + z * a.v_sb + h * a.v_sh + static_cast<int64_t>(kj) * a.v_ss;
+  const char* qp = reinterpret_cast<const char*>(static_cast<const T*>(a.q) + z * a.q_sb + h * a.q_sh);
+  const char* dp = reinterpret_cast<const char*>(static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh);
+  const int64_t q_row_bytes = a.q_ss * static_cast<int64_t>(sizeof(T));
+  const int64_t d_row_bytes = a.do_ss * static_cast<int64_t>(sizeof(T));
+  const float* lse2p = a.ws_lse2 + static_cast<int64_t>(g) * a.ws_rows_pad;
+  const float* deltap = a.ws_delta + static_cast<int64_t>(g) * a.ws_rows_pad;
+
+  frag kf[D / 16];
+  frag vf[D / 16];
+  load_row_frags<T, D>(krow, key_ok, lh, kf);
+  load_row_frags<T, D>(vrow, key_ok, lh, vf);
+  const float c2 = a.scale_log2;
+
+  f32x16 dk[DB];
+  f32x16 dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  // Query rows before the workgroup's first key see none of its keys.
+  const int qbeg = CAUSAL ? (n0 / BQ) * BQ : 0;
+  const int n_tiles = a.seqlen_q > qbeg ? (a.seqlen_q - qbeg + BQ - 1) / BQ : 0;
+
+  QCopy qcopy;
+  QCopy dcopy;
+  qcopy.init(wave, lane, q_row_bytes);
+  dcopy.init(wave, lane, d_row_bytes);
+  auto issue = [&](int t, T* qb, T* db_) {
+    const int q0 = qbeg + t * BQ;
+    const int rows = t < n_tiles ? a.seqlen_q - q0 : 0;
+    qcopy.issue(qp + q0 * q_row_bytes, rows, q_row_bytes, qb, wave);
+    dcopy.issue(dp + q0 * d_row_bytes, rows, d_row_bytes, db_, wave);
+  };
+
+  // Query tile t, one 32-row block at a time: S = Q K^T, P,
+  // dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  Register r belongs to
+  // query row q0 + 32 nb + 8 (r / 4) + 4 h + r % 4; the workspace rows of a
+  // whole tile lie inside its padding, so they are read without bounds checks.
+  auto compute = [&](int t, const T* qc, const T* dc) {
+#pragma nounroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int q0 = qbeg + t * BQ + nb * 32;
+      const T* qb = qc + nb * 32 * kRow / static_cast<int>(sizeof(T));
+      const T* db_ = dc + nb * 32 * kRow / static_cast<int>(sizeof(T));
+      f32x16 s[1] = {f32x16{}};
+      tile_rows_x_regs<T, D, kRow, 1>(qb, kf, li, lh, s);
+      const bool need_mask = (q0 + 32 > a.seqlen_q) || (CAUSAL && q0 < key0 + 31);
+      float pr[16];
+      frag w[1][2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qr = q0 + 8 * g4 + 4 * lh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2p + qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[0][r], c2, -l4[e]));
+          if (need_mask) {
+            const int q = qr + e;
+            if (!(q < a.seqlen_q && (!CAUSAL || kj <= q))) p = 0.f;
+          }
+          pr[r] = p;
+          w[0][r >> 3][r & 7] = static_cast<T>(p);
+        }
+      }
+      tile_tr_x_frags<T, kRow, 1, DB>(db_, w, lane, dv);
+      f32x16 dpp[1] = {f32x16{}};
+      tile_rows_x_regs<T, D, kRow, 1>(db_, vf, li, lh, dpp);
+      frag ws[1][2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltap + q0 + 8 * g4 + 4 * lh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          ws[0][r >> 3][r & 7] = static_cast<T>(pr[r] * (dpp[0][r] - d4[e]));
+        }
+      }
+      tile_tr_x_frags<T, kRow, 1, DB>(qb, ws, lane, dk);
+      interleave_reads<2 * (D / 16) + 4 * DB, 2 * (D / 16) + 8 * DB>();
+    }
+  };
+
+  if (n_tiles > 0) {
+    issue(0, q_lds0, d_lds0);
+    wait_vmem();
+    barrier_lds();
+    for (int t = 0;; t += 2) {
+      issue(t + 1, q_lds1, d_lds1);
+      compute(t, q_lds0, d_lds0);
+      wait_vmem();
+      barrier_lds();
+      if (t + 1 >= n_tiles) break;
+      issue(t + 2, q_lds0, d_lds0);
+      compute(t + 1, q_lds1, d_lds1);
+      wait_vmem();
+      barrier_lds();
+      if (t + 2 >= n_tiles) break;
+    }
+  }
+
+  if (key_ok) {
+    T* dkrow = static_cast<T*>(a.dk) + z * a.k_sb + h * a.k_sh + static_cast<int64_t>(kj) * a.k_ss;
+    T* dvrow = static_cast<T*>(a.dv) + z * a.v_sb + h * a.v_sh + static_cast<int64_t>(kj) * a.v_ss;
+    store_row<T, DB>(dkrow, dk, a.scale, lh);
+    store_row<T, DB>(dvrow, dv, 1.f, lh);
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+int launch_typed(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.num_z) * a.num_heads * a.ws_rows_pad;
+  const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
+  if (a.seqlen_q > 0) {
+    hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D>), dim3(static_cast<uint32_t>((rows + 255) / 256)),
+                       dim3(256), 0, s, a);
+    int err = static_cast<int>(hipGetLastError());
+    if (err != 0) return err;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>),
+                       dim3(static_cast<uint32_t>(a.q_tiles) * groups), dim3(kBwdDqRows * 2), 0, s, a);
+    err = static_cast<int>(hipGetLastError());
+    if (err != 0) return err;
+  }
+  if (a.k_tiles > 0) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>),
+                       dim3(static_cast<uint32_t>(a.k_tiles) * groups), dim3(kBwdDkvKeys * 2), 0, s, a);
+    return static_cast<int>(hipGetLastError());
+  }
+  return 0;
+}
+
+template <typename T>
+int launch_dim(const BwdArgs& a, int head_dim, bool causal, hipStream_t s) {
+  if (head_dim == 64) return causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
+  return causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+}
+
+}  // namespace
+
+int launch_attn_bwd(const BwdArgs& a, int dtype, int head_dim, bool causal, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == 1 ? launch_dim<_Float16>(a, head_dim, causal, s)
+                    : launch_dim<__bf16>(a, head_dim, causal, s);
+}
+
+}  // namespace sdpa03

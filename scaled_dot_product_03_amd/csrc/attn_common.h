@@ -1,0 +1,203 @@
+// Device helpers shared by the attention kernels (forward and backward):
+// vector types, MFMA wrappers, wave reductions, memory waits, the LDS-only
+// workgroup barrier and the HBM -> LDS tile copy (namespace sdpa03).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa03 {
+
+using f32x16 = float __attribute__((ext_vector_type(16)));
+using f32x4 = float __attribute__((ext_vector_type(4)));
+using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
+using f16x8 = _Float16 __attribute__((ext_vector_type(8)));
+using lds_void_ptr = __attribute__((address_space(3))) void*;
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.6931471805599453f;
+// Fourth dword of a raw buffer descriptor on gfx9 (32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Workgroup barrier for LDS hand-offs.  __syncthreads() (and any release
+// fence covering LDS) waits for every outstanding vector-memory load first
+// (vmcnt(0)), because a buffer load into LDS counts as an LDS write -- which
+// would drain tile loads that are meant to stay in flight across the barrier.
+// Here each wave waits for its own tile loads explicitly (wait_vmem_allow)
+// before it arrives; the barrier itself waits only for the wave's LDS reads
+// (so no later load can overwrite a buffer still being read), and the memory
+// clobber and the scheduling barriers keep the compiler from moving LDS
+// accesses -- or any other instruction -- across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory
+// loads are still in flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_allow() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core paths.  Each provides: Q fragments held in registers, the
+// S^T = K Q^T product from a K tile in LDS, the probabilities P of a score
+// tile, and O^T += V^T P^T from a V tile in LDS.  Tiles in LDS are row-major
+// [key][dim] with 16-byte chunks XOR-swizzled per row.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+struct Mma16;
+
+template <>
+struct Mma16<__bf16> {
+  using frag = bf16x8;
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma16<_Float16> {
+  using frag = f16x8;
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Sum of the 16 floats of an accumulator as a balanced tree (short
+// dependency chains for the in-order VALU).
+__device__ __forceinline__ float tree_sum16(const float (&x)[16]) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+  float b0 = (a[0] + a[1]) + (a[2] + a[3]);
+  float b1 = (a[4] + a[5]) + (a[6] + a[7]);
+  return b0 + b1;
+}
+
+// ---------------------------------------------------------------------------
+// Tile copies: buffer loads straight into LDS
+// ---------------------------------------------------------------------------
+// buffer_load_dwordx4 ... lds writes lane L's 16 bytes to (wave-uniform LDS
+// base + 16 L): one instruction fills a 1 KiB block of LDS from 64
+// independent source offsets.  A tile of BN rows at LDS row stride ROW
+// occupies BN * ROW bytes; every wave issues the same number of blocks
+// (the last ones may lie past the tile, inside the array).  A lane whose
+// 16 bytes fall on row padding, or past the tile, gets an offset outside
+// the descriptor's range and writes zeros.  The descriptor starts at the
+// tile's first row and covers only the rows that exist, so rows past the
+// sequence read back as zeros too, with no bounds arithmetic in the loop.
+// Source offsets are 32-bit: the host limits row strides accordingly.
+
+template <typename T, int D, int BN, int NW, int ROW>
+struct TileCopy {
+  static constexpr int kDataBytes = D * static_cast<int>(sizeof(T));  // payload per row
+  static constexpr int kBlocks = (BN * ROW + 1023) / 1024;
+  static constexpr int kInstPerWave = (kBlocks + NW - 1) / NW;
+  static constexpr int kArrayBytes = kInstPerWave * NW * 1024;  // LDS array size per tile
+  static constexpr uint32_t kNowhere = 0x80000000u;  // past any descriptor range
+
+  uint32_t voff[kInstPerWave];
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t row_bytes) {
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const int pos = (i * NW + wave) * 1024 + lane * 16;
+      const int r = pos / ROW;
+      const int col = pos % ROW;
+      const bool data = r < BN && col < kDataBytes;
+      voff[i] = data ? static_cast<uint32_t>(r * row_bytes) + static_cast<uint32_t>(col) : kNowhere;
+    }
+  }
+
+  // Rows [0, valid_rows) of the tile starting at `tile` land in `lds_tile`.
+  __device__ __forceinline__ void issue(const char* tile, int valid_rows, int64_t row_bytes,
+                                        T* lds_tile, int wave) const {
+    // hipcc's host (x86) pass parses this body too but has no buffer-resource
+    // type; left visible there, it stops the host pass from emitting the
+    // launch stubs of later kernel instantiations.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int rows = valid_rows < 0 ? 0 : (valid_rows > BN ? BN : valid_rows);
+    const uint32_t bytes = static_cast<uint32_t>(rows * row_bytes);  // <= 2^30
+    // Every input of the descriptor is wave-uniform; saying so explicitly
+    // keeps the descriptor in SGPRs.  (Left in VGPRs, the compiler wraps each
+    // buffer load in a loop over the distinct descriptor values of the wave.)
+    // readfirstlane returns int: keep both halves unsigned 32-bit before
+    // widening, or a low half with bit 31 set would sign-extend into the
+    // high half of the address.
+    const uint64_t addr = reinterpret_cast<uint64_t>(tile);
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr >> 32))));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr))));
+    const uint64_t base = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, nrec, kBufferFlags);
+    char* lds = reinterpret_cast<char*>(lds_tile);
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_void_ptr)(lds + (i * NW + wave) * 1024), 16, voff[i], 0, 0, 0);
+    }
+#endif
+  }
+
+  // The same copy written as inline assembly.  The compiler neither moves
+  // these loads nor counts them, so it inserts no waits of its own for them
+  // (its tracking of which LDS buffer a load writes is lost across the
+  // ping-pong loop and would make it drain every load in flight); the caller
+  // waits with explicit vmcnt counts, and must have no compiler-issued
+  // vector-memory load outstanding that it relies on the compiler to wait
+  // for.  The memory clobber keeps LDS reads of earlier code before the
+  // loads.  s_nop 4 covers the wait states between a VALU write of a
+  // descriptor SGPR (readfirstlane) and its use by a vector-memory
+  // instruction; s_nop 0 those between writing M0 and an LDS load.
+  __device__ __forceinline__ void issue_untracked(const char* tile, int valid_rows,
+                                                  int64_t row_bytes, T* lds_tile, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using i32x4 = int __attribute__((ext_vector_type(4)));
+    const int rows = valid_rows < 0 ? 0 : (valid_rows > BN ? BN : valid_rows);
+    const uint32_t bytes = static_cast<uint32_t>(rows * row_bytes);  // <= 2^30
+    const uint64_t addr = reinterpret_cast<uint64_t>(tile);
+    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr >> 32)));
+    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr)));
+    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    // Raw descriptor: base (48 bits, stride 0), num_records, format/flags.
+    const i32x4 rsrc = {lo, hi & 0xFFFF, nrec, kBufferFlags};
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_ptr)(lds_tile);  // LDS byte address
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+          static_cast<int>(lds + static_cast<uint32_t>((i * NW + wave) * 1024))));
+      asm volatile(
+          "s_nop 4\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %0, %2, 0 offen lds"
+          :
+          : "v"(voff[i]), "s"(m0v), "s"(rsrc)
+          : "memory", "m0");
+    }
+#endif
+  }
+};
+
+}  // namespace sdpa03
