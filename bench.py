@@ -10,8 +10,8 @@ workload), inputs resident in HBM.  FLOPs are 4*Sq*Sk*D*H*B per forward,
 halved for causal.  The line also carries the compact varlen THD workload
 (16 sequences, lengths U{1..4096} from seed 4, H=16, D=128, bf16, causal)
 and the fp16 B=2, H=32, Sq=512, Sk=8192, D=64 workload (through attn_fwd
-and through the key-parallel attn_fwd_splitk) timed the same way, a
-roofline record for the dominant kernel (the
+and through the key-parallel attn_fwd_splitk) and the backward of the dense
+workload timed the same way, a roofline record for the dominant kernel (the
 non-causal forward, timed with HIP events on the stream it runs on around the
 block of its back-to-back launches) and the float64 CPU oracle timed on a bounded sample of the same
 workload.
@@ -38,6 +38,7 @@ METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16 BHSD S=2048 D=128; varlen THD)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/attn_fwd.hip",
+                  "scaled_dot_product_03_amd/csrc/attn_common.h",
                   "scaled_dot_product_03_amd/csrc/dispatch_table.inc"]
 
 
@@ -129,6 +130,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (a kernel of "
                          "known HBM traffic, for scaling counter readings)")
@@ -269,6 +271,29 @@ def main():
                            "pct_mfma_peak": 100 * sf / (s_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         breakdown["dense_fp16_sq512_sk8192"] = entry
         del sq, sk, sv, so, slse, ws
+
+    if not args.no_bwd:
+        # Backward of the same workload: gradients for an upstream dO drawn
+        # from the same seeded generator.  FLOPs are the five products of the
+        # method (S, dP, dV, dK, dQ: 2.5x the forward's), halved for causal;
+        # the kernels recompute S and dP once more than that.
+        rng = np.random.default_rng(2 + 1000)
+        dout = torch.from_numpy(rng.standard_normal(tuple(x.q.shape), dtype=np.float32)).to(
+            x.q.dtype).to(dev)
+        ws = torch.empty(binding.bwd_workspace_bytes(B, H, Sq), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bwd = {"workload": "dense_bf16_b4h16s2048d128 (seed 2), dO seed 1002"}
+        for causal in (False, True):
+            bo, blse = binding.attn_fwd(q, k, v, scale=x.scale, causal=causal)
+            b_avg = block_ms(lambda: binding.attn_bwd(q, k, v, bo, dout, blse, scale=x.scale,
+                                                      causal=causal, dq=dq, dk=dk, dv=dv,
+                                                      workspace=ws))
+            bf = 2.5 * dense_flops(B, H, Sq, Sk, D, causal)
+            bwd["causal" if causal else "noncausal"] = {
+                "flops": bf, "avg_ms": b_avg, "tflops": bf / (b_avg * 1e-3) / 1e12,
+                "pct_mfma_peak": 100 * bf / (b_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        breakdown["backward_dense_bf16_s2048"] = bwd
+        del dout, ws, dq, dk, dv, bo, blse
 
     bm, bn, waves = binding.kernel_config(torch.bfloat16, D)
     record = {
