@@ -159,37 +159,42 @@ __device__ __forceinline__ void store_row(T* row, const f32x16 (&acc)[DB], float
 }
 
 // ---------------------------------------------------------------------------
-// Prep: delta = rowsum(dO * O) and LSE * log2(e), one thread per workspace
-// row.  Padding rows (past seqlen_q) get delta = 0 and +inf, so that any
-// weight computed from them is exactly 0.
+// Prep: delta = rowsum(dO * O) and LSE * log2(e) per workspace row.  D / 8
+// threads share a row, each reading 16 contiguous bytes of O and of dO (so a
+// wave reads whole rows), and a butterfly over the row's threads sums them.
+// Padding rows (past seqlen_q) get delta = 0 and +inf, so that any weight
+// computed from them is exactly 0.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int kThreadsPerRow = D / 8;
+  constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  const int c = threadIdx.x % kThreadsPerRow;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
   const int64_t rows = static_cast<int64_t>(a.num_z) * a.num_heads * a.ws_rows_pad;
-  if (gid >= rows) return;
+  const bool in_range = gid < rows;
   const int64_t i = gid % a.ws_rows_pad;
   const int64_t zh = gid / a.ws_rows_pad;
-  if (i >= a.seqlen_q) {
-    a.ws_delta[gid] = 0.f;
-    a.ws_lse2[gid] = __builtin_huge_valf();
-    return;
-  }
   const int64_t h = zh % a.num_heads;
   const int64_t z = zh / a.num_heads;
-  const T* orow = static_cast<const T*>(a.o) + z * a.o_sb + h * a.o_sh + i * a.o_ss;
-  const T* drow = static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh + i * a.do_ss;
+  const bool real_row = in_range && i < a.seqlen_q;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
+  if (real_row) {
+    const T* orow = static_cast<const T*>(a.o) + z * a.o_sb + h * a.o_sh + i * a.o_ss;
+    const T* drow = static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh + i * a.do_ss;
     const frag_t<T> ov = *reinterpret_cast<const frag_t<T>*>(orow + 8 * c);
     const frag_t<T> dv = *reinterpret_cast<const frag_t<T>*>(drow + 8 * c);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(ov[e]), static_cast<float>(dv[e]), acc);
   }
-  const int64_t w = zh * a.ws_rows_pad + i;
-  a.ws_delta[w] = acc;
-  a.ws_lse2[w] = a.lse[z * a.lse_sb + h * a.lse_sh + i] * kLog2e;
+  // Every lane takes part in the butterfly (the groups are aligned in the wave).
+#pragma unroll
+  for (int off = kThreadsPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kThreadsPerRow);
+  if (in_range && c == 0) {
+    a.ws_delta[gid] = real_row ? acc : 0.f;
+    a.ws_lse2[gid] = real_row ? a.lse[z * a.lse_sb + h * a.lse_sh + i] * kLog2e
+                              : __builtin_huge_valf();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -494,7 +499,9 @@ int launch_typed(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(a.num_z) * a.num_heads * a.ws_rows_pad;
   const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
   if (a.seqlen_q > 0) {
-    hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D>), dim3(static_cast<uint32_t>((rows + 255) / 256)),
+    constexpr int64_t kRowsPerBlock = 256 / (D / 8);
+    hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D>),
+                       dim3(static_cast<uint32_t>((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                        dim3(256), 0, s, a);
     int err = static_cast<int>(hipGetLastError());
     if (err != 0) return err;
