@@ -246,8 +246,61 @@ sdpa_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, uint64_t workspace_bytes, void* hip_stream);
 
 /*
- * Workspace bytes attn_bwd needs: 2 * B * H * roundup(seqlen_q, 64) * 4.
- * SDPA_ERR_SHAPE for negative sizes.
+ * Variable-length backward, compact (THD) layout: the gradients of
+ * attn_fwd_compact_varlen with the same arguments.  Each sequence is an
+ * independent problem, so its gradients are attn_bwd's on that sequence's
+ * rows and keys alone (AOTriton PR #31 gives each varlen forward its
+ * backward).  dout, o, dq have q's (1, H, total_q, head_dim) shape (dq with
+ * q's strides), dk and dv k's and v's; lse is the forward's (1, H, total_q)
+ * fp32 output.  Every row and key inside a sequence is written (zeros where
+ * nothing contributes); tokens past cu_seqlens_*[num_seqs] are neither read
+ * nor written.
+ *
+ * workspace: at least sdpa_bwd_workspace_bytes(1, H, total_q) bytes, as
+ * for attn_bwd.  Same argument checks and device-side contract as
+ * attn_fwd_compact_varlen; SDPA_ERR_DTYPE for fp32; SDPA_ERR_WORKSPACE as
+ * attn_bwd.
+ */
+sdpa_status attn_bwd_compact_varlen(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dout, const float* lse, void* dq, void* dk,
+                                    void* dv, sdpa_dtype dtype, int32_t B, int32_t H,
+                                    int32_t total_q, int32_t total_k, int32_t head_dim,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t num_seqs, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k,
+                                    const int64_t q_stride[4], const int64_t k_stride[4],
+                                    const int64_t v_stride[4], const int64_t o_stride[4],
+                                    const int64_t dout_stride[4], float scale, int32_t causal,
+                                    void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/*
+ * Variable-length backward, padded layout: the gradients of
+ * attn_fwd_padded_varlen with the same arguments (Q-side tensors
+ * (B, H, seqlen_q_max, head_dim), key side (B, H, seqlen_k_max, head_dim),
+ * lse (B, H, seqlen_q_max) fp32).  Rows and keys inside a batch's true
+ * lengths are written (zeros where nothing contributes); those at or past
+ * them are neither read nor written.
+ *
+ * workspace: at least sdpa_bwd_workspace_bytes(B, H, seqlen_q_max) bytes.
+ * Same checks and device-side contract as attn_fwd_padded_varlen;
+ * SDPA_ERR_DTYPE for fp32; SDPA_ERR_WORKSPACE as attn_bwd.
+ */
+sdpa_status attn_bwd_padded_varlen(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, sdpa_dtype dtype, int32_t B, int32_t H,
+                                   int32_t seqlen_q_max, int32_t seqlen_k_max,
+                                   int32_t head_dim, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k,
+                                   const int64_t q_stride[4], const int64_t k_stride[4],
+                                   const int64_t v_stride[4], const int64_t o_stride[4],
+                                   const int64_t dout_stride[4], float scale, int32_t causal,
+                                   void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/*
+ * Workspace bytes the backward entry points need for B batches of H heads
+ * with seqlen_q rows in the query view (total_q for the compact layout,
+ * seqlen_q_max for the padded one): 2 * B * H * (roundup(seqlen_q, 64) + 64)
+ * * 4.  SDPA_ERR_SHAPE for negative sizes.
  */
 sdpa_status sdpa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t seqlen_q,
                                      uint64_t* workspace_bytes);

@@ -35,6 +35,8 @@ EXPORTED = (
     "attn_fwd_splitk",
     "sdpa_fwd_splitk_plan",
     "attn_bwd",
+    "attn_bwd_compact_varlen",
+    "attn_bwd_padded_varlen",
     "sdpa_bwd_workspace_bytes",
     "sdpa_check_cu_seqlens_host",
     "sdpa_kernel_config",
@@ -96,6 +98,16 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
          _stride, _stride, _stride, _stride, _stride, ctypes.c_float, _i32, _p, ctypes.c_uint64,
          _p])
+    bwd_tail = [_stride, _stride, _stride, _stride, _stride, ctypes.c_float, _i32, _p,
+                ctypes.c_uint64, _p]
+    lib.attn_bwd_compact_varlen.restype = ctypes.c_int
+    lib.attn_bwd_compact_varlen.argtypes = (
+        [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p,
+         _i32, _i32, _i32] + bwd_tail)
+    lib.attn_bwd_padded_varlen.restype = ctypes.c_int
+    lib.attn_bwd_padded_varlen.argtypes = (
+        [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p]
+        + bwd_tail)
     lib.sdpa_bwd_workspace_bytes.restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [_i32, _i32, _i32, ctypes.POINTER(ctypes.c_uint64)]
     lib.sdpa_check_cu_seqlens_host.restype = ctypes.c_int
@@ -233,12 +245,7 @@ def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, 
         raise ValueError("lse must be a contiguous (B, H, Sq) float32 tensor")
     if len({t.dtype for t in (q, k, v, o, dout)}) != 1:
         raise ValueError("q, k, v, o and dout must share one dtype")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for g, t in ((dq, q), (dk, k), (dv, v)):
-        if g.stride() != t.stride() or g.shape != t.shape:
-            raise ValueError("dq, dk, dv must have the shapes and strides of q, k, v")
+    dq, dk, dv = _grads_like(q, k, v, dq, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(B, H, Sq), 1), dtype=torch.uint8,
                                 device=q.device)
@@ -262,6 +269,25 @@ def _device_cu(cu, device, total, max_len, check):
     return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
 
 
+def _max_len(cu, given):
+    if given is not None:
+        return int(given)
+    if isinstance(cu, torch.Tensor) and cu.is_cuda:
+        raise ValueError("max_seqlen is required with device cu_seqlens")
+    c = np.asarray(cu.cpu().numpy() if isinstance(cu, torch.Tensor) else cu, dtype=np.int64)
+    return int(np.diff(c).max()) if c.size > 1 else 0
+
+
+def _grads_like(q, k, v, dq, dk, dv):
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for g, t in ((dq, q), (dk, k), (dv, v)):
+        if g.stride() != t.stride() or g.shape != t.shape or g.dtype != t.dtype:
+            raise ValueError("dq, dk, dv must have the shapes, strides and dtype of q, k, v")
+    return dq, dk, dv
+
+
 def attn_fwd_compact_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None,
                             max_seqlen_k=None, scale=None, causal=False, out=None, lse=None,
                             check=True):
@@ -280,14 +306,6 @@ def attn_fwd_compact_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=No
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
-
-    def _max_len(cu, given):
-        if given is not None:
-            return int(given)
-        if isinstance(cu, torch.Tensor) and cu.is_cuda:
-            raise ValueError("max_seqlen is required with device cu_seqlens")
-        c = np.asarray(cu.cpu().numpy() if isinstance(cu, torch.Tensor) else cu, dtype=np.int64)
-        return int(np.diff(c).max()) if c.size > 1 else 0
 
     max_q = _max_len(cu_seqlens_q, max_seqlen_q)
     max_k = _max_len(cu_seqlens_k, max_seqlen_k)
@@ -336,3 +354,78 @@ def attn_fwd_padded_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, caus
         _strides(q), _strides(k), _strides(v), _strides(o),
         _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
     return o, lse
+
+
+def attn_bwd_compact_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k,
+                            max_seqlen_q=None, max_seqlen_k=None, scale=None, causal=False,
+                            dq=None, dk=None, dv=None, workspace=None, check=True):
+    """Compact varlen backward over packed (T, H, D) tokens (bf16/fp16).
+
+    o, dout: (Tq, H, D) like q; lse: (1, H, Tq) fp32 as
+    attn_fwd_compact_varlen returns it.  cu_seqlens as for the forward.
+    Returns (dq, dk, dv) shaped like q, k, v; tokens outside every sequence
+    are left as allocated (uninitialised unless given).
+    """
+    lib = load_library()
+    _require_gpu(q, k, v, o, dout, lse)
+    Tq, H, D = q.shape
+    Tk = k.shape[0]
+    if k.shape != (Tk, H, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o, dout")
+    if lse.shape != (1, H, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous (1, H, Tq) float32 tensor")
+    if len({t.dtype for t in (q, k, v, o, dout)}) != 1:
+        raise ValueError("q, k, v, o and dout must share one dtype")
+    max_q = _max_len(cu_seqlens_q, max_seqlen_q)
+    max_k = _max_len(cu_seqlens_k, max_seqlen_k)
+    cu_q = _device_cu(cu_seqlens_q, q.device, Tq, max_q, check)
+    cu_k = _device_cu(cu_seqlens_k, q.device, Tk, max_k, check)
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same length")
+    dq, dk, dv = _grads_like(q, k, v, dq, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(1, H, Tq), 1), dtype=torch.uint8,
+                                device=q.device)
+    views = [t.transpose(0, 1).unsqueeze(0) for t in (q, k, v, o, dout, dq, dk, dv)]
+    qv, kv, vv, ov, dov, dqv, dkv, dvv = views
+    _check(lib.attn_bwd_compact_varlen(
+        qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), dov.data_ptr(),
+        lse.data_ptr(), dqv.data_ptr(), dkv.data_ptr(), dvv.data_ptr(), _dtype_code(q), 1, H,
+        Tq, Tk, D, cu_q.data_ptr(), cu_k.data_ptr(), cu_q.numel() - 1, max_q, max_k,
+        _strides(qv), _strides(kv), _strides(vv), _strides(ov), _strides(dov),
+        _scale(scale, D), int(bool(causal)), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+def attn_bwd_padded_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, scale=None,
+                           causal=False, dq=None, dk=None, dv=None, workspace=None, check=True):
+    """Padded varlen backward (bf16/fp16).  q/o/dout: (B,H,Sq_max,D), k/v:
+    (B,H,Sk_max,D), lse (B,H,Sq_max) fp32 as attn_fwd_padded_varlen returns
+    it.  Returns (dq, dk, dv); rows past a batch's true length are left as
+    allocated (uninitialised unless given)."""
+    lib = load_library()
+    _require_gpu(q, k, v, o, dout, lse)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o, dout")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous (B, H, Sq_max) float32 tensor")
+    if len({t.dtype for t in (q, k, v, o, dout)}) != 1:
+        raise ValueError("q, k, v, o and dout must share one dtype")
+    cu_q = _device_cu(cu_seqlens_q, q.device, B * Sq, Sq, check)
+    cu_k = _device_cu(cu_seqlens_k, q.device, B * Sk, Sk, check)
+    if cu_q.numel() != B + 1 or cu_k.numel() != B + 1:
+        raise ValueError("padded varlen needs B + 1 cu_seqlens entries")
+    dq, dk, dv = _grads_like(q, k, v, dq, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, Sq), 1), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib.attn_bwd_padded_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_code(q), B, H, Sq, Sk, D,
+        cu_q.data_ptr(), cu_k.data_ptr(), _strides(q), _strides(k), _strides(v), _strides(o),
+        _strides(dout), _scale(scale, D), int(bool(causal)), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
+    return dq, dk, dv

@@ -193,6 +193,116 @@ sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, in
   return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
 }
 
+// One backward call.  The rank-4 views are (num_b, H, rows_q or rows_k, D);
+// mode, num_z and the per-sequence bounds (seqlen_q, seqlen_k, cu_q, cu_k)
+// select the sequences inside them, as in the forward.
+struct BwdCall {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  sdpa_dtype dtype;
+  int32_t num_b, num_heads, rows_q, rows_k, head_dim;
+  const int64_t* q_stride;
+  const int64_t* k_stride;
+  const int64_t* v_stride;
+  const int64_t* o_stride;
+  const int64_t* dout_stride;
+  float scale;
+  int32_t causal;
+  void* workspace;
+  uint64_t workspace_bytes;
+  void* stream;
+  int mode;
+  int32_t num_z, seqlen_q, seqlen_k;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+};
+
+// Checks shared by the three backward entry points (sizes are already known
+// to be non-negative), then the launches.
+sdpa_status run_bwd(const BwdCall& c) {
+  sdpa_status st = check_common(c.dtype, c.head_dim, c.scale);
+  if (st != SDPA_OK) return st;
+  if (c.dtype == SDPA_F32) return SDPA_ERR_DTYPE;
+  const int32_t H = c.num_heads;
+  // Nothing to write when no sequence has a query row or a key.
+  if (static_cast<int64_t>(c.num_b) * H * c.num_z == 0 || (c.seqlen_q == 0 && c.seqlen_k == 0))
+    return SDPA_OK;
+  // Query side (q, o, dout, lse, dq) is needed when the view has query rows;
+  // key side (k, v, dk, dv) when it has keys.
+  if (c.rows_q > 0 && (!c.q || !c.o || !c.dout || !c.lse || !c.dq)) return SDPA_ERR_NULL;
+  if (c.rows_k > 0 && (!c.k || !c.v || !c.dk || !c.dv)) return SDPA_ERR_NULL;
+  if (c.mode != sdpa03::MODE_DENSE) {
+    if (!c.cu_q || !c.cu_k) return SDPA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(c.cu_q) % 4 != 0 ||
+        reinterpret_cast<uintptr_t>(c.cu_k) % 4 != 0)
+      return SDPA_ERR_ALIGN;
+  }
+  const int es = elem_size(c.dtype);
+  const int64_t nb = c.num_b, hd = c.head_dim;
+  const View views[] = {
+      {c.q, {nb, H, c.rows_q, hd}, c.q_stride},    {c.dq, {nb, H, c.rows_q, hd}, c.q_stride},
+      {c.o, {nb, H, c.rows_q, hd}, c.o_stride},    {c.dout, {nb, H, c.rows_q, hd}, c.dout_stride},
+      {c.k, {nb, H, c.rows_k, hd}, c.k_stride},    {c.dk, {nb, H, c.rows_k, hd}, c.k_stride},
+      {c.v, {nb, H, c.rows_k, hd}, c.v_stride},    {c.dv, {nb, H, c.rows_k, hd}, c.v_stride},
+  };
+  for (int i = 0; i < 8; ++i) {
+    const bool key_side = i >= 4;
+    if ((key_side ? c.rows_k : c.rows_q) == 0) continue;
+    if ((st = check_view(views[i], es, true)) != SDPA_OK) return st;
+  }
+  if (reinterpret_cast<uintptr_t>(c.lse) % 4 != 0) return SDPA_ERR_ALIGN;
+  const int64_t pad = sdpa03::bwd_ws_rows_pad(c.rows_q);
+  const int64_t ws_groups = nb * H;  // workspace (b, h) blocks
+  const int64_t q_tiles = (static_cast<int64_t>(c.seqlen_q) + sdpa03::kBwdDqRows - 1) / sdpa03::kBwdDqRows;
+  const int64_t k_tiles = (static_cast<int64_t>(c.seqlen_k) + sdpa03::kBwdDkvKeys - 1) / sdpa03::kBwdDkvKeys;
+  const int64_t groups = static_cast<int64_t>(c.num_z) * H;  // (sequence, head) pairs
+  // The prep kernel covers 16 (D = 128) or 32 workspace rows per workgroup.
+  if (pad > INT32_MAX || q_tiles * groups > kMaxGrid || k_tiles * groups > kMaxGrid ||
+      ws_groups * pad > (int64_t(1) << 40) || (ws_groups * pad + 15) / 16 > kMaxGrid)
+    return SDPA_ERR_SHAPE;
+  const uint64_t need = 2ull * static_cast<uint64_t>(ws_groups * pad) * 4ull;
+  if (q_tiles > 0 && (c.workspace == nullptr ||
+                      reinterpret_cast<uintptr_t>(c.workspace) % 16 != 0 ||
+                      c.workspace_bytes < need))
+    return SDPA_ERR_WORKSPACE;
+
+  sdpa03::BwdArgs a{};
+  a.q = c.q; a.k = c.k; a.v = c.v; a.o = c.o; a.dout = c.dout; a.lse = c.lse;
+  a.cu_q = c.cu_q; a.cu_k = c.cu_k;
+  a.dq = c.dq; a.dk = c.dk; a.dv = c.dv;
+  a.ws_delta = static_cast<float*>(c.workspace);
+  a.ws_lse2 = q_tiles > 0 ? static_cast<float*>(c.workspace) + ws_groups * pad : nullptr;
+  set_strides(c.q_stride, a.q_sb, a.q_sh, a.q_ss);
+  set_strides(c.k_stride, a.k_sb, a.k_sh, a.k_ss);
+  set_strides(c.v_stride, a.v_sb, a.v_sh, a.v_ss);
+  set_strides(c.o_stride, a.o_sb, a.o_sh, a.o_ss);
+  set_strides(c.dout_stride, a.do_sb, a.do_sh, a.do_ss);
+  // The forward's logsumexp layout: (num_b, H, rows_q), contiguous.
+  a.lse_sh = c.rows_q;
+  a.lse_sb = static_cast<int64_t>(H) * c.rows_q;
+  a.seqlen_q = c.seqlen_q;
+  a.seqlen_k = c.seqlen_k;
+  a.total_q = c.rows_q;
+  a.total_k = c.rows_k;
+  a.num_heads = H;
+  a.num_b = c.num_b;
+  a.num_z = c.num_z;
+  a.ws_rows_pad = static_cast<int32_t>(pad);
+  a.q_tiles = static_cast<int32_t>(q_tiles);
+  a.k_tiles = static_cast<int32_t>(k_tiles);
+  a.scale = c.scale;
+  a.scale_log2 = c.scale * 1.4426950408889634f;
+  const int err = sdpa03::launch_attn_bwd(a, c.dtype, c.head_dim, c.mode, c.causal != 0, c.stream);
+  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -234,64 +344,53 @@ sdpa_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const int64_t o_stride[4], const int64_t dout_stride[4], float scale,
                      int32_t causal, void* workspace, uint64_t workspace_bytes,
                      void* hip_stream) {
-  sdpa_status st = check_common(dtype, head_dim, scale);
-  if (st != SDPA_OK) return st;
-  if (dtype == SDPA_F32) return SDPA_ERR_DTYPE;
+  BwdCall c{q, k, v, o, dout, lse, dq, dk, dv, dtype, B, H, seqlen_q, seqlen_k, head_dim,
+            q_stride, k_stride, v_stride, o_stride, dout_stride, scale, causal, workspace,
+            workspace_bytes, hip_stream, sdpa03::MODE_DENSE, B, seqlen_q, seqlen_k,
+            nullptr, nullptr};
   if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H == 0 || (seqlen_q == 0 && seqlen_k == 0)) return SDPA_OK;
-  // Query side (q, o, dout, lse, dq) is needed when there are query rows; key
-  // side (k, v, dk, dv) when there are keys.
-  if (seqlen_q > 0 && (!q || !o || !dout || !lse || !dq)) return SDPA_ERR_NULL;
-  if (seqlen_k > 0 && (!k || !v || !dk || !dv)) return SDPA_ERR_NULL;
-  if (seqlen_q > 0 && seqlen_k > 0 && (!q || !k)) return SDPA_ERR_NULL;
-  const int es = elem_size(dtype);
-  const View views[] = {
-      {q, {B, H, seqlen_q, head_dim}, q_stride},     {dq, {B, H, seqlen_q, head_dim}, q_stride},
-      {o, {B, H, seqlen_q, head_dim}, o_stride},     {dout, {B, H, seqlen_q, head_dim}, dout_stride},
-      {k, {B, H, seqlen_k, head_dim}, k_stride},     {dk, {B, H, seqlen_k, head_dim}, k_stride},
-      {v, {B, H, seqlen_k, head_dim}, v_stride},     {dv, {B, H, seqlen_k, head_dim}, v_stride},
-  };
-  for (int i = 0; i < 8; ++i) {
-    const bool key_side = i >= 4;
-    if ((key_side ? seqlen_k : seqlen_q) == 0) continue;
-    if ((st = check_view(views[i], es, true)) != SDPA_OK) return st;
-  }
-  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
-  const int64_t pad = sdpa03::bwd_ws_rows_pad(seqlen_q);
-  const uint64_t need = 2ull * static_cast<uint64_t>(B) * H * pad * 4ull;
-  if (seqlen_q > 0 && (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 ||
-                       workspace_bytes < need))
-    return SDPA_ERR_WORKSPACE;
-  const int64_t q_tiles = (static_cast<int64_t>(seqlen_q) + sdpa03::kBwdDqRows - 1) / sdpa03::kBwdDqRows;
-  const int64_t k_tiles = (static_cast<int64_t>(seqlen_k) + sdpa03::kBwdDkvKeys - 1) / sdpa03::kBwdDkvKeys;
-  const int64_t groups = static_cast<int64_t>(B) * H;
-  if (q_tiles * groups > kMaxGrid || k_tiles * groups > kMaxGrid ||
-      groups * pad > (int64_t(1) << 40))
-    return SDPA_ERR_SHAPE;
+  return run_bwd(c);
+}
 
-  sdpa03::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv;
-  a.ws_delta = static_cast<float*>(workspace);
-  a.ws_lse2 = seqlen_q > 0 ? static_cast<float*>(workspace) + groups * pad : nullptr;
-  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
-  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
-  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
-  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
-  set_strides(dout_stride, a.do_sb, a.do_sh, a.do_ss);
-  a.lse_sh = seqlen_q;
-  a.lse_sb = static_cast<int64_t>(H) * seqlen_q;
-  a.seqlen_q = seqlen_q;
-  a.seqlen_k = seqlen_k;
-  a.num_heads = H;
-  a.num_z = B;
-  a.ws_rows_pad = static_cast<int32_t>(pad);
-  a.q_tiles = static_cast<int32_t>(q_tiles);
-  a.k_tiles = static_cast<int32_t>(k_tiles);
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  const int err = sdpa03::launch_attn_bwd(a, dtype, head_dim, causal != 0, hip_stream);
-  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
+sdpa_status attn_bwd_compact_varlen(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dout, const float* lse, void* dq, void* dk,
+                                    void* dv, sdpa_dtype dtype, int32_t B, int32_t H,
+                                    int32_t total_q, int32_t total_k, int32_t head_dim,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t num_seqs, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k, const int64_t q_stride[4],
+                                    const int64_t k_stride[4], const int64_t v_stride[4],
+                                    const int64_t o_stride[4], const int64_t dout_stride[4],
+                                    float scale, int32_t causal, void* workspace,
+                                    uint64_t workspace_bytes, void* hip_stream) {
+  if (B != 1) return SDPA_ERR_BATCH;
+  if (H < 0 || total_q < 0 || total_k < 0) return SDPA_ERR_SHAPE;
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > total_q ||
+      max_seqlen_k > total_k)
+    return SDPA_ERR_SEQLEN;
+  BwdCall c{q, k, v, o, dout, lse, dq, dk, dv, dtype, 1, H, total_q, total_k, head_dim,
+            q_stride, k_stride, v_stride, o_stride, dout_stride, scale, causal, workspace,
+            workspace_bytes, hip_stream, sdpa03::MODE_COMPACT, num_seqs, max_seqlen_q,
+            max_seqlen_k, cu_seqlens_q, cu_seqlens_k};
+  return run_bwd(c);
+}
+
+sdpa_status attn_bwd_padded_varlen(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, sdpa_dtype dtype, int32_t B, int32_t H,
+                                   int32_t seqlen_q_max, int32_t seqlen_k_max,
+                                   int32_t head_dim, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, const int64_t q_stride[4],
+                                   const int64_t k_stride[4], const int64_t v_stride[4],
+                                   const int64_t o_stride[4], const int64_t dout_stride[4],
+                                   float scale, int32_t causal, void* workspace,
+                                   uint64_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || H < 0 || seqlen_q_max < 0 || seqlen_k_max < 0) return SDPA_ERR_SHAPE;
+  BwdCall c{q, k, v, o, dout, lse, dq, dk, dv, dtype, B, H, seqlen_q_max, seqlen_k_max,
+            head_dim, q_stride, k_stride, v_stride, o_stride, dout_stride, scale, causal,
+            workspace, workspace_bytes, hip_stream, sdpa03::MODE_PADDED, B, seqlen_q_max,
+            seqlen_k_max, cu_seqlens_q, cu_seqlens_k};
+  return run_bwd(c);
 }
 
 sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t total,

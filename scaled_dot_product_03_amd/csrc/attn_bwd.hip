@@ -162,22 +162,34 @@ __device__ __forceinline__ void store_row(T* row, const f32x16 (&acc)[DB], float
 // Prep: delta = rowsum(dO * O) and LSE * log2(e) per workspace row.  D / 8
 // threads share a row, each reading 16 contiguous bytes of O and of dO (so a
 // wave reads whole rows), and a butterfly over the row's threads sums them.
-// Padding rows (past seqlen_q) get delta = 0 and +inf, so that any weight
-// computed from them is exactly 0.
+// Rows that belong to no sequence (past the end, or padding) get delta = 0
+// and +inf, so that any weight computed from them is exactly 0.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
   constexpr int kThreadsPerRow = D / 8;
   constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
   const int c = threadIdx.x % kThreadsPerRow;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
-  const int64_t rows = static_cast<int64_t>(a.num_z) * a.num_heads * a.ws_rows_pad;
+  const int64_t rows = static_cast<int64_t>(a.num_b) * a.num_heads * a.ws_rows_pad;
   const bool in_range = gid < rows;
   const int64_t i = gid % a.ws_rows_pad;
   const int64_t zh = gid / a.ws_rows_pad;
   const int64_t h = zh % a.num_heads;
-  const int64_t z = zh / a.num_heads;
-  const bool real_row = in_range && i < a.seqlen_q;
+  const int64_t z = zh / a.num_heads;  // batch of the rank-4 view
+  // Rows that belong to a sequence: all rows (dense), the tokens before the
+  // last sequence's end (compact), the batch's true length (padded).
+  int64_t real_rows = a.total_q;
+  if constexpr (MODE == MODE_COMPACT) {
+    real_rows = min(max(static_cast<int64_t>(a.cu_q[a.num_z]), int64_t(0)),
+                    static_cast<int64_t>(a.total_q));
+  } else if constexpr (MODE == MODE_PADDED) {
+    if (in_range) {
+      const int64_t len = static_cast<int64_t>(a.cu_q[z + 1]) - a.cu_q[z];
+      real_rows = min(max(len, int64_t(0)), static_cast<int64_t>(a.total_q));
+    }
+  }
+  const bool real_row = in_range && i < real_rows;
   float acc = 0.f;
   if (real_row) {
     const T* orow = static_cast<const T*>(a.o) + z * a.o_sb + h * a.o_sh + i * a.o_ss;
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
 // dQ: one workgroup per 256 query rows of one (batch, head); 8 waves of 32
 // rows; key tiles of 64 stream through two LDS stages.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = kBwdDqRows / 32;
   constexpr int BM = kBwdDqRows;
@@ -232,8 +244,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   }
   const int h = static_cast<int>(g % static_cast<uint32_t>(a.num_heads));
   const int z = static_cast<int>(g / static_cast<uint32_t>(a.num_heads));
+  const SeqRange sr =
+      seq_range_of<MODE>(a.cu_q, a.cu_k, a.total_q, a.total_k, a.seqlen_q, a.seqlen_k, z);
   const int m0 = m * BM;
-  if (m0 >= a.seqlen_q) return;
+  if (m0 >= sr.len_q) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,13 +255,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const int li = lane & 31;
   const int lh = lane >> 5;
   const int row0 = m0 + wave * 32;
-  const int qi = row0 + li;
-  const bool row_ok = qi < a.seqlen_q;
+  const int qi = row0 + li;                       // local query row
+  const bool row_ok = qi < sr.len_q;
+  const int64_t token = static_cast<int64_t>(sr.q_start) + qi;  // row of the rank-4 view
 
-  const T* qrow = static_cast<const T*>(a.q) + z * a.q_sb + h * a.q_sh + static_cast<int64_t>(qi) * a.q_ss;
-  const T* drow = static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh + static_cast<int64_t>(qi) * a.do_ss;
-  const char* kp = reinterpret_cast<const char*>(static_cast<const T*>(a.k) + z * a.k_sb + h * a.k_sh);
-  const char* vp = reinterpret_cast<const char*>(static_cast<const T*>(a.v) + z * a.v_sb + h * a.v_sh);
+  const T* qrow = static_cast<const T*>(a.q) + sr.b * a.q_sb + h * a.q_sh + token * a.q_ss;
+  const T* drow = static_cast<const T*>(a.dout) + sr.b * a.do_sb + h * a.do_sh + token * a.do_ss;
+  const char* kp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.k) + sr.b * a.k_sb + h * a.k_sh +
+      static_cast<int64_t>(sr.k_start) * a.k_ss);
+  const char* vp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.v) + sr.b * a.v_sb + h * a.v_sh +
+      static_cast<int64_t>(sr.k_start) * a.v_ss);
   const int64_t k_row_bytes = a.k_ss * static_cast<int64_t>(sizeof(T));
   const int64_t v_row_bytes = a.v_ss * static_cast<int64_t>(sizeof(T));
 
@@ -255,7 +274,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   frag df[D / 16];
   load_row_frags<T, D>(qrow, row_ok, lh, qf);
   load_row_frags<T, D>(drow, row_ok, lh, df);
-  const int64_t wrow = static_cast<int64_t>(g) * a.ws_rows_pad + qi;
+  const int64_t wrow = (static_cast<int64_t>(sr.b) * a.num_heads + h) * a.ws_rows_pad + token;
   const float lse2 = row_ok ? a.ws_lse2[wrow] : 0.f;
   const float delta = row_ok ? a.ws_delta[wrow] : 0.f;
   const float c2 = a.scale_log2;
@@ -264,8 +283,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  int kend = a.seqlen_k;
-  if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, a.seqlen_q));
+  int kend = sr.len_k;
+  if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, sr.len_q));
   const int n_tiles = (kend + BN - 1) / BN;
 
   KCopy kcopy;
@@ -291,14 +310,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       tile_rows_x_regs<T, D, kRowK, 1>(kb, qf, li, lh, st);
       f32x16 dpt[1] = {f32x16{}};
       tile_rows_x_regs<T, D, kRowV, 1>(vb, df, li, lh, dpt);
-      const bool need_mask = (j0 + 32 > a.seqlen_k) || (CAUSAL && j0 + 31 > row0);
+      const bool need_mask = (j0 + 32 > sr.len_k) || (CAUSAL && j0 + 31 > row0);
       frag w[1][2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(st[0][r], c2, -lse2));
         if (need_mask) {
           const int key = j0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (!(key < a.seqlen_k && (!CAUSAL || key <= qi))) p = 0.f;
+          if (!(key < sr.len_k && (!CAUSAL || key <= qi))) p = 0.f;
         }
         w[0][r >> 3][r & 7] = static_cast<T>(p * (dpt[0][r] - delta));
       }
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 
   if (row_ok) {
-    T* dqrow = static_cast<T*>(a.dq) + z * a.q_sb + h * a.q_sh + static_cast<int64_t>(qi) * a.q_ss;
+    T* dqrow = static_cast<T*>(a.dq) + sr.b * a.q_sb + h * a.q_sh + token * a.q_ss;
     store_row<T, DB>(dqrow, acc, a.scale, lh);
   }
 }
@@ -341,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 // With D = 128 the wave's K and V rows and both accumulators take more than
 // half a SIMD's registers: one wave per SIMD.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = kBwdDkvKeys / 32;
   constexpr int BQ = 64;
@@ -369,8 +388,10 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   }
   const int h = static_cast<int>(g % static_cast<uint32_t>(a.num_heads));
   const int z = static_cast<int>(g / static_cast<uint32_t>(a.num_heads));
+  const SeqRange sr =
+      seq_range_of<MODE>(a.cu_q, a.cu_k, a.total_q, a.total_k, a.seqlen_q, a.seqlen_k, z);
   const int n0 = kt * kBwdDkvKeys;
-  if (n0 >= a.seqlen_k) return;
+  if (n0 >= sr.len_k) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -378,17 +399,24 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   const int li = lane & 31;
   const int lh = lane >> 5;
   const int key0 = n0 + wave * 32;  // first key of this wave
-  const int kj = key0 + li;         // this lane's key
-  const bool key_ok = kj < a.seqlen_k;
+  const int kj = key0 + li;         // this lane's key (local)
+  const bool key_ok = kj < sr.len_k;
+  const int64_t ktoken = static_cast<int64_t>(sr.k_start) + kj;  // row of the rank-4 view
 
-  const T* krow = static_cast<const T*>(a.k) + z * a.k_sb + h * a.k_sh + static_cast<int64_t>(kj) * a.k_ss;
-  const T* vrow = static_cast<const T*>(a.v) + z * a.v_sb + h * a.v_sh + static_cast<int64_t>(kj) * a.v_ss;
-  const char* qp = reinterpret_cast<const char*>(static_cast<const T*>(a.q) + z * a.q_sb + h * a.q_sh);
-  const char* dp = reinterpret_cast<const char*>(static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh);
+  const T* krow = static_cast<const T*>(a.k) + sr.b * a.k_sb + h * a.k_sh + ktoken * a.k_ss;
+  const T* vrow = static_cast<const T*>(a.v) + sr.b * a.v_sb + h * a.v_sh + ktoken * a.v_ss;
+  const char* qp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.q) + sr.b * a.q_sb + h * a.q_sh +
+      static_cast<int64_t>(sr.q_start) * a.q_ss);
+  const char* dp = reinterpret_cast<const char*>(
+      static_cast<const T*>(a.dout) + sr.b * a.do_sb + h * a.do_sh +
+      static_cast<int64_t>(sr.q_start) * a.do_ss);
   const int64_t q_row_bytes = a.q_ss * static_cast<int64_t>(sizeof(T));
   const int64_t d_row_bytes = a.do_ss * static_cast<int64_t>(sizeof(T));
-  const float* lse2p = a.ws_lse2 + static_cast<int64_t>(g) * a.ws_rows_pad;
-  const float* deltap = a.ws_delta + static_cast<int64_t>(g) * a.ws_rows_pad;
+  // Workspace rows of this sequence's query rows (local row q at [q]).
+  const int64_t wbase = (static_cast<int64_t>(sr.b) * a.num_heads + h) * a.ws_rows_pad + sr.q_start;
+  const float* lse2p = a.ws_lse2 + wbase;
+  const float* deltap = a.ws_delta + wbase;
 
   frag kf[D / 16];
   frag vf[D / 16];
@@ -406,7 +434,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
 
   // Query rows before the workgroup's first key see none of its keys.
   const int qbeg = CAUSAL ? (n0 / BQ) * BQ : 0;
-  const int n_tiles = a.seqlen_q > qbeg ? (a.seqlen_q - qbeg + BQ - 1) / BQ : 0;
+  const int n_tiles = sr.len_q > qbeg ? (sr.len_q - qbeg + BQ - 1) / BQ : 0;
 
   QCopy qcopy;
   QCopy dcopy;
@@ -414,7 +442,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   dcopy.init(wave, lane, d_row_bytes);
   auto issue = [&](int t, T* qb, T* db_) {
     const int q0 = qbeg + t * BQ;
-    const int rows = t < n_tiles ? a.seqlen_q - q0 : 0;
+    const int rows = t < n_tiles ? sr.len_q - q0 : 0;
     qcopy.issue(qp + q0 * q_row_bytes, rows, q_row_bytes, qb, wave);
     dcopy.issue(dp + q0 * d_row_bytes, rows, d_row_bytes, db_, wave);
   };
@@ -431,20 +459,21 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
       const T* db_ = dc + nb * 32 * kRow / static_cast<int>(sizeof(T));
       f32x16 s[1] = {f32x16{}};
       tile_rows_x_regs<T, D, kRow, 1>(qb, kf, li, lh, s);
-      const bool need_mask = (q0 + 32 > a.seqlen_q) || (CAUSAL && q0 < key0 + 31);
+      const bool need_mask = (q0 + 32 > sr.len_q) || (CAUSAL && q0 < key0 + 31);
       float pr[16];
       frag w[1][2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = q0 + 8 * g4 + 4 * lh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2p + qr);
+        f32x4 l4;  // the sequence may start at any row: 4-byte aligned copy
+        __builtin_memcpy(&l4, lse2p + qr, sizeof(l4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           float p = __builtin_amdgcn_exp2f(fmaf(s[0][r], c2, -l4[e]));
           if (need_mask) {
             const int q = qr + e;
-            if (!(q < a.seqlen_q && (!CAUSAL || kj <= q))) p = 0.f;
+            if (!(q < sr.len_q && (!CAUSAL || kj <= q))) p = 0.f;
           }
           pr[r] = p;
           w[0][r >> 3][r & 7] = static_cast<T>(p);
@@ -456,7 +485,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
       frag ws[1][2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(deltap + q0 + 8 * g4 + 4 * lh);
+        f32x4 d4;
+        __builtin_memcpy(&d4, deltap + q0 + 8 * g4 + 4 * lh, sizeof(d4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -487,49 +517,61 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   }
 
   if (key_ok) {
-    T* dkrow = static_cast<T*>(a.dk) + z * a.k_sb + h * a.k_sh + static_cast<int64_t>(kj) * a.k_ss;
-    T* dvrow = static_cast<T*>(a.dv) + z * a.v_sb + h * a.v_sh + static_cast<int64_t>(kj) * a.v_ss;
+    T* dkrow = static_cast<T*>(a.dk) + sr.b * a.k_sb + h * a.k_sh + ktoken * a.k_ss;
+    T* dvrow = static_cast<T*>(a.dv) + sr.b * a.v_sb + h * a.v_sh + ktoken * a.v_ss;
     store_row<T, DB>(dkrow, dk, a.scale, lh);
     store_row<T, DB>(dvrow, dv, 1.f, lh);
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int MODE, bool CAUSAL>
 int launch_typed(const BwdArgs& a, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(a.num_z) * a.num_heads * a.ws_rows_pad;
+  const int64_t rows = static_cast<int64_t>(a.num_b) * a.num_heads * a.ws_rows_pad;
   const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
-  if (a.seqlen_q > 0) {
+  if (a.q_tiles > 0) {
     constexpr int64_t kRowsPerBlock = 256 / (D / 8);
-    hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D>),
+    hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D, MODE>),
                        dim3(static_cast<uint32_t>((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                        dim3(256), 0, s, a);
     int err = static_cast<int>(hipGetLastError());
     if (err != 0) return err;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>),
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MODE, CAUSAL>),
                        dim3(static_cast<uint32_t>(a.q_tiles) * groups), dim3(kBwdDqRows * 2), 0, s, a);
     err = static_cast<int>(hipGetLastError());
     if (err != 0) return err;
   }
   if (a.k_tiles > 0) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MODE, CAUSAL>),
                        dim3(static_cast<uint32_t>(a.k_tiles) * groups), dim3(kBwdDkvKeys * 2), 0, s, a);
     return static_cast<int>(hipGetLastError());
   }
   return 0;
 }
 
+template <typename T, int D>
+int launch_mode(const BwdArgs& a, int mode, bool causal, hipStream_t s) {
+  switch (mode) {
+    case MODE_DENSE:
+      return causal ? launch_typed<T, D, MODE_DENSE, true>(a, s) : launch_typed<T, D, MODE_DENSE, false>(a, s);
+    case MODE_COMPACT:
+      return causal ? launch_typed<T, D, MODE_COMPACT, true>(a, s) : launch_typed<T, D, MODE_COMPACT, false>(a, s);
+    default:
+      return causal ? launch_typed<T, D, MODE_PADDED, true>(a, s) : launch_typed<T, D, MODE_PADDED, false>(a, s);
+  }
+}
+
 template <typename T>
-int launch_dim(const BwdArgs& a, int head_dim, bool causal, hipStream_t s) {
-  if (head_dim == 64) return causal ? launch_typed<T, 64, true>(a, s) : launch_typed<T, 64, false>(a, s);
-  return causal ? launch_typed<T, 128, true>(a, s) : launch_typed<T, 128, false>(a, s);
+int launch_dim(const BwdArgs& a, int head_dim, int mode, bool causal, hipStream_t s) {
+  return head_dim == 64 ? launch_mode<T, 64>(a, mode, causal, s) : launch_mode<T, 128>(a, mode, causal, s);
 }
 
 }  // namespace
 
-int launch_attn_bwd(const BwdArgs& a, int dtype, int head_dim, bool causal, void* stream) {
+int launch_attn_bwd(const BwdArgs& a, int dtype, int head_dim, int mode, bool causal,
+                    void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == 1 ? launch_dim<_Float16>(a, head_dim, causal, s)
-                    : launch_dim<__bf16>(a, head_dim, causal, s);
+  return dtype == DT_F16 ? launch_dim<_Float16>(a, head_dim, mode, causal, s)
+                         : launch_dim<__bf16>(a, head_dim, mode, causal, s);
 }
 
 }  // namespace sdpa03

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fwd_args.h"  // Mode
+
 namespace sdpa03 {
 
 using f32x16 = float __attribute__((ext_vector_type(16)));
@@ -199,5 +201,54 @@ struct TileCopy {
 #endif
   }
 };
+
+struct SeqRange {
+  int64_t b;    // batch index into the rank-4 view
+  int q_start;  // first token of the sequence along seq (compact), else 0
+  int k_start;
+  int len_q;
+  int len_k;
+};
+
+// Rows and keys of program z (forward and backward kernels).  seqlen_q and seqlen_k are
+// the rank-4 view's sequence lengths (dense), the maximum lengths (compact)
+// or the padded lengths (padded).  Dense: batch z, all rows.  Compact: batch 0,
+// tokens [cu[z], cu[z+1]).  Padded: batch z, lengths cu[z+1] - cu[z] from
+// offset 0 (the padded branch of the fwd_kernel.py excerpt quoted in
+// AOTriton PR #31).  Ranges are clamped to the addressable rows so that
+// malformed cu_seqlens can never move an access out of bounds: compact
+// token ranges to [0, total), padded lengths to [0, padded length].
+template <int MODE>
+__device__ __forceinline__ SeqRange seq_range_of(const int32_t* cu_q, const int32_t* cu_k,
+                                                 int total_q, int total_k, int seqlen_q,
+                                                 int seqlen_k, int z) {
+  SeqRange r;
+  if constexpr (MODE == MODE_DENSE) {
+    r.b = z;
+    r.q_start = 0;
+    r.k_start = 0;
+    r.len_q = seqlen_q;
+    r.len_k = seqlen_k;
+  } else if constexpr (MODE == MODE_COMPACT) {
+    const int q0 = min(max(cu_q[z], 0), total_q);
+    const int q1 = min(max(cu_q[z + 1], q0), total_q);
+    const int k0 = min(max(cu_k[z], 0), total_k);
+    const int k1 = min(max(cu_k[z + 1], k0), total_k);
+    r.b = 0;
+    r.q_start = q0;
+    r.k_start = k0;
+    r.len_q = min(q1 - q0, seqlen_q);
+    r.len_k = min(k1 - k0, seqlen_k);
+  } else {
+    const int64_t lq = static_cast<int64_t>(cu_q[z + 1]) - cu_q[z];
+    const int64_t lk = static_cast<int64_t>(cu_k[z + 1]) - cu_k[z];
+    r.b = z;
+    r.q_start = 0;
+    r.k_start = 0;
+    r.len_q = static_cast<int>(min(max(lq, int64_t(0)), static_cast<int64_t>(seqlen_q)));
+    r.len_k = static_cast<int>(min(max(lk, int64_t(0)), static_cast<int64_t>(seqlen_k)));
+  }
+  return r;
+}
 
 }  // namespace sdpa03

@@ -370,49 +370,10 @@ __device__ __forceinline__ void decode_tile(int m_tiles, int num_heads, int num_
   z = static_cast<int>(rest / static_cast<uint32_t>(num_heads));
 }
 
-struct SeqRange {
-  int64_t b;    // batch index into the rank-4 view
-  int q_start;  // first token of the sequence along seq (compact), else 0
-  int k_start;
-  int len_q;
-  int len_k;
-};
-
-// Rows and keys of program z.  Dense: batch z, all rows.  Compact: batch 0,
-// tokens [cu[z], cu[z+1]).  Padded: batch z, lengths cu[z+1] - cu[z] from
-// offset 0 (the padded branch of the fwd_kernel.py excerpt quoted in
-// AOTriton PR #31).  Ranges are clamped to the addressable rows so that
-// malformed cu_seqlens can never move an access out of bounds: compact
-// token ranges to [0, total), padded lengths to [0, padded length].
+// Rows and keys of program z (the shared rule in attn_common.h).
 template <int MODE>
 __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
-  SeqRange r;
-  if constexpr (MODE == MODE_DENSE) {
-    r.b = z;
-    r.q_start = 0;
-    r.k_start = 0;
-    r.len_q = a.seqlen_q;
-    r.len_k = a.seqlen_k;
-  } else if constexpr (MODE == MODE_COMPACT) {
-    const int q0 = min(max(a.cu_q[z], 0), a.total_q);
-    const int q1 = min(max(a.cu_q[z + 1], q0), a.total_q);
-    const int k0 = min(max(a.cu_k[z], 0), a.total_k);
-    const int k1 = min(max(a.cu_k[z + 1], k0), a.total_k);
-    r.b = 0;
-    r.q_start = q0;
-    r.k_start = k0;
-    r.len_q = min(q1 - q0, a.seqlen_q);
-    r.len_k = min(k1 - k0, a.seqlen_k);
-  } else {
-    const int64_t lq = static_cast<int64_t>(a.cu_q[z + 1]) - a.cu_q[z];
-    const int64_t lk = static_cast<int64_t>(a.cu_k[z + 1]) - a.cu_k[z];
-    r.b = z;
-    r.q_start = 0;
-    r.k_start = 0;
-    r.len_q = static_cast<int>(min(max(lq, int64_t(0)), static_cast<int64_t>(a.seqlen_q)));
-    r.len_k = static_cast<int>(min(max(lk, int64_t(0)), static_cast<int64_t>(a.seqlen_k)));
-  }
-  return r;
+  return seq_range_of<MODE>(a.cu_q, a.cu_k, a.total_q, a.total_k, a.seqlen_q, a.seqlen_k, z);
 }
 
 // ---------------------------------------------------------------------------

@@ -37,7 +37,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_compact_varlen", "attn_fwd_padded_varlen", "attn_fwd_splitk",
-              "sdpa_fwd_splitk_plan", "sdpa_status_string"):
+              "sdpa_fwd_splitk_plan", "attn_bwd", "attn_bwd_compact_varlen",
+              "attn_bwd_padded_varlen", "sdpa_bwd_workspace_bytes", "sdpa_status_string"):
         assert n in names
     assert set(names) == set(binding.EXPORTED)
 
@@ -205,3 +206,77 @@ def test_splitk_validation(kw, status):
 @no_gpu
 def test_splitk_empty_problem_is_ok_without_launch():
     assert _splitk(q=None, ws=None, Sq=0) == 0
+
+
+# --- backward: workspace size and validation --------------------------------
+
+def test_bwd_workspace_bytes():
+    # two fp32 values per query row, rows of each (batch, head) rounded up to
+    # 64 with 64 spare rows
+    assert binding.bwd_workspace_bytes(4, 16, 2048) == 2 * 4 * 16 * (2048 + 64) * 4
+    assert binding.bwd_workspace_bytes(1, 3, 65) == 2 * 3 * (128 + 64) * 4
+    assert binding.bwd_workspace_bytes(2, 2, 0) == 2 * 2 * 2 * 64 * 4
+    with pytest.raises(binding.SdpaError) as e:
+        binding.bwd_workspace_bytes(1, -1, 5)
+    assert e.value.status == 4
+
+
+def _bwd(fn="attn_bwd", **kw):
+    lib = binding.load_library()
+    a = dict(q=DUMMY, k=DUMMY, v=DUMMY, o=DUMMY, do=DUMMY, lse=DUMMY, dq=DUMMY, dk=DUMMY,
+             dv=DUMMY, dtype=2, B=1, H=2, Sq=64, Sk=64, D=64, cu_q=DUMMY, cu_k=DUMMY,
+             num_seqs=3, max_q=40, max_k=40, scale=0.125, ws=DUMMY, ws_bytes=1 << 30,
+             qs=_st(64 * 2 * 64, 64 * 64, 64, 1))
+    a.update(kw)
+    st = _st(64 * 2 * 64, 64 * 64, 64, 1)
+    ptrs = [a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")]
+    tail = [a["qs"], st, st, st, st, a["scale"], 1, a["ws"], a["ws_bytes"], None]
+    if fn == "attn_bwd":
+        return lib.attn_bwd(*ptrs, a["dtype"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], *tail)
+    if fn == "compact":
+        return lib.attn_bwd_compact_varlen(*ptrs, a["dtype"], a["B"], a["H"], a["Sq"], a["Sk"],
+                                           a["D"], a["cu_q"], a["cu_k"], a["num_seqs"],
+                                           a["max_q"], a["max_k"], *tail)
+    return lib.attn_bwd_padded_varlen(*ptrs, a["dtype"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"],
+                                      a["cu_q"], a["cu_k"], *tail)
+
+
+@no_gpu
+@pytest.mark.parametrize("fn", ["attn_bwd", "compact", "padded"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), 2), (dict(dtype=9), 2), (dict(D=80), 3), (dict(scale=0.0), 9),
+    (dict(dq=None), 1), (dict(do=None), 1), (dict(dv=None), 1), (dict(lse=None), 1),
+    (dict(ws=None), 11), (dict(ws=DUMMY + 4), 11), (dict(ws_bytes=1024), 11),
+    (dict(qs=_st(64 * 2 * 64, 64 * 64, 64, 2)), 5), (dict(dk=DUMMY + 8), 6),
+    (dict(lse=DUMMY + 2), 6), (dict(Sk=-1), 4),
+])
+def test_bwd_validation(fn, kw, status):
+    assert _bwd(fn, **kw) == status
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=2), 7), (dict(B=0), 7), (dict(cu_q=None), 1), (dict(cu_k=DUMMY + 2), 6),
+    (dict(num_seqs=-1), 8), (dict(max_q=65), 8), (dict(max_k=-1), 8),
+])
+def test_bwd_compact_validation(kw, status):
+    assert _bwd("compact", **kw) == status
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [(dict(cu_k=None), 1), (dict(cu_q=DUMMY + 1), 6),
+                                       (dict(B=-1), 4)])
+def test_bwd_padded_validation(kw, status):
+    assert _bwd("padded", **kw) == status
+
+
+@no_gpu
+def test_bwd_empty_problems_are_ok_without_launch():
+    # nothing to write: no pointer or workspace is needed
+    none = dict(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None,
+                ws=None)
+    assert _bwd("attn_bwd", Sq=0, Sk=0, **none) == 0
+    assert _bwd("attn_bwd", H=0, **none) == 0
+    assert _bwd("compact", num_seqs=0, **none) == 0
+    assert _bwd("compact", max_q=0, max_k=0, **none) == 0
+    assert _bwd("padded", B=0, **none) == 0

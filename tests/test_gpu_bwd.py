@@ -1,11 +1,14 @@
-"""GPU parity of the dense backward (attn_bwd) against the float64 oracle.
+"""GPU parity of the backward (attn_bwd and its compact and padded varlen
+forms) against the float64 oracle.
 
-The forward's own outputs (O and LSE from attn_fwd on the GPU) feed the
+The forward's own outputs (O and LSE from the GPU forward) feed the
 backward, as in training; the oracle's gradients are computed from Q, K, V
 and dO alone.  Every gradient element of small and ragged shapes is compared
 (both masks, D 64 and 128, bf16 and fp16); whole heads of the dense bf16
-B4 H16 S2048 D128 workload are compared in full.  Also: determinism, empty
-query or key axes, the fp32 refusal and a too-small workspace.
+B4 H16 S2048 D128 workload and whole (sequence, head) pairs of the THD and
+padded workloads are compared in full.  Also: determinism, empty query or key
+axes, untouched rows outside every sequence, no gradient crossing a sequence
+boundary, the fp32 refusal and a too-small workspace.
 
 Tolerance.  The gradients are sums of products whose factors were rounded to
 the input type (P and dS before the matrix products, O before delta), so the
@@ -25,7 +28,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import sdpa_dense_bwd
+from oracle import (attention_head_bwd, sdpa_compact_varlen_bwd, sdpa_dense_bwd,
+                    sdpa_padded_varlen_bwd)
 from parity import to64
 from scaled_dot_product_03_amd import binding, inputs
 
@@ -60,6 +64,10 @@ def _grad_check(got, ref, dt, label):
     assert np.isfinite(got).all(), label
     assert mx <= MAX_REL[dt] * scale, label
     assert mean <= MEAN_REL[dt] * scale, label
+
+
+def _dev(t):
+    return t.to(DEV)
 
 
 def _run(B, H, Sq, Sk, D, dt, causal, seed, heads=None):
@@ -159,3 +167,188 @@ def test_bwd_refusals_leave_outputs_untouched():
     assert e.value.status == 11
     torch.cuda.synchronize()
     assert (dq == 5.0).all()
+
+
+# ---------------------------------------------------------------------------
+# Variable-length backward
+# ---------------------------------------------------------------------------
+
+def _dout_like(shape, dt, seed):
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(inputs.DTYPES[dt])
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("bf16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_compact_small(dt, D, causal):
+    lengths_q = [1, 128, 129, 300, 0, 77, 255]
+    lengths_k = [1, 128, 129, 300, 5, 0, 400]
+    H = 3
+    _log(f"bwd compact small {dt} D{D} causal={causal}")
+    x = inputs.compact_inputs(len(lengths_q), H, D, dt, seed=61, len_lo=1, len_hi=2,
+                              lengths_q=lengths_q, lengths_k=lengths_k, extra_tokens=5)
+    do = _dout_like(tuple(x.q.shape), dt, 62)
+    q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+    o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                             scale=x.scale, causal=causal)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    binding.attn_bwd_compact_varlen(q, k, v, o, dod, lse, x.cu_seqlens_q, x.cu_seqlens_k,
+                                    scale=x.scale, causal=causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = sdpa_compact_varlen_bwd(to64(x.q), to64(x.k), to64(x.v), to64(do), x.cu_seqlens_q,
+                                  x.cu_seqlens_k, x.scale, causal)
+    tq, tk = int(x.cu_seqlens_q[-1]), int(x.cu_seqlens_k[-1])
+    # tokens past the last sequence are neither read nor written
+    assert torch.isnan(dq[tq:]).all()
+    assert torch.isnan(dk[tk:]).all() and torch.isnan(dv[tk:]).all()
+    for name, g, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, (tq, tk, tk)):
+        _grad_check(g[:t], r[:t], dt, f"compact {dt} D{D} causal={causal} {name}")
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_padded_small(dt, D, causal):
+    B, H, Sq, Sk = 4, 2, 300, 270
+    lengths_q = [300, 1, 129, 0]
+    lengths_k = [270, 64, 1, 33]
+    _log(f"bwd padded small {dt} D{D} causal={causal}")
+    x = inputs.padded_inputs(B, H, Sq, Sk, D, dt, seed=71, len_lo=1, len_hi=2,
+                             lengths_q=lengths_q, lengths_k=lengths_k)
+    do = _dout_like((B, H, Sq, D), dt, 72)
+    q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, Sq), float("nan"), device=DEV)
+    binding.attn_fwd_padded_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k, scale=x.scale,
+                                   causal=causal, out=o, lse=lse)
+    # poison every input past the true lengths: it must never be read
+    for b in range(B):
+        q[b, :, lengths_q[b]:] = float("nan")
+        dod[b, :, lengths_q[b]:] = float("nan")
+        k[b, :, lengths_k[b]:] = float("inf")
+        v[b, :, lengths_k[b]:] = float("nan")
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    binding.attn_bwd_padded_varlen(q, k, v, o, dod, lse, x.cu_seqlens_q, x.cu_seqlens_k,
+                                   scale=x.scale, causal=causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = sdpa_padded_varlen_bwd(to64(x.q), to64(x.k), to64(x.v), to64(do), x.cu_seqlens_q,
+                                 x.cu_seqlens_k, x.scale, causal)
+    for b in range(B):
+        lq, lk = lengths_q[b], lengths_k[b]
+        assert torch.isnan(dq[b, :, lq:]).all()
+        assert torch.isnan(dk[b, :, lk:]).all() and torch.isnan(dv[b, :, lk:]).all()
+        for name, g, r, n in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, (lq, lk, lk)):
+            if n:
+                _grad_check(g[b, :, :n], r[b, :, :n], dt,
+                            f"padded {dt} D{D} causal={causal} b={b} {name}")
+
+
+def test_bwd_compact_no_cross_sequence_leak_bit_exact():
+    """Sequence z's Q, K and dO rows are multiples of the unit vector e_z, so
+    each of its gradients lies along e_z: a weight or gradient term taken
+    across a sequence boundary would make another column non-zero."""
+    lengths = [5, 130, 1, 257, 64, 63, 200]
+    H, D = 2, 64
+    x = inputs.compact_inputs(len(lengths), H, D, "bf16", seed=81, len_lo=1, len_hi=2,
+                              lengths_q=lengths, lengths_k=lengths)
+    cu = x.cu_seqlens_q
+    rng = np.random.default_rng(82)
+    q = torch.zeros_like(x.q)
+    k = torch.zeros_like(x.k)
+    do = torch.zeros_like(x.q)
+    for z in range(len(lengths)):
+        s, e = int(cu[z]), int(cu[z + 1])
+        for t, scale in ((q, 2.0), (k, 2.0), (do, 1.0)):
+            t[s:e, :, z] = torch.from_numpy(
+                rng.uniform(0.5, 1.0, size=(e - s, H)).astype(np.float32) * scale).to(t.dtype)
+    q, k, v, dod = _dev(q), _dev(k), _dev(x.v), _dev(do)
+    for causal in (False, True):
+        o, lse = binding.attn_fwd_compact_varlen(q, k, v, cu, cu, scale=x.scale, causal=causal)
+        grads = binding.attn_bwd_compact_varlen(q, k, v, o, dod, lse, cu, cu, scale=x.scale,
+                                                causal=causal)
+        torch.cuda.synchronize()
+        for name, g in zip(("dq", "dk", "dv"), grads):
+            g = g.cpu().float()
+            for z in range(len(lengths)):
+                blk = g[cu[z]:cu[z + 1]]
+                others = torch.cat([blk[..., :z], blk[..., z + 1:]], dim=-1)
+                assert torch.count_nonzero(others) == 0, f"{name} of sequence {z} leaked"
+            assert torch.count_nonzero(g) > 0, name
+
+
+def test_bwd_compact_deterministic():
+    x = inputs.compact_inputs(5, 2, 128, "fp16", seed=91, len_lo=1, len_hi=400)
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    do = torch.randn_like(q)
+    o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k, causal=True)
+    a = binding.attn_bwd_compact_varlen(q, k, v, o, do, lse, x.cu_seqlens_q, x.cu_seqlens_k,
+                                        causal=True)
+    b = binding.attn_bwd_compact_varlen(q, k, v, o, do, lse, x.cu_seqlens_q, x.cu_seqlens_k,
+                                        causal=True)
+    torch.cuda.synchronize()
+    for ga, gb in zip(a, b):
+        assert torch.equal(ga, gb)
+
+
+def test_bwd_workload_compact_thd_pairs():
+    """THD workload (16 sequences of 1 to 4096 tokens, H16 D128, causal bf16):
+    the whole gradients of one head of four sequences, the longest among
+    them."""
+    x = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
+    lengths = x.meta["lengths_q"]
+    _log(f"bwd compact THD lengths {lengths}")
+    do = _dout_like(tuple(x.q.shape), "bf16", 104)
+    q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+    o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                             scale=x.scale, causal=True)
+    grads = binding.attn_bwd_compact_varlen(q, k, v, o, dod, lse, x.cu_seqlens_q,
+                                            x.cu_seqlens_k, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    cu = x.cu_seqlens_q
+    order = np.argsort(lengths)
+    picks = list(dict.fromkeys([int(order[-1]), int(order[0]), int(order[len(order) // 2]), 5]))
+    for z in picks:
+        s, e = int(cu[z]), int(cu[z + 1])
+        h = (3 * z + 1) % 16
+        _log(f"  sequence {z} (length {e - s}) head {h}")
+        ref = attention_head_bwd(to64(x.q[s:e, h]), to64(x.k[s:e, h]), to64(x.v[s:e, h]),
+                                 to64(do[s:e, h]), x.scale, True)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+            _grad_check(g[s:e, h], r, "bf16", f"THD z={z} h={h} {name}")
+
+
+def test_bwd_workload_padded_pairs():
+    """Padded workload (B8 H32, 8192-row slabs, true lengths 2048 to 8192,
+    causal bf16): the whole gradients of one head of the two shortest
+    batches; padding rows stay untouched everywhere."""
+    x = inputs.workload("padded_bf16_b8h32smax8192d128_len2048to8192_causal")
+    lengths = x.meta["lengths_q"]
+    _log(f"bwd padded lengths {lengths}")
+    B, H, S, D = x.q.shape
+    do = _dout_like((B, H, S, D), "bf16", 105)
+    q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+    o, lse = binding.attn_fwd_padded_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                            scale=x.scale, causal=True)
+    scale = x.scale
+    del x  # keep host memory to the sampled heads below
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    binding.attn_bwd_padded_varlen(q, k, v, o, dod, lse, inputs.cu_from_lengths(lengths),
+                                   inputs.cu_from_lengths(lengths), causal=True, dq=dq, dk=dk,
+                                   dv=dv, scale=scale)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lengths):
+        for g in (dq, dk, dv):
+            assert torch.isnan(g[b, :, L:]).all()
+            assert torch.isfinite(g[b, :, :L]).all()
+    for b in [int(i) for i in np.argsort(lengths)[:2]]:
+        L, h = lengths[b], (5 * b + 2) % H
+        _log(f"  batch {b} (length {L}) head {h}")
+        ref = attention_head_bwd(to64(q[b, h, :L]), to64(k[b, h, :L]), to64(v[b, h, :L]),
+                                 to64(dod[b, h, :L]), scale, True)
+        for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            _grad_check(g[b, h, :L], r, "bf16", f"padded b={b} h={h} {name}")
