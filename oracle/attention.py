@@ -28,6 +28,20 @@ A row with no allowed key (only possible when ``Lk == 0``) has ``O = 0`` and
 backward what it cannot cheaply recompute; one number per query row is enough
 to rebuild P.
 
+Additive bias.  The AOTriton PR #31 (opening comment, note 1) keeps a rank-4
+bias tensor input ``b`` in every forward call, reserved there; the nvFuser
+issue points at PyTorch's ``scaled_dot_product_attention``, whose floating
+``attn_mask`` is added to the scaled scores.  With a bias the scores are::
+
+    S[i, j]  = scale * sum_d Q[i, d] * K[j, d] + bias[i, j]
+
+and everything else is unchanged.  Bias entries may be -inf (a key the row
+must not see); a row whose allowed scores are all -inf is treated like a row
+with no allowed key (``O = 0``, ``LSE = -inf``).  The bias view is indexed
+like the scores of the rank-4 view: in the compact layout it is (1, H, Tq,
+Tk) and sequence z reads the block at rows ``cu_q[z]..`` and columns
+``cu_k[z]..``; in the padded layout batch b reads rows and columns from 0.
+
 Causal alignment when ``Lq != Lk`` is not stated on the pages; this oracle
 takes the top-left reading (query i sees keys 0..i, local indices), which is
 what PyTorch's ``is_causal`` does.
@@ -58,13 +72,13 @@ __all__ = [
 ]
 
 
-def attention_head(q, k, v, scale, causal, rows=None):
+def attention_head(q, k, v, scale, causal, rows=None, bias=None):
     """Attention of one (sequence, head) in float64, score matrix materialised.
 
     q: (Lq, D), k: (Lk, D), v: (Lk, Dv).  ``rows`` optionally selects which
     local query indices to compute (their causal limit is still their own
-    index).  Returns ``(O, LSE)`` with shapes ``(len(rows), Dv)`` and
-    ``(len(rows),)``.
+    index).  ``bias`` (optional) is (Lq, Lk), added to the scaled scores.
+    Returns ``(O, LSE)`` with shapes ``(len(rows), Dv)`` and ``(len(rows),)``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -77,19 +91,28 @@ def attention_head(q, k, v, scale, causal, rows=None):
     if rows is None:
         rows = np.arange(lq)
     rows = np.asarray(rows, dtype=np.int64)
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float64)
+        if bias.shape != (lq, lk):
+            raise ValueError(f"bias must be (Lq, Lk) = {(lq, lk)}, got {bias.shape}")
+        if np.isnan(bias).any() or (bias == np.inf).any():
+            raise ValueError("bias entries must be finite or -inf")
     dv = v.shape[1]
     out = np.zeros((rows.size, dv), dtype=np.float64)
     lse = np.full((rows.size,), -np.inf, dtype=np.float64)
     if rows.size == 0 or lk == 0:
         return out, lse
 
-    # Step 1: scaled scores (one library matmul).
+    # Step 1: scaled scores (one library matmul), plus the bias.
     s = float(scale) * (q[rows] @ k.T)
-    # Step 2: which keys each row may see.
+    if bias is not None:
+        s = s + bias[rows]
+    # Step 2: which keys each row may see (a -inf score is never seen).
     key_idx = np.arange(lk)[None, :]
     allowed = np.ones((rows.size, lk), dtype=bool)
     if causal:
         allowed = key_idx <= rows[:, None]
+    allowed = allowed & (s > -np.inf)
     has_key = allowed.any(axis=1)
     # Step 3: row max over allowed keys, exponentials, row sums.
     s_masked = np.where(allowed, s, -np.inf)
@@ -125,8 +148,17 @@ def lengths_from_cu(cu, total=None):
     return lengths
 
 
-def sdpa_dense(q, k, v, scale, causal, heads=None):
-    """Dense BHSD forward.  q: (B,H,Sq,D), k/v: (B,H,Sk,D).
+def _bias_view(bias, shape):
+    """The bias as a float64 array broadcast to ``shape`` (stride-0 views of a
+    smaller bias, as PyTorch broadcasts ``attn_mask``), or None."""
+    if bias is None:
+        return None
+    return np.broadcast_to(np.asarray(bias, dtype=np.float64), shape)
+
+
+def sdpa_dense(q, k, v, scale, causal, heads=None, bias=None):
+    """Dense BHSD forward.  q: (B,H,Sq,D), k/v: (B,H,Sk,D), bias (optional)
+    broadcastable to (B,H,Sq,Sk).
 
     Returns ``(O, LSE)`` shaped (B,H,Sq,Dv) and (B,H,Sq).  ``heads``
     optionally restricts the work to a list of (b, h) pairs; the other
@@ -136,21 +168,24 @@ def sdpa_dense(q, k, v, scale, causal, heads=None):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     b_, h_, sq, _ = q.shape
+    bias = _bias_view(bias, (b_, h_, sq, k.shape[2]))
     out = np.full(q.shape[:3] + (v.shape[3],), np.nan)
     lse = np.full((b_, h_, sq), np.nan)
     pairs = [(b, h) for b in range(b_) for h in range(h_)] if heads is None else heads
     for b, h in pairs:
-        out[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal)
+        out[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal,
+                                              bias=None if bias is None else bias[b, h])
     return out, lse
 
 
-def sdpa_compact_varlen(q, k, v, cu_q, cu_k, scale, causal):
+def sdpa_compact_varlen(q, k, v, cu_q, cu_k, scale, causal, bias=None):
     """Compact variable-length forward over packed THD tokens.
 
     q: (Tq, H, D), k/v: (Tk, H, D).  Sequence z owns query tokens
     ``[cu_q[z], cu_q[z+1])`` and key tokens ``[cu_k[z], cu_k[z+1])``; the mask
-    uses indices local to the sequence.  Returns ``(O, LSE)`` shaped
-    (Tq, H, Dv) and (H, Tq); tokens past ``cu_q[-1]`` stay NaN.
+    uses indices local to the sequence.  ``bias`` (optional) is broadcastable
+    to (1, H, Tq, Tk); sequence z reads its block of it.  Returns ``(O, LSE)``
+    shaped (Tq, H, Dv) and (H, Tq); tokens past ``cu_q[-1]`` stay NaN.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -162,24 +197,27 @@ def sdpa_compact_varlen(q, k, v, cu_q, cu_k, scale, causal):
     lengths_from_cu(cu_k, k.shape[0])
     if cu_q.size != cu_k.size:
         raise ValueError("cu_seqlens_q and cu_seqlens_k need the same sequence count")
+    bias = _bias_view(bias, (1, h_, tq, k.shape[0]))
     out = np.full((tq, h_, v.shape[2]), np.nan)
     lse = np.full((h_, tq), np.nan)
     for z in range(cu_q.size - 1):
         qs, qe = cu_q[z], cu_q[z + 1]
         ks, ke = cu_k[z], cu_k[z + 1]
         for h in range(h_):
-            o_zh, lse_zh = attention_head(q[qs:qe, h], k[ks:ke, h], v[ks:ke, h], scale, causal)
+            o_zh, lse_zh = attention_head(q[qs:qe, h], k[ks:ke, h], v[ks:ke, h], scale, causal,
+                                          bias=None if bias is None else bias[0, h, qs:qe, ks:ke])
             out[qs:qe, h] = o_zh
             lse[h, qs:qe] = lse_zh
     return out, lse
 
 
-def sdpa_padded_varlen(q, k, v, cu_q, cu_k, scale, causal):
+def sdpa_padded_varlen(q, k, v, cu_q, cu_k, scale, causal, bias=None):
     """Padded variable-length forward over rank-4 BHSD slabs.
 
-    q: (B,H,Sq_max,D), k/v: (B,H,Sk_max,D).  Batch b uses rows
-    ``0 .. cu_q[b+1]-cu_q[b]-1`` and keys ``0 .. cu_k[b+1]-cu_k[b]-1``.  Rows
-    past a batch's true length are not defined and stay NaN.
+    q: (B,H,Sq_max,D), k/v: (B,H,Sk_max,D), bias (optional) broadcastable to
+    (B,H,Sq_max,Sk_max).  Batch b uses rows ``0 .. cu_q[b+1]-cu_q[b]-1`` and
+    keys ``0 .. cu_k[b+1]-cu_k[b]-1``.  Rows past a batch's true length are
+    not defined and stay NaN.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -191,12 +229,14 @@ def sdpa_padded_varlen(q, k, v, cu_q, cu_k, scale, causal):
         raise ValueError("padded varlen needs B+1 cu_seqlens entries")
     if (lq > sq).any() or (lk > k.shape[2]).any():
         raise ValueError("a true length exceeds the padded length")
+    bias = _bias_view(bias, (b_, h_, sq, k.shape[2]))
     out = np.full(q.shape[:3] + (v.shape[3],), np.nan)
     lse = np.full((b_, h_, sq), np.nan)
     for b in range(b_):
         for h in range(h_):
             o_bh, lse_bh = attention_head(
-                q[b, h, : lq[b]], k[b, h, : lk[b]], v[b, h, : lk[b]], scale, causal
+                q[b, h, : lq[b]], k[b, h, : lk[b]], v[b, h, : lk[b]], scale, causal,
+                bias=None if bias is None else bias[b, h, : lq[b], : lk[b]],
             )
             out[b, h, : lq[b]] = o_bh
             lse[b, h, : lq[b]] = lse_bh
