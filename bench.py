@@ -10,8 +10,9 @@ workload), inputs resident in HBM.  FLOPs are 4*Sq*Sk*D*H*B per forward,
 halved for causal.  The line also carries the compact varlen THD workload
 (16 sequences, lengths U{1..4096} from seed 4, H=16, D=128, bf16, causal)
 and the fp16 B=2, H=32, Sq=512, Sk=8192, D=64 workload (through attn_fwd
-and through the key-parallel attn_fwd_splitk) and the backward of the dense
-workload timed the same way, a roofline record for the dominant kernel (the
+and through the key-parallel attn_fwd_splitk), the dense workload with a full
+(B, H, Sq, Sk) additive bias, and the backward of the dense workload timed
+the same way, a roofline record for the dominant kernel (the
 non-causal forward, timed with HIP events on the stream it runs on around the
 block of its back-to-back launches) and the float64 CPU oracle timed on a bounded sample of the same
 workload.
@@ -38,6 +39,7 @@ METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16 BHSD S=2048 D=128; varlen THD)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/attn_fwd.hip",
+                  "scaled_dot_product_03_amd/csrc/attn_fwd_kernels.h",
                   "scaled_dot_product_03_amd/csrc/attn_common.h",
                   "scaled_dot_product_03_amd/csrc/dispatch_table.inc"]
 
@@ -131,6 +133,7 @@ def main():
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-bias", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (a kernel of "
                          "known HBM traffic, for scaling counter readings)")
@@ -271,6 +274,41 @@ def main():
                            "pct_mfma_peak": 100 * sf / (s_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         breakdown["dense_fp16_sq512_sk8192"] = entry
         del sq, sk, sv, so, slse, ws
+
+    if not args.no_bias:
+        # The same workload with a full (B, H, Sq, Sk) bf16 additive bias
+        # (seeded standard normal, rows padded to 8 elements in memory).  The
+        # bias is read once per allowed (row, key) tile, which makes the
+        # kernel HBM-bound: algorithmic bytes are Q, K, V, O and LSE plus the
+        # bias entries of the loaded key tiles (all of them non-causal; the
+        # tiles up to each query tile's diagonal causal).
+        bias = inputs.bias_tensor((B, H, Sq, Sk), "bf16", seed=402)
+        bpad = (Sk + 7) // 8 * 8
+        bd = torch.empty((B, H, Sq, bpad), dtype=q.dtype, device=dev)[..., :Sk]
+        bd.copy_(bias)
+        del bias
+        bm_, bn_, _ = binding.kernel_config(torch.bfloat16, D)
+        io_bytes = B * H * (2 * Sq * D * 2 + 2 * Sk * D * 2 + Sq * 4)
+        entry = {"workload": "dense_bf16_b4h16s2048d128 (seed 2) + bias (B,H,Sq,Sk) bf16 seed 402"}
+        for causal in (False, True):
+            b_avg = block_ms(lambda: binding.attn_fwd(q, k, v, scale=x.scale, causal=causal,
+                                                      out=o, lse=lse, bias=bd))
+            if causal:
+                # query tile m reads key tiles 0 .. (m+1)*bm/bn - 1, bm rows each
+                keys = sum(min(Sk, (m + 1) * bm_) for m in range((Sq + bm_ - 1) // bm_))
+                bias_bytes = B * H * bm_ * keys * 2
+            else:
+                bias_bytes = B * H * Sq * Sk * 2
+            hbm = io_bytes + bias_bytes
+            bf = dense_flops(B, H, Sq, Sk, D, causal)
+            entry["causal" if causal else "noncausal"] = {
+                "flops": bf, "avg_ms": b_avg, "tflops": bf / (b_avg * 1e-3) / 1e12,
+                "pct_mfma_peak": 100 * bf / (b_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "roofline": {"bound": "hbm", "algorithmic_bytes": hbm,
+                             "achieved_gbs": hbm / (b_avg * 1e-3) / 1e9,
+                             "frac": hbm / (b_avg * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        breakdown["dense_bf16_s2048_bias"] = entry
+        del bd
 
     if not args.no_bwd:
         # Backward of the same workload: gradients for an upstream dO drawn

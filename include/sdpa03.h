@@ -164,6 +164,59 @@ sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, 
                                    float scale, int32_t causal, void* hip_stream);
 
 /*
+ * Forward with an additive bias, one entry point per layout.  AOTriton PR #31
+ * (opening comment, note 1) keeps a rank-4 bias tensor input in its forward
+ * calls (reserved there); the nvFuser issue #2278 points at PyTorch's
+ * scaled_dot_product_attention, whose floating attn_mask is added to the
+ * scaled scores.  Here the scores become
+ *
+ *     S = scale * q k^T + bias
+ *
+ * and everything else (mask, softmax, O, LSE) is as in the call without the
+ * bias.  Arguments are those of attn_fwd, attn_fwd_compact_varlen and
+ * attn_fwd_padded_varlen, plus:
+ *  - bias: DEVICE memory of the same element type as q, read only, viewed
+ *    as a rank-4 tensor indexed like the scores of the rank-4 views:
+ *    (B, H, seqlen_q, seqlen_k) dense, (1, H, total_q, total_k) compact
+ *    (sequence z reads the block at rows cu_seqlens_q[z].. and columns
+ *    cu_seqlens_k[z]..), (B, H, seqlen_q_max, seqlen_k_max) padded (batch b
+ *    reads from row and column 0).  Only entries of allowed (row, key) pairs
+ *    are read.
+ *  - bias_stride: element strides of that view.  The key stride must be 1;
+ *    the others >= 0 (0 broadcasts, as PyTorch's expand does) and multiples
+ *    of 4 elements; the base 16-byte aligned.
+ * Entries must be finite or -inf.  A -inf entry hides the key from the row;
+ * a row whose allowed scores are all -inf gets O = 0 and LSE = -inf, like a
+ * row with no key.  Errors as the call without the bias, plus SDPA_ERR_NULL,
+ * SDPA_ERR_STRIDE and SDPA_ERR_ALIGN for the bias.  The compact layout is
+ * correct for any cu_seqlens_k, but a sequence whose keys start off a
+ * multiple of 4 tokens loads its bias element by element (slower).
+ */
+sdpa_status attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                          void* o, float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                          int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                          const int64_t q_stride[4], const int64_t k_stride[4],
+                          const int64_t v_stride[4], const int64_t bias_stride[4],
+                          const int64_t o_stride[4], float scale, int32_t causal,
+                          void* hip_stream);
+
+sdpa_status attn_fwd_compact_varlen_bias(
+    const void* q, const void* k, const void* v, const void* bias, void* o, float* lse,
+    sdpa_dtype dtype, int32_t B, int32_t H, int32_t total_q, int32_t total_k, int32_t head_dim,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, const int64_t q_stride[4],
+    const int64_t k_stride[4], const int64_t v_stride[4], const int64_t bias_stride[4],
+    const int64_t o_stride[4], float scale, int32_t causal, void* hip_stream);
+
+sdpa_status attn_fwd_padded_varlen_bias(
+    const void* q, const void* k, const void* v, const void* bias, void* o, float* lse,
+    sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q_max, int32_t seqlen_k_max,
+    int32_t head_dim, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    const int64_t q_stride[4], const int64_t k_stride[4], const int64_t v_stride[4],
+    const int64_t bias_stride[4], const int64_t o_stride[4], float scale, int32_t causal,
+    void* hip_stream);
+
+/*
  * Key-parallel ("split") dense forward for few query rows against many keys.
  * Triton issue #2267 (opening comment) counts differing numbers of queries
  * and keys among the use cases; with, say, 512 queries against 8192 keys a

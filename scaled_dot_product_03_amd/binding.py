@@ -32,6 +32,9 @@ EXPORTED = (
     "attn_fwd",
     "attn_fwd_compact_varlen",
     "attn_fwd_padded_varlen",
+    "attn_fwd_bias",
+    "attn_fwd_compact_varlen_bias",
+    "attn_fwd_padded_varlen_bias",
     "attn_fwd_splitk",
     "sdpa_fwd_splitk_plan",
     "attn_bwd",
@@ -86,6 +89,17 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_padded_varlen.restype = ctypes.c_int
     lib.attn_fwd_padded_varlen.argtypes = (
         [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p] + common_tail)
+    bias_tail = [_stride, _stride, _stride, _stride, _stride, ctypes.c_float, _i32, _p]
+    lib.attn_fwd_bias.restype = ctypes.c_int
+    lib.attn_fwd_bias.argtypes = (
+        [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32] + bias_tail)
+    lib.attn_fwd_compact_varlen_bias.restype = ctypes.c_int
+    lib.attn_fwd_compact_varlen_bias.argtypes = (
+        [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32,
+         _i32] + bias_tail)
+    lib.attn_fwd_padded_varlen_bias.restype = ctypes.c_int
+    lib.attn_fwd_padded_varlen_bias.argtypes = (
+        [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _p, _p] + bias_tail)
     lib.attn_fwd_splitk.restype = ctypes.c_int
     lib.attn_fwd_splitk.argtypes = (
         [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _stride, _stride, _stride,
@@ -162,8 +176,20 @@ def check_cu_seqlens_host(cu, total: int, max_len: int) -> None:
     _check(load_library().sdpa_check_cu_seqlens_host(ptr, arr.size - 1, int(total), int(max_len)))
 
 
-def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
-    """Dense forward.  q: (B,H,Sq,D), k/v: (B,H,Sk,D) -> (o, lse (B,H,Sq) fp32)."""
+def _bias_view(bias, q, shape):
+    """The bias broadcast (stride 0, no copy) to the rank-4 score view."""
+    if not bias.is_cuda or bias.device != q.device:
+        raise ValueError("bias must be on the device of q")
+    if bias.dtype != q.dtype:
+        raise ValueError("bias must have the dtype of q")
+    return bias.expand(*shape)
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, bias=None):
+    """Dense forward.  q: (B,H,Sq,D), k/v: (B,H,Sk,D) -> (o, lse (B,H,Sq) fp32).
+
+    ``bias`` (optional, q's dtype, broadcastable to (B,H,Sq,Sk)) is added to
+    the scaled scores."""
     lib = load_library()
     _require_gpu(q, k, v)
     B, H, Sq, D = q.shape
@@ -174,11 +200,19 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
         raise ValueError("q, k and v must share one dtype")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(lib.attn_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-        _dtype_code(q), B, H, Sq, Sk, D,
-        _strides(q), _strides(k), _strides(v), _strides(o),
-        _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    if bias is None:
+        _check(lib.attn_fwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            _dtype_code(q), B, H, Sq, Sk, D,
+            _strides(q), _strides(k), _strides(v), _strides(o),
+            _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    else:
+        bv = _bias_view(bias, q, (B, H, Sq, Sk))
+        _check(lib.attn_fwd_bias(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), bv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            _dtype_code(q), B, H, Sq, Sk, D,
+            _strides(q), _strides(k), _strides(v), _strides(bv), _strides(o),
+            _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
     return o, lse
 
 
@@ -290,13 +324,14 @@ def _grads_like(q, k, v, dq, dk, dv):
 
 def attn_fwd_compact_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None,
                             max_seqlen_k=None, scale=None, causal=False, out=None, lse=None,
-                            check=True):
+                            check=True, bias=None):
     """Compact varlen forward over packed (T, H, D) tokens.
 
     cu_seqlens may be host arrays (checked with the library's host check,
     then copied to the device) or device int32 tensors (used as given).
     Returns (o (Tq,H,D), lse (1,H,Tq) fp32).  Max lengths default to the
-    largest length in host cu_seqlens.
+    largest length in host cu_seqlens.  ``bias`` (optional) is broadcastable
+    to (1, H, Tq, Tk); sequence z reads its block of it.
     """
     lib = load_library()
     _require_gpu(q, k, v)
@@ -318,21 +353,30 @@ def attn_fwd_compact_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=No
     lse = torch.empty((1, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
     # (T, H, D) token memory seen as the rank-4 view (1, H, T, D).
     qv, kv, vv, ov = (t.transpose(0, 1).unsqueeze(0) for t in (q, k, v, o))
-    _check(lib.attn_fwd_compact_varlen(
-        qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
-        _dtype_code(q), 1, H, Tq, Tk, D, cu_q.data_ptr(), cu_k.data_ptr(), num_seqs, max_q, max_k,
-        _strides(qv), _strides(kv), _strides(vv), _strides(ov),
-        _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    if bias is None:
+        _check(lib.attn_fwd_compact_varlen(
+            qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
+            _dtype_code(q), 1, H, Tq, Tk, D, cu_q.data_ptr(), cu_k.data_ptr(), num_seqs, max_q,
+            max_k, _strides(qv), _strides(kv), _strides(vv), _strides(ov),
+            _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    else:
+        bv = _bias_view(bias, q, (1, H, Tq, Tk))
+        _check(lib.attn_fwd_compact_varlen_bias(
+            qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), bv.data_ptr(), ov.data_ptr(),
+            lse.data_ptr(), _dtype_code(q), 1, H, Tq, Tk, D, cu_q.data_ptr(), cu_k.data_ptr(),
+            num_seqs, max_q, max_k, _strides(qv), _strides(kv), _strides(vv), _strides(bv),
+            _strides(ov), _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
     return o, lse
 
 
 def attn_fwd_padded_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False,
-                           out=None, lse=None, check=True):
+                           out=None, lse=None, check=True, bias=None):
     """Padded varlen forward.  q: (B,H,Sq_max,D), k/v: (B,H,Sk_max,D).
 
     Batch b's true lengths are the differences of cu_seqlens.  Rows past a
     true length are left as allocated (uninitialised unless ``out``/``lse``
-    are given).  Returns (o, lse (B,H,Sq_max) fp32).
+    are given).  ``bias`` (optional) is broadcastable to
+    (B, H, Sq_max, Sk_max).  Returns (o, lse (B,H,Sq_max) fp32).
     """
     lib = load_library()
     _require_gpu(q, k, v)
@@ -348,11 +392,19 @@ def attn_fwd_padded_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, caus
         raise ValueError("padded varlen needs B + 1 cu_seqlens entries")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(lib.attn_fwd_padded_varlen(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-        _dtype_code(q), B, H, Sq, Sk, D, cu_q.data_ptr(), cu_k.data_ptr(),
-        _strides(q), _strides(k), _strides(v), _strides(o),
-        _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    if bias is None:
+        _check(lib.attn_fwd_padded_varlen(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            _dtype_code(q), B, H, Sq, Sk, D, cu_q.data_ptr(), cu_k.data_ptr(),
+            _strides(q), _strides(k), _strides(v), _strides(o),
+            _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
+    else:
+        bv = _bias_view(bias, q, (B, H, Sq, Sk))
+        _check(lib.attn_fwd_padded_varlen_bias(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), bv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            _dtype_code(q), B, H, Sq, Sk, D, cu_q.data_ptr(), cu_k.data_ptr(),
+            _strides(q), _strides(k), _strides(v), _strides(bv), _strides(o),
+            _scale(scale, D), int(bool(causal)), _stream_handle(q.device)))
     return o, lse
 
 

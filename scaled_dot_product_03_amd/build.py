@@ -3,7 +3,8 @@
     python -m scaled_dot_product_03_amd.build
 
 compiles the HIP kernels and the C-ABI layer into
-``scaled_dot_product_03_amd/libsdpa03.so``.  Every call recompiles.
+``scaled_dot_product_03_amd/libsdpa03.so``, one hipcc process per source
+file.  Every call recompiles.
 """
 
 from __future__ import annotations
@@ -11,6 +12,8 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -20,28 +23,26 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_bias.hip", "attn_bwd.hip", "api.cpp"]
 
 # Packed fp32 VALU instructions are kept out of the device code; hipcc's
 # host pass does not know the feature and says so, which is harmless.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def compile_command(out_path: str = LIB_PATH, extra=()) -> list:
+def object_command(source: str, out_path: str, extra=()) -> list:
+    """hipcc command that compiles one source of the library to an object."""
     return [
-        HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Wall", "-Wno-unused-function",
         *DEVICE_FLAGS,
         "-I", os.path.join(ROOT, "include"),
-        "-x", "hip",
-        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-x", "hip", "-c", os.path.join(CSRC, source),
         "-o", out_path, *extra,
     ]
 
 
-def build_library(verbose: bool = True) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,8 +52,21 @@ def build_library(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+
+
+def build_library(verbose: bool = True, out_path: str = LIB_PATH, extra=()) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link
+    ``out_path``; ``extra`` goes to every compile (e.g. -D overrides)."""
+    with tempfile.TemporaryDirectory(prefix="sdpa03_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+            for f in [pool.submit(_run, object_command(s, o, extra), verbose)
+                      for s, o in zip(SOURCES, objs)]:
+                f.result()
+        tmp = out_path + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
+        os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

@@ -124,8 +124,33 @@ sdpa_status dense_args(const void* q, const void* k, const void* v, void* o, flo
   a->num_heads = H;
   a->num_z = B;
   a->scale_log2 = scale * 1.4426950408889634f;
+  a->scale = scale;
   a->num_splits = 1;
   return SDPA_OK;
+}
+
+// The bias view (num_b, H, rows_q, rows_k), read-only: key stride 1, other
+// strides >= 0 (0 broadcasts) and multiples of 4 elements, base 16-byte
+// aligned, every offset within 64-bit addressing.
+sdpa_status check_bias(const void* bias, int64_t num_b, int64_t H, int64_t rows_q,
+                       int64_t rows_k, const int64_t* stride, int esize) {
+  if (bias == nullptr || stride == nullptr) return SDPA_ERR_NULL;
+  if (stride[3] != 1) return SDPA_ERR_STRIDE;
+  for (int i = 0; i < 3; ++i) {
+    if (stride[i] < 0) return SDPA_ERR_STRIDE;
+    if (stride[i] % 4 != 0) return SDPA_ERR_ALIGN;
+  }
+  if (reinterpret_cast<uintptr_t>(bias) % 16 != 0) return SDPA_ERR_ALIGN;
+  const View vb{bias, {num_b, H, rows_q, rows_k}, stride};
+  if (max_offset(vb) < 0 || max_offset(vb) > INT64_MAX / esize) return SDPA_ERR_STRIDE;
+  return SDPA_OK;
+}
+
+void set_bias(FwdArgs& a, const void* bias, const int64_t* stride) {
+  a.bias = bias;
+  a.bias_sb = stride[0];
+  a.bias_sh = stride[1];
+  a.bias_sq = stride[2];
 }
 
 // Key ranges of a split forward and the workspace they need.  The library
@@ -180,6 +205,113 @@ sdpa_status split_plan(int dtype, int32_t B, int32_t H, int32_t seqlen_q, int32_
   return SDPA_OK;
 }
 
+// Argument checks and kernel arguments of a compact varlen call.
+sdpa_status compact_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                         sdpa_dtype dtype, int32_t B, int32_t H, int32_t total_q, int32_t total_k,
+                         int32_t head_dim, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, const int64_t q_stride[4],
+                         const int64_t k_stride[4], const int64_t v_stride[4],
+                         const int64_t o_stride[4], float scale, FwdArgs* a, bool* empty) {
+  *empty = false;
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (B != 1) return SDPA_ERR_BATCH;
+  if (H < 0 || total_q < 0 || total_k < 0) return SDPA_ERR_SHAPE;
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > total_q ||
+      max_seqlen_k > total_k)
+    return SDPA_ERR_SEQLEN;
+  if (static_cast<int64_t>(H) * num_seqs * max_seqlen_q == 0) {
+    *empty = true;
+    return SDPA_OK;
+  }
+  if ((st = check_pointers(q, k, v, o, lse, total_k)) != SDPA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
+  const int es = elem_size(dtype);
+  const View vq{q, {1, H, total_q, head_dim}, q_stride};
+  const View vk{k, {1, H, total_k, head_dim}, k_stride};
+  const View vv{v, {1, H, total_k, head_dim}, v_stride};
+  const View vo{o, {1, H, total_q, head_dim}, o_stride};
+  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
+      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
+    return st;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
+    return SDPA_ERR_ALIGN;
+
+  *a = FwdArgs{};
+  a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
+  a->cu_q = cu_seqlens_q; a->cu_k = cu_seqlens_k;
+  set_strides(q_stride, a->q_sb, a->q_sh, a->q_ss);
+  set_strides(k_stride, a->k_sb, a->k_sh, a->k_ss);
+  set_strides(v_stride, a->v_sb, a->v_sh, a->v_ss);
+  set_strides(o_stride, a->o_sb, a->o_sh, a->o_ss);
+  a->lse_sh = total_q;
+  a->lse_sb = static_cast<int64_t>(H) * total_q;
+  a->seqlen_q = max_seqlen_q;
+  a->seqlen_k = max_seqlen_k;
+  a->total_q = total_q;
+  a->total_k = total_k;
+  a->num_heads = H;
+  a->num_z = num_seqs;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->scale = scale;
+  a->num_splits = 1;
+  return SDPA_OK;
+}
+
+// Argument checks and kernel arguments of a padded varlen call.
+sdpa_status padded_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                        sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q_max,
+                        int32_t seqlen_k_max, int32_t head_dim, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, const int64_t q_stride[4],
+                        const int64_t k_stride[4], const int64_t v_stride[4],
+                        const int64_t o_stride[4], float scale, FwdArgs* a, bool* empty) {
+  *empty = false;
+  sdpa_status st = check_common(dtype, head_dim, scale);
+  if (st != SDPA_OK) return st;
+  if (B < 0 || H < 0 || seqlen_q_max < 0 || seqlen_k_max < 0) return SDPA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H * seqlen_q_max == 0) {
+    *empty = true;
+    return SDPA_OK;
+  }
+  if ((st = check_pointers(q, k, v, o, lse, seqlen_k_max)) != SDPA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
+  const int es = elem_size(dtype);
+  const View vq{q, {B, H, seqlen_q_max, head_dim}, q_stride};
+  const View vk{k, {B, H, seqlen_k_max, head_dim}, k_stride};
+  const View vv{v, {B, H, seqlen_k_max, head_dim}, v_stride};
+  const View vo{o, {B, H, seqlen_q_max, head_dim}, o_stride};
+  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
+      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
+    return st;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
+    return SDPA_ERR_ALIGN;
+
+  *a = FwdArgs{};
+  a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
+  a->cu_q = cu_seqlens_q; a->cu_k = cu_seqlens_k;
+  set_strides(q_stride, a->q_sb, a->q_sh, a->q_ss);
+  set_strides(k_stride, a->k_sb, a->k_sh, a->k_ss);
+  set_strides(v_stride, a->v_sb, a->v_sh, a->v_ss);
+  set_strides(o_stride, a->o_sb, a->o_sh, a->o_ss);
+  a->lse_sh = seqlen_q_max;
+  a->lse_sb = static_cast<int64_t>(H) * seqlen_q_max;
+  a->seqlen_q = seqlen_q_max;
+  a->seqlen_k = seqlen_k_max;
+  a->total_q = seqlen_q_max;
+  a->total_k = seqlen_k_max;
+  a->num_heads = H;
+  a->num_z = B;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->scale = scale;
+  a->num_splits = 1;
+  return SDPA_OK;
+}
+
 sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, int mode,
                               int32_t causal, void* stream) {
   sdpa03::KernelConfig cfg;
@@ -189,7 +321,9 @@ sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, in
   if (grid > kMaxGrid) return SDPA_ERR_SHAPE;
   if (grid == 0) return SDPA_OK;
   a.m_tiles = static_cast<int32_t>(m_tiles);
-  const int err = sdpa03::launch_attn_fwd(a, dtype, head_dim, mode, causal != 0, stream);
+  const int err = a.bias != nullptr
+                      ? sdpa03::launch_attn_fwd_bias(a, dtype, head_dim, mode, causal != 0, stream)
+                      : sdpa03::launch_attn_fwd(a, dtype, head_dim, mode, causal != 0, stream);
   return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
 }
 
@@ -493,46 +627,13 @@ sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v,
                                     const int64_t k_stride[4], const int64_t v_stride[4],
                                     const int64_t o_stride[4], float scale, int32_t causal,
                                     void* hip_stream) {
-  sdpa_status st = check_common(dtype, head_dim, scale);
-  if (st != SDPA_OK) return st;
-  if (B != 1) return SDPA_ERR_BATCH;
-  if (H < 0 || total_q < 0 || total_k < 0) return SDPA_ERR_SHAPE;
-  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > total_q ||
-      max_seqlen_k > total_k)
-    return SDPA_ERR_SEQLEN;
-  if (static_cast<int64_t>(H) * num_seqs * max_seqlen_q == 0) return SDPA_OK;
-  if ((st = check_pointers(q, k, v, o, lse, total_k)) != SDPA_OK) return st;
-  if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
-  const int es = elem_size(dtype);
-  const View vq{q, {1, H, total_q, head_dim}, q_stride};
-  const View vk{k, {1, H, total_k, head_dim}, k_stride};
-  const View vv{v, {1, H, total_k, head_dim}, v_stride};
-  const View vo{o, {1, H, total_q, head_dim}, o_stride};
-  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
-      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
-    return st;
-  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
-  if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
-      reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
-    return SDPA_ERR_ALIGN;
-
-  FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
-  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
-  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
-  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
-  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
-  a.lse_sh = total_q;
-  a.lse_sb = static_cast<int64_t>(H) * total_q;
-  a.seqlen_q = max_seqlen_q;
-  a.seqlen_k = max_seqlen_k;
-  a.total_q = total_q;
-  a.total_k = total_k;
-  a.num_heads = H;
-  a.num_z = num_seqs;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.num_splits = 1;
+  FwdArgs a;
+  bool empty;
+  const sdpa_status st = compact_args(q, k, v, o, lse, dtype, B, H, total_q, total_k, head_dim,
+                                      cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
+                                      max_seqlen_k, q_stride, k_stride, v_stride, o_stride, scale,
+                                      &a, &empty);
+  if (st != SDPA_OK || empty) return st;
   return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_COMPACT, causal, hip_stream);
 }
 
@@ -544,42 +645,69 @@ sdpa_status attn_fwd_padded_varlen(const void* q, const void* k, const void* v, 
                                    const int64_t k_stride[4], const int64_t v_stride[4],
                                    const int64_t o_stride[4], float scale, int32_t causal,
                                    void* hip_stream) {
-  sdpa_status st = check_common(dtype, head_dim, scale);
-  if (st != SDPA_OK) return st;
-  if (B < 0 || H < 0 || seqlen_q_max < 0 || seqlen_k_max < 0) return SDPA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H * seqlen_q_max == 0) return SDPA_OK;
-  if ((st = check_pointers(q, k, v, o, lse, seqlen_k_max)) != SDPA_OK) return st;
-  if (!cu_seqlens_q || !cu_seqlens_k) return SDPA_ERR_NULL;
-  const int es = elem_size(dtype);
-  const View vq{q, {B, H, seqlen_q_max, head_dim}, q_stride};
-  const View vk{k, {B, H, seqlen_k_max, head_dim}, k_stride};
-  const View vv{v, {B, H, seqlen_k_max, head_dim}, v_stride};
-  const View vo{o, {B, H, seqlen_q_max, head_dim}, o_stride};
-  if ((st = check_view(vq, es, false)) != SDPA_OK || (st = check_view(vk, es, true)) != SDPA_OK ||
-      (st = check_view(vv, es, true)) != SDPA_OK || (st = check_view(vo, es, false)) != SDPA_OK)
-    return st;
-  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return SDPA_ERR_ALIGN;
-  if (reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0 ||
-      reinterpret_cast<uintptr_t>(cu_seqlens_k) % 4 != 0)
-    return SDPA_ERR_ALIGN;
+  FwdArgs a;
+  bool empty;
+  const sdpa_status st = padded_args(q, k, v, o, lse, dtype, B, H, seqlen_q_max, seqlen_k_max,
+                                     head_dim, cu_seqlens_q, cu_seqlens_k, q_stride, k_stride,
+                                     v_stride, o_stride, scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
+  return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_PADDED, causal, hip_stream);
+}
 
-  FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
-  set_strides(q_stride, a.q_sb, a.q_sh, a.q_ss);
-  set_strides(k_stride, a.k_sb, a.k_sh, a.k_ss);
-  set_strides(v_stride, a.v_sb, a.v_sh, a.v_ss);
-  set_strides(o_stride, a.o_sb, a.o_sh, a.o_ss);
-  a.lse_sh = seqlen_q_max;
-  a.lse_sb = static_cast<int64_t>(H) * seqlen_q_max;
-  a.seqlen_q = seqlen_q_max;
-  a.seqlen_k = seqlen_k_max;
-  a.total_q = seqlen_q_max;
-  a.total_k = seqlen_k_max;
-  a.num_heads = H;
-  a.num_z = B;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.num_splits = 1;
+sdpa_status attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                          void* o, float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                          int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                          const int64_t q_stride[4], const int64_t k_stride[4],
+                          const int64_t v_stride[4], const int64_t bias_stride[4],
+                          const int64_t o_stride[4], float scale, int32_t causal,
+                          void* hip_stream) {
+  FwdArgs a;
+  bool empty;
+  sdpa_status st = dense_args(q, k, v, o, lse, dtype, B, H, seqlen_q, seqlen_k, head_dim,
+                              q_stride, k_stride, v_stride, o_stride, scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
+  if ((st = check_bias(bias, B, H, seqlen_q, seqlen_k, bias_stride, elem_size(dtype))) != SDPA_OK)
+    return st;
+  set_bias(a, bias, bias_stride);
+  return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_DENSE, causal, hip_stream);
+}
+
+sdpa_status attn_fwd_compact_varlen_bias(
+    const void* q, const void* k, const void* v, const void* bias, void* o, float* lse,
+    sdpa_dtype dtype, int32_t B, int32_t H, int32_t total_q, int32_t total_k, int32_t head_dim,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, const int64_t q_stride[4],
+    const int64_t k_stride[4], const int64_t v_stride[4], const int64_t bias_stride[4],
+    const int64_t o_stride[4], float scale, int32_t causal, void* hip_stream) {
+  FwdArgs a;
+  bool empty;
+  sdpa_status st = compact_args(q, k, v, o, lse, dtype, B, H, total_q, total_k, head_dim,
+                                cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k,
+                                q_stride, k_stride, v_stride, o_stride, scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
+  if ((st = check_bias(bias, 1, H, total_q, total_k, bias_stride, elem_size(dtype))) != SDPA_OK)
+    return st;
+  set_bias(a, bias, bias_stride);
+  return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_COMPACT, causal, hip_stream);
+}
+
+sdpa_status attn_fwd_padded_varlen_bias(
+    const void* q, const void* k, const void* v, const void* bias, void* o, float* lse,
+    sdpa_dtype dtype, int32_t B, int32_t H, int32_t seqlen_q_max, int32_t seqlen_k_max,
+    int32_t head_dim, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    const int64_t q_stride[4], const int64_t k_stride[4], const int64_t v_stride[4],
+    const int64_t bias_stride[4], const int64_t o_stride[4], float scale, int32_t causal,
+    void* hip_stream) {
+  FwdArgs a;
+  bool empty;
+  sdpa_status st = padded_args(q, k, v, o, lse, dtype, B, H, seqlen_q_max, seqlen_k_max, head_dim,
+                               cu_seqlens_q, cu_seqlens_k, q_stride, k_stride, v_stride, o_stride,
+                               scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
+  if ((st = check_bias(bias, B, H, seqlen_q_max, seqlen_k_max, bias_stride, elem_size(dtype))) !=
+      SDPA_OK)
+    return st;
+  set_bias(a, bias, bias_stride);
   return finish_and_launch(a, dtype, head_dim, sdpa03::MODE_PADDED, causal, hip_stream);
 }
 

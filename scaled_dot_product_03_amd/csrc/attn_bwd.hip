@@ -37,8 +37,6 @@
 namespace sdpa03 {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // LDS row stride (bytes) of a tile that is read both as 16-row MFMA operands
 // (ds_read_b128: the 16 rows of one pass must start in distinct 16-byte bank
 // groups of gfx950's 256-byte bank cycle) and transposed (ds_read_b64_tr_b16:

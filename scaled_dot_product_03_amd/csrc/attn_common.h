@@ -18,6 +18,7 @@ using lds_void_ptr = __attribute__((address_space(3))) void*;
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
 // Fourth dword of a raw buffer descriptor on gfx9 (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
 

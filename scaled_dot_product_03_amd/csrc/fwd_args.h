@@ -31,6 +31,11 @@ struct FwdArgs {
   int32_t num_z;      // batches (dense, padded) or sequences (compact)
   int32_t m_tiles;    // ceil(seqlen_q / block_m)
   float scale_log2;   // scale * log2(e): scores go straight into exp2
+  // Additive bias (nullptr: none), same element type as q, indexed like the
+  // scores of the rank-4 view: (b, h, row, key) with key stride 1.
+  const void* bias;
+  int64_t bias_sb, bias_sh, bias_sq;
+  float scale;        // the bias is added to scale * q.k before the softmax
   // Key-parallel (split) dense forward only: split s of a query tile covers
   // key tiles [s * split_tiles, (s + 1) * split_tiles) and writes its
   // normalised fp32 partial output and its logsumexp to the workspace.
@@ -73,6 +78,10 @@ bool split_kernel_config(int dtype, int head_dim, KernelConfig* cfg);
 // code of the launch (0 on success).  Arguments are assumed validated.
 int launch_attn_fwd(const FwdArgs& args, int dtype, int head_dim, int mode, bool causal,
                     void* stream);
+
+// The same with the additive bias of args.bias (non-null).
+int launch_attn_fwd_bias(const FwdArgs& args, int dtype, int head_dim, int mode, bool causal,
+                         void* stream);
 
 // Split dense forward: the partial kernel (grid m_tiles * heads * batches *
 // splits), then the merge kernel, both on `stream`.

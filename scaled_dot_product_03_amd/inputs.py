@@ -82,6 +82,20 @@ def dense_inputs(B, H, Sq, Sk, D, dtype, seed, scale=None, causal_modes=(False, 
     )
 
 
+def bias_tensor(shape, dtype, seed, neg_inf_frac=0.0, key_pad=8):
+    """A seeded standard-normal additive bias of ``shape`` (rank 4), stored
+    with its last dimension padded to a multiple of ``key_pad`` elements (the
+    library needs row strides in multiples of 4) and returned as the
+    unpadded view.  ``neg_inf_frac`` of the entries become -inf."""
+    rng = np.random.default_rng(seed)
+    *lead, sk = shape
+    padded = (sk + key_pad - 1) // key_pad * key_pad if sk else key_pad
+    x = rng.standard_normal((*lead, padded), dtype=np.float32)
+    if neg_inf_frac > 0:
+        x[rng.random(x.shape) < neg_inf_frac] = -np.inf
+    return torch.from_numpy(x).to(DTYPES[dtype])[..., :sk]
+
+
 def compact_inputs(n_seqs, H, D, dtype, seed, len_lo, len_hi, same_kv_lengths=True,
                    lengths_q=None, lengths_k=None, extra_tokens=0, causal_modes=(True,)):
     """Packed THD tokens: Q (Tq,H,D), K/V (Tk,H,D) plus int32 cu_seqlens.

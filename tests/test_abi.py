@@ -280,3 +280,40 @@ def test_bwd_empty_problems_are_ok_without_launch():
     assert _bwd("compact", num_seqs=0, **none) == 0
     assert _bwd("compact", max_q=0, max_k=0, **none) == 0
     assert _bwd("padded", B=0, **none) == 0
+
+
+# --- forward with a bias: validation ----------------------------------------
+
+def _fwd_bias(fn="dense", **kw):
+    lib = binding.load_library()
+    a = dict(q=DUMMY, k=DUMMY, v=DUMMY, bias=DUMMY, o=DUMMY, lse=DUMMY, dtype=2, B=1, H=2, S=64,
+             D=64, bs=_st(2 * 64 * 64, 64 * 64, 64, 1), scale=0.125, cu=DUMMY)
+    a.update(kw)
+    st = _st(64 * 2 * 64, 64 * 64, 64, 1)
+    ptrs = [a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"]]
+    tail = [st, st, st, a["bs"], st, a["scale"], 0, None]
+    if fn == "dense":
+        return lib.attn_fwd_bias(*ptrs, a["dtype"], a["B"], a["H"], a["S"], a["S"], a["D"], *tail)
+    if fn == "compact":
+        return lib.attn_fwd_compact_varlen_bias(*ptrs, a["dtype"], a["B"], a["H"], a["S"], a["S"],
+                                                a["D"], a["cu"], a["cu"], 3, 20, 20, *tail)
+    return lib.attn_fwd_padded_varlen_bias(*ptrs, a["dtype"], a["B"], a["H"], a["S"], a["S"],
+                                           a["D"], a["cu"], a["cu"], *tail)
+
+
+@no_gpu
+@pytest.mark.parametrize("fn", ["dense", "compact", "padded"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(bias=None), 1), (dict(bs=None), 1), (dict(bs=_st(2 * 64 * 64, 64 * 64, 64, 2)), 5),
+    (dict(bs=_st(2 * 64 * 64, -64 * 64, 64, 1)), 5), (dict(bs=_st(2 * 64 * 64, 64 * 64, 66, 1)), 6),
+    (dict(bs=_st(2 * 64 * 64, 64 * 64 + 2, 64, 1)), 6), (dict(bias=DUMMY + 8), 6),
+    (dict(bs=_st(2 ** 62, 2 ** 62, 2 ** 40, 1), B=1, H=2), 5),
+    (dict(q=None), 1), (dict(D=48), 3), (dict(dtype=4), 2),
+])
+def test_fwd_bias_validation(fn, kw, status):
+    assert _fwd_bias(fn, **kw) == status
+
+
+@no_gpu
+def test_fwd_bias_empty_problem_is_ok_without_launch():
+    assert _fwd_bias("dense", q=None, k=None, v=None, o=None, lse=None, bias=None, S=0) == 0
