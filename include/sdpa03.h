@@ -367,14 +367,27 @@ sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t tot
                                        int32_t max_len);
 
 /*
- * The compiled-in kernel choice for a problem class: query rows per
- * workgroup (block_m), keys per tile (block_n) and wavefronts per
- * workgroup.  mode: 0 dense, 1 compact varlen, 2 padded varlen.  Any output
- * pointer may be NULL.  Returns SDPA_ERR_DTYPE / SDPA_ERR_HEAD_DIM for
- * unsupported classes.
+ * The compiled-in kernel choice of the forward (attn_fwd and the varlen
+ * calls without a bias) for a problem: query rows per workgroup (block_m),
+ * keys per tile (block_n) and wavefronts per workgroup.  The dispatch key
+ * is the dtype, head_dim and the sequence extents, as in the tuning
+ * database of AOTriton issue #12 (the maintainer's replies: an
+ * ahead-of-time autotune probing sequence lengths, head dim and dtype that
+ * guides which kernel serves an input): seqlen_q and seqlen_k are the dense
+ * lengths, the varlen calls'
+ * max_seqlen_q / max_seqlen_k, or the padded calls' seqlen_*_max, in three
+ * query buckets (<= 128, <= 512, longer) and two key buckets (<= 512,
+ * longer).  causal and mode are accepted for a finer key later and do not
+ * change the choice today (mode: 0 dense, 1 compact, 2 padded).
+ * single_group != 0 asks for the shape of the split forward and of the
+ * forward with a bias, which never use the two-group (ping-pong) schedule.
+ * Any output pointer may be NULL.  Returns SDPA_ERR_DTYPE /
+ * SDPA_ERR_HEAD_DIM for unsupported classes, SDPA_ERR_SHAPE for a bad mode
+ * or negative length.
  */
 sdpa_status sdpa_kernel_config(sdpa_dtype dtype, int32_t head_dim, int32_t causal,
-                               int32_t mode, int32_t* block_m, int32_t* block_n,
+                               int32_t mode, int32_t seqlen_q, int32_t seqlen_k,
+                               int32_t single_group, int32_t* block_m, int32_t* block_n,
                                int32_t* waves);
 
 #ifdef __cplusplus

@@ -127,7 +127,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sdpa_check_cu_seqlens_host.restype = ctypes.c_int
     lib.sdpa_check_cu_seqlens_host.argtypes = [_i32p, _i32, _i32, _i32]
     lib.sdpa_kernel_config.restype = ctypes.c_int
-    lib.sdpa_kernel_config.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32p, _i32p, _i32p]
+    lib.sdpa_kernel_config.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32, _i32p,
+                                       _i32p, _i32p]
     _lib = lib
     return lib
 
@@ -160,12 +161,16 @@ def _require_gpu(*ts):
             raise ValueError("inputs must be ROCm device tensors")
 
 
-def kernel_config(dtype: torch.dtype, head_dim: int, causal: bool = False, mode: int = 0):
-    """(block_m, block_n, waves) of the compiled kernel for a problem class."""
+def kernel_config(dtype: torch.dtype, head_dim: int, seqlen_q: int, seqlen_k: int,
+                  causal: bool = False, mode: int = 0, single_group: bool = False):
+    """(block_m, block_n, waves) of the compiled forward kernel for these
+    sizes (varlen: the longest sequence's lengths); single_group for the
+    split forward and the forward with a bias."""
     lib = load_library()
     bm, bn, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib.sdpa_kernel_config(_DTYPE_CODES.get(dtype, _BAD_DTYPE), head_dim, int(causal), mode,
-                                  ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(w)))
+                                  seqlen_q, seqlen_k, int(bool(single_group)), ctypes.byref(bm),
+                                  ctypes.byref(bn), ctypes.byref(w)))
     return bm.value, bn.value, w.value
 
 

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_fwd_bias.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_fwd_f32.hip", "attn_bwd.hip",
+           "api.cpp"]
 
 # Packed fp32 VALU instructions are kept out of the device code; hipcc's
 # host pass does not know the feature and says so, which is harmless.

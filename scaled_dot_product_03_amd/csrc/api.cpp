@@ -176,7 +176,8 @@ sdpa_status split_plan(int dtype, int32_t B, int32_t H, int32_t seqlen_q, int32_
   if (head_dim != 64 && head_dim != 128) return SDPA_ERR_HEAD_DIM;
   if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
   sdpa03::KernelConfig cfg;
-  if (!sdpa03::split_kernel_config(dtype, head_dim, &cfg)) return SDPA_ERR_HEAD_DIM;
+  if (!sdpa03::kernel_config(dtype, head_dim, seqlen_q, seqlen_k, true, &cfg))
+    return SDPA_ERR_HEAD_DIM;
   const int64_t key_tiles = (static_cast<int64_t>(seqlen_k) + cfg.block_n - 1) / cfg.block_n;
   const int64_t m_tiles = (static_cast<int64_t>(seqlen_q) + cfg.block_m - 1) / cfg.block_m;
   const int64_t base = m_tiles * H * B;
@@ -315,7 +316,8 @@ sdpa_status padded_args(const void* q, const void* k, const void* v, void* o, fl
 sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, int mode,
                               int32_t causal, void* stream) {
   sdpa03::KernelConfig cfg;
-  if (!sdpa03::kernel_config(dtype, head_dim, causal != 0, mode, &cfg)) return SDPA_ERR_HEAD_DIM;
+  if (!sdpa03::kernel_config(dtype, head_dim, a.seqlen_q, a.seqlen_k, a.bias != nullptr, &cfg))
+    return SDPA_ERR_HEAD_DIM;
   const int64_t m_tiles = (static_cast<int64_t>(a.seqlen_q) + cfg.block_m - 1) / cfg.block_m;
   const int64_t grid = m_tiles * a.num_heads * static_cast<int64_t>(a.num_z);
   if (grid > kMaxGrid) return SDPA_ERR_SHAPE;
@@ -541,11 +543,15 @@ sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t tot
 }
 
 sdpa_status sdpa_kernel_config(sdpa_dtype dtype, int32_t head_dim, int32_t causal, int32_t mode,
+                               int32_t seqlen_q, int32_t seqlen_k, int32_t single_group,
                                int32_t* block_m, int32_t* block_n, int32_t* waves) {
   if (!dtype_ok(dtype)) return SDPA_ERR_DTYPE;
   if (mode < 0 || mode > 2) return SDPA_ERR_SHAPE;
+  if (seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
+  (void)causal;
   sdpa03::KernelConfig cfg;
-  if (!sdpa03::kernel_config(dtype, head_dim, causal != 0, mode, &cfg)) return SDPA_ERR_HEAD_DIM;
+  if (!sdpa03::kernel_config(dtype, head_dim, seqlen_q, seqlen_k, single_group != 0, &cfg))
+    return SDPA_ERR_HEAD_DIM;
   if (block_m) *block_m = cfg.block_m;
   if (block_n) *block_n = cfg.block_n;
   if (waves) *waves = cfg.waves;

@@ -1,34 +1,25 @@
-// Launchers of the plain and split flash-attention forward (the kernels are
-// in attn_fwd_kernels.h) and the compiled-in kernel choice.
+// Entry of the flash-attention forward launches (plain, with a bias, split;
+// the kernels are in attn_fwd_kernels.h, the per-type launches in
+// attn_fwd_{bf16,f16,f32}.hip) and the compiled-in kernel choice.
 
 #include "attn_fwd_kernels.h"
 
 namespace sdpa03 {
 
-bool kernel_config(int dtype, int head_dim, bool causal, int mode, KernelConfig* cfg) {
-  (void)causal;
-  (void)mode;
+bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool single_group,
+                   KernelConfig* cfg) {
   if (head_dim != 64 && head_dim != 128) return false;
+  const int b = seq_bucket(seqlen_q, seqlen_k);
+  auto pick = [&](auto tag) {
+    using T = decltype(tag);
+    if (head_dim == 64) return single_group ? entry_for<T, 64, true>(b) : entry_for<T, 64, false>(b);
+    return single_group ? entry_for<T, 128, true>(b) : entry_for<T, 128, false>(b);
+  };
   TableEntry e;
   switch (dtype) {
-    case DT_F32: e = head_dim == 64 ? table_entry<float, 64>() : table_entry<float, 128>(); break;
-    case DT_F16: e = head_dim == 64 ? table_entry<_Float16, 64>() : table_entry<_Float16, 128>(); break;
-    case DT_BF16: e = head_dim == 64 ? table_entry<__bf16, 64>() : table_entry<__bf16, 128>(); break;
-    default: return false;
-  }
-  cfg->block_m = e.waves * 32;
-  cfg->block_n = e.block_n;
-  cfg->waves = e.waves;
-  return true;
-}
-
-bool split_kernel_config(int dtype, int head_dim, KernelConfig* cfg) {
-  if (head_dim != 64 && head_dim != 128) return false;
-  TableEntry e;
-  switch (dtype) {
-    case DT_F32: e = head_dim == 64 ? single_group_entry<float, 64>() : single_group_entry<float, 128>(); break;
-    case DT_F16: e = head_dim == 64 ? single_group_entry<_Float16, 64>() : single_group_entry<_Float16, 128>(); break;
-    case DT_BF16: e = head_dim == 64 ? single_group_entry<__bf16, 64>() : single_group_entry<__bf16, 128>(); break;
+    case DT_F32: e = pick(float{}); break;
+    case DT_F16: e = pick(_Float16{}); break;
+    case DT_BF16: e = pick(__bf16{}); break;
     default: return false;
   }
   cfg->block_m = e.waves * 32;
@@ -57,9 +48,19 @@ int launch_attn_fwd_split(const FwdArgs& a, const MergeArgs& mg, int dtype, int 
 int launch_attn_fwd(const FwdArgs& a, int dtype, int head_dim, int mode, bool causal, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
-    case DT_F32: return launch_dim<float, false>(a, head_dim, mode, causal, s);
-    case DT_F16: return launch_dim<_Float16, false>(a, head_dim, mode, causal, s);
-    default: return launch_dim<__bf16, false>(a, head_dim, mode, causal, s);
+    case DT_F32: return launch_fwd_dtype<float, false>(a, head_dim, mode, causal, s);
+    case DT_F16: return launch_fwd_dtype<_Float16, false>(a, head_dim, mode, causal, s);
+    default: return launch_fwd_dtype<__bf16, false>(a, head_dim, mode, causal, s);
+  }
+}
+
+int launch_attn_fwd_bias(const FwdArgs& a, int dtype, int head_dim, int mode, bool causal,
+                         void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case DT_F32: return launch_fwd_dtype<float, true>(a, head_dim, mode, causal, s);
+    case DT_F16: return launch_fwd_dtype<_Float16, true>(a, head_dim, mode, causal, s);
+    default: return launch_fwd_dtype<__bf16, true>(a, head_dim, mode, causal, s);
   }
 }
 

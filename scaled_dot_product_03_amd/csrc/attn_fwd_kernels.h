@@ -1,6 +1,6 @@
 // Flash-attention forward kernels for CDNA4 (gfx950): the kernel templates
-// and their typed launchers, included by attn_fwd.hip (plain and split
-// forward) and attn_fwd_bias.hip (forward with a bias).
+// and their typed launchers, included by attn_fwd.hip (dispatch, split
+// forward) and attn_fwd_{bf16,f16,f32}.hip (one element type each).
 //
 // One workgroup computes block_m = 32 * waves query rows of one
 // (batch or sequence, head); each wavefront owns 32 rows.  The workgroup
@@ -1093,9 +1093,9 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeArgs a) {
 
 namespace {
 
-template <typename T, int D, int MODE, bool CAUSAL, bool BIAS>
-int launch_typed(const FwdArgs& a, hipStream_t stream) {
-  constexpr TableEntry e = BIAS ? single_group_entry<T, D>() : table_entry<T, D>();
+template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
+int launch_bucket(const FwdArgs& a, hipStream_t stream) {
+  constexpr TableEntry e = launch_entry<T, D, BUCKET, BIAS>();
   const uint32_t grid = static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z;
   if constexpr (e.pingpong != 0) {
     static_assert(e.waves == 8 && sizeof(T) == 2, "ping-pong: 8 waves, 16-bit inputs");
@@ -1109,9 +1109,23 @@ int launch_typed(const FwdArgs& a, hipStream_t stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-template <typename T, int D, bool CAUSAL>
-int launch_split_typed(const FwdArgs& a, const MergeArgs& mg, hipStream_t stream) {
-  constexpr TableEntry e = single_group_entry<T, D>();
+// The bucket of the dispatch key comes from the sequence extents the kernel
+// arguments carry (the longest sequence in the varlen layouts).
+template <typename T, int D, int MODE, bool CAUSAL, bool BIAS>
+int launch_typed(const FwdArgs& a, hipStream_t s) {
+  switch (seq_bucket(a.seqlen_q, a.seqlen_k)) {
+    case 0: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 0>(a, s);
+    case 1: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 1>(a, s);
+    case 2: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 2>(a, s);
+    case 3: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 3>(a, s);
+    case 4: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 4>(a, s);
+    default: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 5>(a, s);
+  }
+}
+
+template <typename T, int D, bool CAUSAL, int BUCKET>
+int launch_split_bucket(const FwdArgs& a, const MergeArgs& mg, hipStream_t stream) {
+  constexpr TableEntry e = launch_entry<T, D, BUCKET, true>();
   const uint32_t grid =
       static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z * static_cast<uint32_t>(a.num_splits);
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE_DENSE, CAUSAL, true, false>),
@@ -1122,6 +1136,31 @@ int launch_split_typed(const FwdArgs& a, const MergeArgs& mg, hipStream_t stream
   hipLaunchKernelGGL((attn_fwd_merge_kernel<T, D>), dim3(static_cast<uint32_t>((threads + 255) / 256)),
                      dim3(256), 0, stream, mg);
   return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, int D, bool CAUSAL>
+int launch_split_typed(const FwdArgs& a, const MergeArgs& mg, hipStream_t s) {
+  switch (seq_bucket(a.seqlen_q, a.seqlen_k)) {
+    case 0: return launch_split_bucket<T, D, CAUSAL, 0>(a, mg, s);
+    case 1: return launch_split_bucket<T, D, CAUSAL, 1>(a, mg, s);
+    case 2: return launch_split_bucket<T, D, CAUSAL, 2>(a, mg, s);
+    case 3: return launch_split_bucket<T, D, CAUSAL, 3>(a, mg, s);
+    case 4: return launch_split_bucket<T, D, CAUSAL, 4>(a, mg, s);
+    default: return launch_split_bucket<T, D, CAUSAL, 5>(a, mg, s);
+  }
+}
+
+// The table entry a launch will use, at run time (host side).
+template <typename T, int D, bool SINGLE_GROUP>
+TableEntry entry_for(int bucket) {
+  switch (bucket) {
+    case 0: return launch_entry<T, D, 0, SINGLE_GROUP>();
+    case 1: return launch_entry<T, D, 1, SINGLE_GROUP>();
+    case 2: return launch_entry<T, D, 2, SINGLE_GROUP>();
+    case 3: return launch_entry<T, D, 3, SINGLE_GROUP>();
+    case 4: return launch_entry<T, D, 4, SINGLE_GROUP>();
+    default: return launch_entry<T, D, 5, SINGLE_GROUP>();
+  }
 }
 
 template <typename T, int D, bool BIAS>
@@ -1139,12 +1178,23 @@ int launch_mode(const FwdArgs& a, int mode, bool causal, hipStream_t s) {
   }
 }
 
+}  // namespace
+
+// The launches of one element type, with or without a bias.  Each element
+// type's kernels are instantiated in a translation unit of their own
+// (attn_fwd_{bf16,f16,f32}.hip, explicit instantiations below) so that they
+// compile in parallel; other units only call these.
 template <typename T, bool BIAS>
-int launch_dim(const FwdArgs& a, int head_dim, int mode, bool causal, hipStream_t s) {
+int launch_fwd_dtype(const FwdArgs& a, int head_dim, int mode, bool causal, hipStream_t s) {
   return head_dim == 64 ? launch_mode<T, 64, BIAS>(a, mode, causal, s)
                         : launch_mode<T, 128, BIAS>(a, mode, causal, s);
 }
 
-}  // namespace
+extern template int launch_fwd_dtype<__bf16, false>(const FwdArgs&, int, int, bool, hipStream_t);
+extern template int launch_fwd_dtype<__bf16, true>(const FwdArgs&, int, int, bool, hipStream_t);
+extern template int launch_fwd_dtype<_Float16, false>(const FwdArgs&, int, int, bool, hipStream_t);
+extern template int launch_fwd_dtype<_Float16, true>(const FwdArgs&, int, int, bool, hipStream_t);
+extern template int launch_fwd_dtype<float, false>(const FwdArgs&, int, int, bool, hipStream_t);
+extern template int launch_fwd_dtype<float, true>(const FwdArgs&, int, int, bool, hipStream_t);
 
 }  // namespace sdpa03

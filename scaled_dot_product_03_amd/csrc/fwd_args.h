@@ -68,11 +68,11 @@ struct KernelConfig {
   int waves;
 };
 
-// Picks the compiled kernel for a problem class; false if unsupported.
-bool kernel_config(int dtype, int head_dim, bool causal, int mode, KernelConfig* cfg);
-
-// The kernel shape of the split dense forward for (dtype, head_dim).
-bool split_kernel_config(int dtype, int head_dim, KernelConfig* cfg);
+// The compiled kernel shape a launch uses for (dtype, head_dim) and the
+// sequence extents (seqlen_q and seqlen_k of FwdArgs); single_group for the
+// split forward and the forward with a bias.  False if unsupported.
+bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool single_group,
+                   KernelConfig* cfg);
 
 // Launches the forward on `stream` (a hipStream_t).  Returns the HIP error
 // code of the launch (0 on success).  Arguments are assumed validated.

@@ -1,16 +1,22 @@
 """Offline sweep that writes the compiled-in dispatch table.
 
-For every problem class (dtype, head_dim) a set of candidate kernel shapes
-(waves per workgroup, keys per tile, LDS stages, schedule: 0 single group,
-1 ping-pong of two wave groups) is compiled into its own
-build of libsdpa03.so.  A candidate counts only if its build has no register
+The dispatch key is (dtype, head_dim, sequence-length bucket): three query
+buckets (<= 128, <= 512, longer) by two key buckets (<= 512, longer), as
+AOTriton's tuning database probes sequence lengths, head dim and dtype
+(AOTriton issue #12, the maintainer's replies).  For every class (dtype,
+head_dim) a set of candidate kernel shapes (waves per workgroup, keys per
+tile, LDS stages, schedule: 0 single group, 1 ping-pong of two wave groups)
+is compiled into its own build of libsdpa03.so, the shape applied to every
+bucket of the class.  A candidate counts only if its build has no register
 spills, keeps two waves per SIMD, and then passes the GPU parity tests
-(tests/test_gpu_parity.py, run against that build); only then is it timed
-on the workloads of its class.  The fastest candidate per class goes into
+(tests/test_gpu_parity.py, run against that build): the same page warns that
+a kernel built with some configurations runs but gives wrong results.  Only
+then is it timed, on workloads of every bucket.  Per bucket, the fastest
+passing candidate on that bucket's workloads goes into
 csrc/dispatch_table.inc.  There is no tuning at run time.
 
-    python -m scaled_dot_product_03_amd.sweep build   # CPU: compile candidates
-    python -m scaled_dot_product_03_amd.sweep run     # GPU: parity, then timing
+    python -m scaled_dot_product_03_amd.sweep build [name ...]  # CPU: compile candidates
+    python -m scaled_dot_product_03_amd.sweep run [name ...]    # GPU: parity, then timing
     python -m scaled_dot_product_03_amd.sweep write   # rewrite dispatch_table.inc
 
 `run` writes _sweep/results.json; `write` reads it.
@@ -34,18 +40,39 @@ DTYPE_CODES = {"fp32": 0, "fp16": 1, "bf16": 2}
 
 # Candidate (waves, block_n, stages, pingpong) per class.
 CANDIDATES = {
-    ("bf16", 128): [(4, 64, 2, 0), (4, 32, 3, 0), (8, 64, 2, 0), (8, 64, 3, 0), (8, 32, 3, 0),
-                    (8, 64, 3, 1), (8, 128, 2, 1)],
-    ("fp16", 64): [(4, 64, 2, 0), (4, 64, 3, 0), (4, 32, 3, 0), (8, 64, 3, 0), (8, 64, 3, 1),
-                   (8, 128, 2, 1)],
+    ("bf16", 128): [(2, 32, 2, 0), (4, 32, 2, 0), (4, 64, 2, 0), (4, 32, 3, 0), (8, 64, 2, 0),
+                    (8, 64, 3, 0), (8, 32, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1)],
+    ("fp16", 64): [(2, 32, 2, 0), (4, 32, 2, 0), (4, 64, 2, 0), (4, 64, 3, 0), (4, 32, 3, 0),
+                   (8, 64, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1)],
 }
 
-# Timed workloads per class: (workload name from inputs.WORKLOADS, weight).
-TIMED = {
-    ("bf16", 128): ["dense_bf16_b4h16s2048d128", "thd_bf16_16seq_len1to4096_h16d128_causal",
-                    "padded_bf16_b8h32smax8192d128_len2048to8192_causal"],
-    ("fp16", 64): ["dense_fp16_b2h32sq512sk8192d64"],
-}
+BUCKETS = ["q<=128,k<=512", "q<=128,k>512", "q<=512,k<=512", "q<=512,k>512", "q>512,k<=512",
+           "q>512,k>512"]
+
+
+def _bucket_workloads(dtype, d):
+    """Timed workloads per bucket: (name, builder, kwargs).  The five named
+    workloads sit in their buckets; the others are seeded synthetic shapes of
+    the same recipe (inputs.py) that fill the short buckets."""
+    dense = lambda B, H, Sq, Sk, causal=(False, True): (
+        f"dense_{dtype}_b{B}h{H}sq{Sq}sk{Sk}d{d}", "dense",
+        dict(B=B, H=H, Sq=Sq, Sk=Sk, D=d, dtype=dtype, seed=11, causal_modes=causal))
+    thd = lambda n, hi: (f"thd_{dtype}_{n}seq_len1to{hi}_h16d{d}_causal", "compact",
+                         dict(n_seqs=n, H=16, D=d, dtype=dtype, seed=12, len_lo=1, len_hi=hi))
+    w = {
+        0: [dense(128, 16, 64, 64), dense(64, 16, 128, 128), thd(256, 128)],
+        1: [dense(16, 16, 128, 4096, (False,))],
+        2: [dense(16, 16, 256, 256), dense(8, 16, 512, 512), thd(128, 256), thd(64, 512)],
+        3: [dense(2, 32, 512, 8192, (False,))],
+        4: [dense(4, 16, 2048, 512, (False,))],
+        5: [dense(4, 16, 2048, 2048), thd(16, 4096)],
+    }
+    if (dtype, d) == ("bf16", 128):
+        w[5].append(("padded_bf16_b8h32smax8192d128_len2048to8192_causal", "named", {}))
+    return w
+
+
+TIMED = {cls: _bucket_workloads(*cls) for cls in CANDIDATES}
 
 
 def _cand4(cand):
@@ -67,7 +94,8 @@ def _resources(cls, cand):
     defs = _defines(cls, cand)
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-c",
            *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-x", "hip",
-           os.path.join(CSRC, "attn_fwd.hip"), "-o", os.devnull,
+           os.path.join(CSRC, f"attn_fwd_{ {'bf16': 'bf16', 'fp16': 'f16', 'fp32': 'f32'}[cls[0]] }.hip"),
+           "-o", os.devnull,
            "-Rpass-analysis=kernel-resource-usage", *defs]
     out = subprocess.run(cmd, capture_output=True, text=True).stderr
     dt_tag = {"bf16": "DF16b", "fp16": "DF16_", "fp32": "f"}[cls[0]]
@@ -102,7 +130,12 @@ def _defines(cls, cand):
 
 
 def build(only=None):
-    """Compile the candidates (those whose name contains one of `only`, if given)."""
+    """Compile the candidates (those whose name contains one of `only`, if given),
+    two at a time (each build runs one compiler per source file)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from .build import build_library
+
     os.makedirs(SWEEP_DIR, exist_ok=True)
     plan = []
     for cls, cands in CANDIDATES.items():
@@ -113,27 +146,30 @@ def build(only=None):
             ok = sp == 0 and occ >= 2
             print(f"{_name(cls, cand):28s} vgpr={vg} spill={sp} waves/simd={occ} "
                   f"{'build' if ok else 'skip'}", flush=True)
-            if not ok:
-                continue
-            cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-                   *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-x", "hip",
-                   *[os.path.join(CSRC, s) for s in SOURCES], "-o", _lib_path(cls, cand),
-                   *_defines(cls, cand)]
-            plan.append((cls, cand, subprocess.Popen(cmd, stdout=subprocess.DEVNULL,
-                                                     stderr=subprocess.PIPE, text=True)))
-    built = []
-    for cls, cand, proc in plan:
-        _, err = proc.communicate()
-        if proc.returncode != 0:
-            raise RuntimeError(f"build of {_name(cls, cand)} failed:\n{err}")
-        built.append({"dtype": cls[0], "head_dim": cls[1], "cand": list(cand)})
+            if ok:
+                plan.append((cls, cand))
+    with ThreadPoolExecutor(max_workers=2) as pool:
+        futs = [pool.submit(build_library, False, _lib_path(cls, cand), _defines(cls, cand))
+                for cls, cand in plan]
+        for f in futs:
+            f.result()
+    built = [{"dtype": cls[0], "head_dim": cls[1], "cand": list(cand)} for cls, cand in plan]
     with open(os.path.join(SWEEP_DIR, "built.json"), "w") as f:
         json.dump(built, f)
     print(f"built {len(built)} candidates", flush=True)
 
 
-def _time_workload(binding, torch, inputs, name, reps=10):
-    x = inputs.workload(name)
+def _make_inputs(inputs, kind, kwargs, name):
+    if kind == "named":
+        return inputs.workload(name)
+    if kind == "dense":
+        return inputs.dense_inputs(**kwargs)
+    return inputs.compact_inputs(**kwargs, causal_modes=(True,))
+
+
+def _time_workload(binding, torch, inputs, spec, reps=10):
+    name, kind, kwargs = spec
+    x = _make_inputs(inputs, kind, kwargs, name)
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     calls = []
@@ -151,8 +187,15 @@ def _time_workload(binding, torch, inputs, name, reps=10):
                                                             causal=True))
     out = []
     for call in calls:
-        for _ in range(3):
+        # Untimed sustained load first: the GPU raises its clocks only after
+        # ~0.1 s of it, and inputs were just generated on the host.
+        t_end = time.time() + 0.2
+        n = 0
+        while n < 3 or time.time() < t_end:
             call()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -166,25 +209,38 @@ def _time_workload(binding, torch, inputs, name, reps=10):
 
 
 def _timing_child(lib):
-    """Runs in a fresh process with SDPA03_LIBRARY set: prints JSON timings."""
+    """Runs in a fresh process with SDPA03_LIBRARY set: prints JSON timings
+    per bucket and workload."""
     import torch
     from . import binding, inputs
     binding.load_library(lib)
-    cls = json.loads(os.environ["SDPA03_SWEEP_CLASS"])
+    cls = tuple(json.loads(os.environ["SDPA03_SWEEP_CLASS"]))
     res = {}
-    for name in TIMED.get(tuple(cls), []):
-        res[name] = _time_workload(binding, torch, inputs, name)
+    for bucket, specs in TIMED.get(cls, {}).items():
+        for spec in specs:
+            res.setdefault(str(bucket), {})[spec[0]] = _time_workload(binding, torch, inputs, spec)
+            print(f"   timed bucket {bucket} {spec[0]}", file=sys.stderr, flush=True)
     print("SWEEP_TIMINGS " + json.dumps(res), flush=True)
 
 
-def run():
+def run(only=None):
+    """Parity, then timing, of the built candidates (those whose name contains
+    one of `only`, if given: their results replace earlier ones of the same
+    candidate in results.json, the others are kept)."""
     with open(os.path.join(SWEEP_DIR, "built.json")) as f:
         built = json.load(f)
     results = []
+    if only and os.path.exists(RESULTS):
+        with open(RESULTS) as f:
+            results = json.load(f)
     for b in built:
         cls, cand = (b["dtype"], b["head_dim"]), _cand4(b["cand"])
         if cls not in TIMED:
             continue
+        if only and not any(o in _name(cls, cand) for o in only):
+            continue
+        results = [r for r in results
+                   if not ((r["dtype"], r["head_dim"]) == cls and _cand4(r["cand"]) == cand)]
         lib = _lib_path(cls, cand)
         env = dict(os.environ, SDPA03_LIBRARY=lib, SDPA03_SWEEP_CLASS=json.dumps(list(cls)))
         print(f"== {_name(cls, cand)}: parity", flush=True)
@@ -215,36 +271,48 @@ def run():
             json.dump(results, f, indent=1)
 
 
+def _entry(cand):
+    w, n, st, pp = cand
+    return f"{{{w}, {n}, {st}, {pp}}}"
+
+
 def write(results_path=RESULTS, table_path=TABLE):
+    """Per (class, bucket): the passing candidate with the smallest sum of that
+    bucket's workload times.  Classes without timed workloads follow the timed
+    class of the same head_dim."""
     with open(results_path) as f:
         results = json.load(f)
-    best = {}
+    best = {}  # (dtype, d, bucket) -> (total ms, cand)
     for r in results:
         if not r["parity"] or not r["ms"]:
             continue
-        cls = (r["dtype"], r["head_dim"])
-        total = sum(sum(v) for v in r["ms"].values())
-        if cls not in best or total < best[cls][0]:
-            best[cls] = (total, _cand4(r["cand"]), r["ms"])
-    fallback = {("bf16", 128): (4, 64, 2, 0), ("fp16", 128): (4, 64, 2, 0),
-                ("bf16", 64): (4, 64, 3, 0), ("fp16", 64): (4, 64, 3, 0)}
-    pick = {cls: (best[cls][1] if cls in best else fallback[cls]) for cls in fallback}
-    # classes without their own timed workload follow the timed class of the same head_dim
-    if ("bf16", 128) in best:
-        pick[("fp16", 128)] = best[("bf16", 128)][1]
-    if ("fp16", 64) in best:
-        pick[("bf16", 64)] = best[("fp16", 64)][1]
-    lines = ["  // BEGIN TABLE (generated)"]
-    for cls, (total, cand, ms) in sorted(best.items()):
-        lines.append(f"  // {cls[0]} d{cls[1]}: (waves, block_n, stages, pingpong) = {cand}; "
+        for bucket, times in r["ms"].items():
+            key = (r["dtype"], r["head_dim"], int(bucket))
+            total = sum(sum(v) for v in times.values())
+            if key not in best or total < best[key][0]:
+                best[key] = (total, _cand4(r["cand"]))
+    default = {128: (4, 64, 2, 0), 64: (4, 64, 3, 0)}
+    timed_class = {128: "bf16", 64: "fp16"}
+    pick = {}
+    for dt in ("bf16", "fp16"):
+        for d in (128, 64):
+            for b in range(len(BUCKETS)):
+                src = (dt, d, b) if (dt, d, b) in best else (timed_class[d], d, b)
+                pick[(dt, d, b)] = best[src][1] if src in best else default[d]
+    lines = ["  // BEGIN TABLE (generated)",
+             "  // buckets: " + ", ".join(f"({b})" for b in BUCKETS)]
+    for (dt, d, b), (total, cand) in sorted(best.items()):
+        lines.append(f"  // {dt} d{d} bucket {b}: (waves, block_n, stages, pingpong) = {cand}; "
                      f"sum of timed workloads {total:.3f} ms")
     lines += ["  if constexpr (sizeof(T) == 4) {", "    return TableEntry{4, 32, 2, 0};"]
     for dt in ("bf16", "fp16"):
         for d in (128, 64):
-            w, n, st, pp = pick[(dt, d)]
-            cond = (f"dtype_code<T>() == {'DT_BF16' if dt == 'bf16' else 'DT_F16'} && D == {d}")
+            cond = f"dtype_code<T>() == {'DT_BF16' if dt == 'bf16' else 'DT_F16'} && D == {d}"
+            ents = [_entry(pick[(dt, d, b)]) for b in range(len(BUCKETS))]
             lines += [f"  }} else if constexpr ({cond}) {{",
-                      f"    return TableEntry{{{w}, {n}, {st}, {pp}}};"]
+                      "    constexpr TableEntry e[kSeqBuckets] = {" + ", ".join(ents[:3]) + ",",
+                      "                                           " + ", ".join(ents[3:]) + "};",
+                      "    return e[BUCKET];"]
     lines += ["  } else {", "    return TableEntry{4, 64, 2, 0};", "  }", "  // END TABLE"]
     text = open(table_path).read()
     text = re.sub(r"  // BEGIN TABLE \(generated\).*  // END TABLE", "\n".join(lines), text,
@@ -258,5 +326,7 @@ def write(results_path=RESULTS, table_path=TABLE):
 if __name__ == "__main__":
     if sys.argv[1] == "build":
         build(sys.argv[2:] or None)
+    elif sys.argv[1] == "run":
+        run(sys.argv[2:] or None)
     else:
-        {"run": run, "write": write}[sys.argv[1]]()
+        write()

@@ -60,14 +60,32 @@ def test_status_strings():
 def test_kernel_config_table():
     for dt in (torch.float32, torch.float16, torch.bfloat16):
         for d in (64, 128):
-            bm, bn, w = binding.kernel_config(dt, d)
-            assert bm == 32 * w and bn % 32 == 0 and bm > 0
+            for sq, sk in [(1, 1), (128, 512), (129, 513), (512, 8192), (513, 100), (8192, 8192)]:
+                for sg in (False, True):
+                    bm, bn, w = binding.kernel_config(dt, d, sq, sk, single_group=sg)
+                    assert bm == 32 * w and bn % 32 == 0 and bm > 0
+                    if sg:  # the split and bias kernels are single-group shapes
+                        assert w in (2, 4, 8)
     with pytest.raises(binding.SdpaError) as e:
-        binding.kernel_config(torch.float16, 96)
+        binding.kernel_config(torch.float16, 96, 64, 64)
     assert e.value.status == 3
     with pytest.raises(binding.SdpaError) as e:
-        binding.kernel_config(torch.float64, 64)
+        binding.kernel_config(torch.float64, 64, 64, 64)
     assert e.value.status == 2
+    with pytest.raises(binding.SdpaError) as e:
+        binding.kernel_config(torch.float16, 64, -1, 64)
+    assert e.value.status == 4
+
+
+def test_kernel_config_bucket_edges():
+    """The choice can change only at the bucket edges of the dispatch key
+    (query extent 128 / 512, key extent 512)."""
+    for dt in (torch.float16, torch.bfloat16):
+        for d in (64, 128):
+            cfg = lambda sq, sk: binding.kernel_config(dt, d, sq, sk)
+            for lo, hi in [(1, 128), (129, 512), (513, 1 << 20)]:
+                for klo, khi in [(1, 512), (513, 1 << 20)]:
+                    assert cfg(lo, klo) == cfg(hi, khi) == cfg(lo, khi) == cfg(hi, klo)
 
 
 def test_host_cu_seqlens_check():
@@ -164,9 +182,9 @@ def test_splitk_plan():
     assert used == 2
     assert nbytes == 2 * rows * 64 * 4 + 2 * rows * 4
     # a request is cut to the key tiles and then dealt out without empty ranges
-    _, bn, _ = binding.kernel_config(bf, 128)
-    tiles = lambda sk: -(-sk // bn)
-    assert binding.splitk_plan(bf, 1, 1, 64, 100, 128, 1000)[0] == tiles(100)
+    bn_of = lambda sk: binding.kernel_config(bf, 128, 64, sk, single_group=True)[1]
+    assert binding.splitk_plan(bf, 1, 1, 64, 100, 128, 1000)[0] == -(-100 // bn_of(100))
+    bn = next(n for n in (32, 64, 128) if bn_of(10 * n) == n)  # ten tiles in the same bucket
     assert binding.splitk_plan(bf, 1, 1, 64, 10 * bn, 128, 4)[0] == 4   # 3+3+3+1 tiles
     assert binding.splitk_plan(bf, 1, 1, 64, 10 * bn, 128, 6)[0] == 5   # 2 tiles each
     assert binding.splitk_plan(bf, 1, 1, 64, 0, 128, 8)[0] == 1
