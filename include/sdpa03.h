@@ -376,7 +376,7 @@ sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t tot
  * guides which kernel serves an input): seqlen_q and seqlen_k are the dense
  * lengths, the varlen calls'
  * max_seqlen_q / max_seqlen_k, or the padded calls' seqlen_*_max, in three
- * query buckets (<= 128, <= 512, longer) and two key buckets (<= 512,
+ * query buckets (<= 128, <= 512, <= 4096, longer) and two key buckets (<= 512,
  * longer).  causal and mode are accepted for a finer key later and do not
  * change the choice today (mode: 0 dense, 1 compact, 2 padded).
  * single_group != 0 asks for the shape of the split forward and of the

@@ -626,15 +626,29 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
     barrier_lds();  // every wave is done with K(0) before K(STAGES) replaces it
   }
 
+  // Under the causal mask a wave whose rows all precede the first key of
+  // tile t has nothing left to add: tile t and every later one are masked
+  // for all its rows.  Such a wave still issues its share of the tile copies
+  // and meets every barrier, but skips the products and the softmax (a
+  // wave-uniform branch).  The result is unchanged: the skipped weights are
+  // exactly 0 and a tile without weights never triggers a rescale.  With
+  // 256-row workgroups this removes 12 of the 32 wave-tiles of each diagonal
+  // block.
+  auto wave_done = [&](int t) { return CAUSAL && (tile0 + t) * BN > row0 + 31; };
+
   // Pipeline step for tile t when tile t+1 exists.  k_cur holds K(t) (done
   // with; K(t+STAGES) is loaded into it), k_nxt holds K(t+1), v_cur holds V(t)
   // and v_pre receives V(t+STAGES-1).  Phase A is straight-line code, so the
   // scheduler can interleave the softmax VALU work with the next tile's
   // score MFMAs.
   auto step = [&](int t, T* k_cur, T* k_nxt, T* v_cur, T* v_pre) {
+    // The next tile's bias goes out before the tile copies, so waiting for it
+    // never waits for them (also when this wave skips the tile: a
+    // conditional load would keep two copies of the bias registers alive).
     if constexpr (BIAS) load_bias(t + 1, bias_next);
     issue_k(t + STAGES, k_cur, t + STAGES < n_tiles ? kend : 0);
     issue_v(t + STAGES - 1, v_pre, t + STAGES - 1 < n_tiles ? kend : 0);
+    if (!wave_done(t)) {
 
     // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
     PRegs p;
@@ -668,6 +682,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
+    }  // !wave_done(t)
 
     // K(t+2) and V(t+1) -- issued one step earlier with three stages, in
     // this step with two -- must have landed before the next step.
@@ -676,6 +691,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   };
   // The last tile: probabilities and P.V only.
   auto last_step = [&](const T* v_cur) {
+    if (wave_done(n_tiles - 1)) return;
     PRegs p;
     l_run += probabilities(s, p);
     Path::template pv<NB, DB>(v_cur, p, lane, acc);
@@ -1119,7 +1135,9 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
     case 2: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 2>(a, s);
     case 3: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 3>(a, s);
     case 4: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 4>(a, s);
-    default: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 5>(a, s);
+    case 5: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 5>(a, s);
+    case 6: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 6>(a, s);
+    default: return launch_bucket<T, D, MODE, CAUSAL, BIAS, 7>(a, s);
   }
 }
 
@@ -1146,7 +1164,9 @@ int launch_split_typed(const FwdArgs& a, const MergeArgs& mg, hipStream_t s) {
     case 2: return launch_split_bucket<T, D, CAUSAL, 2>(a, mg, s);
     case 3: return launch_split_bucket<T, D, CAUSAL, 3>(a, mg, s);
     case 4: return launch_split_bucket<T, D, CAUSAL, 4>(a, mg, s);
-    default: return launch_split_bucket<T, D, CAUSAL, 5>(a, mg, s);
+    case 5: return launch_split_bucket<T, D, CAUSAL, 5>(a, mg, s);
+    case 6: return launch_split_bucket<T, D, CAUSAL, 6>(a, mg, s);
+    default: return launch_split_bucket<T, D, CAUSAL, 7>(a, mg, s);
   }
 }
 
@@ -1159,7 +1179,9 @@ TableEntry entry_for(int bucket) {
     case 2: return launch_entry<T, D, 2, SINGLE_GROUP>();
     case 3: return launch_entry<T, D, 3, SINGLE_GROUP>();
     case 4: return launch_entry<T, D, 4, SINGLE_GROUP>();
-    default: return launch_entry<T, D, 5, SINGLE_GROUP>();
+    case 5: return launch_entry<T, D, 5, SINGLE_GROUP>();
+    case 6: return launch_entry<T, D, 6, SINGLE_GROUP>();
+    default: return launch_entry<T, D, 7, SINGLE_GROUP>();
   }
 }
 

@@ -1,7 +1,8 @@
 """Offline sweep that writes the compiled-in dispatch table.
 
-The dispatch key is (dtype, head_dim, sequence-length bucket): three query
-buckets (<= 128, <= 512, longer) by two key buckets (<= 512, longer), as
+The dispatch key is (dtype, head_dim, sequence-length bucket): four query
+buckets (<= 128, <= 512, <= 4096, longer) by two key buckets (<= 512,
+longer), as
 AOTriton's tuning database probes sequence lengths, head dim and dtype
 (AOTriton issue #12, the maintainer's replies).  For every class (dtype,
 head_dim) a set of candidate kernel shapes (waves per workgroup, keys per
@@ -11,9 +12,9 @@ bucket of the class.  A candidate counts only if its build has no register
 spills, keeps two waves per SIMD, and then passes the GPU parity tests
 (tests/test_gpu_parity.py, run against that build): the same page warns that
 a kernel built with some configurations runs but gives wrong results.  Only
-then is it timed, on workloads of every bucket.  Per bucket, the fastest
-passing candidate on that bucket's workloads goes into
-csrc/dispatch_table.inc.  There is no tuning at run time.
+then is it timed, on workloads of every bucket.  Per bucket, the passing
+candidate with the lowest score on that bucket's workloads (its time over the
+best time, summed over the timed calls) goes into csrc/dispatch_table.inc.  There is no tuning at run time.
 
     python -m scaled_dot_product_03_amd.sweep build [name ...]  # CPU: compile candidates
     python -m scaled_dot_product_03_amd.sweep run [name ...]    # GPU: parity, then timing
@@ -46,8 +47,8 @@ CANDIDATES = {
                    (8, 64, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1)],
 }
 
-BUCKETS = ["q<=128,k<=512", "q<=128,k>512", "q<=512,k<=512", "q<=512,k>512", "q>512,k<=512",
-           "q>512,k>512"]
+BUCKETS = ["q<=128,k<=512", "q<=128,k>512", "q<=512,k<=512", "q<=512,k>512",
+           "q<=4096,k<=512", "q<=4096,k>512", "q>4096,k<=512", "q>4096,k>512"]
 
 
 def _bucket_workloads(dtype, d):
@@ -66,9 +67,11 @@ def _bucket_workloads(dtype, d):
         3: [dense(2, 32, 512, 8192, (False,))],
         4: [dense(4, 16, 2048, 512, (False,))],
         5: [dense(4, 16, 2048, 2048), thd(16, 4096)],
+        6: [dense(1, 16, 8192, 512, (False,))],
+        7: [dense(1, 16, 8192, 8192)],
     }
     if (dtype, d) == ("bf16", 128):
-        w[5].append(("padded_bf16_b8h32smax8192d128_len2048to8192_causal", "named", {}))
+        w[7].append(("padded_bf16_b8h32smax8192d128_len2048to8192_causal", "named", {}))
     return w
 
 
@@ -277,20 +280,29 @@ def _entry(cand):
 
 
 def write(results_path=RESULTS, table_path=TABLE):
-    """Per (class, bucket): the passing candidate with the smallest sum of that
-    bucket's workload times.  Classes without timed workloads follow the timed
-    class of the same head_dim."""
+    """Per (class, bucket): the passing candidate with the smallest score, the
+    sum over that bucket's timed calls of its time divided by the best time
+    any passing candidate reached on the call (so every workload counts
+    alike, whatever its length).  Classes without timed workloads follow the
+    timed class of the same head_dim."""
     with open(results_path) as f:
         results = json.load(f)
-    best = {}  # (dtype, d, bucket) -> (total ms, cand)
-    for r in results:
-        if not r["parity"] or not r["ms"]:
-            continue
+    passing = [r for r in results if r["parity"] and r["ms"]]
+    fastest = {}  # (dtype, d, bucket, workload, call index) -> best ms
+    for r in passing:
+        for bucket, times in r["ms"].items():
+            for name, calls in times.items():
+                for i, t in enumerate(calls):
+                    k = (r["dtype"], r["head_dim"], int(bucket), name, i)
+                    fastest[k] = min(fastest.get(k, t), t)
+    best = {}  # (dtype, d, bucket) -> (score, cand)
+    for r in passing:
         for bucket, times in r["ms"].items():
             key = (r["dtype"], r["head_dim"], int(bucket))
-            total = sum(sum(v) for v in times.values())
-            if key not in best or total < best[key][0]:
-                best[key] = (total, _cand4(r["cand"]))
+            score = sum(t / fastest[key + (name, i)]
+                        for name, calls in times.items() for i, t in enumerate(calls))
+            if key not in best or score < best[key][0]:
+                best[key] = (score, _cand4(r["cand"]))
     default = {128: (4, 64, 2, 0), 64: (4, 64, 3, 0)}
     timed_class = {128: "bf16", 64: "fp16"}
     pick = {}
@@ -301,9 +313,10 @@ def write(results_path=RESULTS, table_path=TABLE):
                 pick[(dt, d, b)] = best[src][1] if src in best else default[d]
     lines = ["  // BEGIN TABLE (generated)",
              "  // buckets: " + ", ".join(f"({b})" for b in BUCKETS)]
-    for (dt, d, b), (total, cand) in sorted(best.items()):
+    for (dt, d, b), (score, cand) in sorted(best.items()):
+        n_calls = sum(1 for k in fastest if k[:3] == (dt, d, b))
         lines.append(f"  // {dt} d{d} bucket {b}: (waves, block_n, stages, pingpong) = {cand}; "
-                     f"sum of timed workloads {total:.3f} ms")
+                     f"score {score:.3f} over {n_calls} timed calls (1 per call is best)")
     lines += ["  if constexpr (sizeof(T) == 4) {", "    return TableEntry{4, 32, 2, 0};"]
     for dt in ("bf16", "fp16"):
         for d in (128, 64):

@@ -79,11 +79,11 @@ def test_kernel_config_table():
 
 def test_kernel_config_bucket_edges():
     """The choice can change only at the bucket edges of the dispatch key
-    (query extent 128 / 512, key extent 512)."""
+    (query extent 128 / 512 / 4096, key extent 512)."""
     for dt in (torch.float16, torch.bfloat16):
         for d in (64, 128):
             cfg = lambda sq, sk: binding.kernel_config(dt, d, sq, sk)
-            for lo, hi in [(1, 128), (129, 512), (513, 1 << 20)]:
+            for lo, hi in [(1, 128), (129, 512), (513, 4096), (4097, 1 << 20)]:
                 for klo, khi in [(1, 512), (513, 1 << 20)]:
                     assert cfg(lo, klo) == cfg(hi, khi) == cfg(lo, khi) == cfg(hi, klo)
 

@@ -1,0 +1,93 @@
+"""GPU parity of every entry of the compiled-in dispatch table.
+
+The table keys the kernel shape on (dtype, head_dim, sequence-length
+bucket).  For every 16-bit class and every bucket, a dense problem whose
+lengths fall in that bucket runs through attn_fwd (both masks) and, in the
+long buckets, through the forward with a bias and the split forward (which
+take the bucket's single-group shape); sampled rows are compared with the
+float64 oracle, so each compiled shape of the committed library is
+parity-checked, not only those the small parity shapes happen to reach.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_head
+from parity import check, sample_rows, to64
+from scaled_dot_product_03_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (query length, key length) per bucket: query extent <= 128, <= 512,
+# <= 4096, longer; key extent <= 512, longer.
+BUCKET_SHAPES = [(100, 300), (128, 700), (300, 512), (257, 1500), (1000, 200), (2048, 900),
+                 (4200, 64), (4500, 4500)]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sampled_check(x, o, lse, causal, dt, label, bias=None, heads=((0, 0), (0, 1))):
+    rng = np.random.default_rng(7)
+    go, gl, ro, rl = [], [], [], []
+    for b, h in heads:
+        rows = sample_rows(x.q.shape[2], rng, extra=6)
+        r_o, r_l = attention_head(to64(x.q[b, h]), to64(x.k[b, h]), to64(x.v[b, h]), x.scale,
+                                  causal, rows=rows,
+                                  bias=None if bias is None else to64(bias[b, h]))
+        go.append(to64(o[b, h, rows]))
+        gl.append(to64(lse[b, h, rows]))
+        ro.append(r_o)
+        rl.append(r_l)
+    check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl), dt,
+          label=label)
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 64)])
+@pytest.mark.parametrize("bucket", range(len(BUCKET_SHAPES)))
+def test_every_table_entry(dt, D, bucket):
+    sq, sk = BUCKET_SHAPES[bucket]
+    bm, bn, w = binding.kernel_config(inputs.DTYPES[dt], D, sq, sk)
+    _log(f"dispatch {dt} D{D} bucket {bucket} Sq{sq} Sk{sk}: block_m {bm} block_n {bn} "
+         f"waves {w}")
+    x = inputs.dense_inputs(1, 2, sq, sk, D, dt, seed=500 + bucket)
+    q, k, v = x.q.to(DEV), x.k.to(DEV), x.v.to(DEV)
+    for causal in (False, True):
+        o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        _sampled_check(x, o, lse, causal, dt, f"{dt} D{D} bucket {bucket} causal={causal}")
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("bucket", [5, 7])
+def test_single_group_entries_with_bias_and_split(dt, D, bucket):
+    sq, sk = BUCKET_SHAPES[bucket]
+    _log(f"dispatch single-group {dt} D{D} bucket {bucket}")
+    x = inputs.dense_inputs(1, 2, sq, sk, D, dt, seed=600 + bucket)
+    q, k, v = x.q.to(DEV), x.k.to(DEV), x.v.to(DEV)
+    bias = inputs.bias_tensor((1, 2, sq, sk), dt, seed=601)
+    pad = (sk + 7) // 8 * 8
+    bd = torch.empty((1, 2, sq, pad), dtype=q.dtype, device=DEV)[..., :sk]
+    bd.copy_(bias)
+    o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=True, bias=bd)
+    torch.cuda.synchronize()
+    _sampled_check(x, o, lse, True, dt, f"bias {dt} D{D} bucket {bucket}", bias=bias)
+    o, lse = binding.attn_fwd_splitk(q, k, v, scale=x.scale, causal=False)
+    torch.cuda.synchronize()
+    _sampled_check(x, o, lse, False, dt, f"split {dt} D{D} bucket {bucket}")
