@@ -37,16 +37,19 @@
 namespace sdpa03 {
 namespace {
 
-// LDS row stride (bytes) of a tile that is read both as 16-row MFMA operands
-// (ds_read_b128: the 16 rows of one pass must start in distinct 16-byte bank
-// groups of gfx950's 256-byte bank cycle) and transposed (ds_read_b64_tr_b16:
-// the 4 rows of one 32-lane pass must start in distinct 64-byte blocks).  An
-// odd multiple of 16 satisfies the first; D * 2 + 80 also satisfies the
-// second: consecutive rows start 0, 80, 160, 240 (D = 128) or 0, 208, 160,
-// 112 (D = 64) bytes into the cycle.
+// Tiles read both as 16-row MFMA operands and transposed.  In the dK/dV
+// kernel (Q and dO) they are unpadded and chunk-swizzled (swizzle_of<D>,
+// conflict-free for both reads).  No padding serves both reads: D * 2 + 80,
+// used for K in the dQ kernel, keeps the plain reads clean, but the 4 rows
+// of a transposing pass then overlap in the bank cycle (a 2-way conflict on
+// part of every such pass).  The dQ kernel runs two waves per SIMD and has no
+// registers left for the swizzle's per-lane offsets.
 template <int D>
-constexpr int dual_row_bytes() { return D * 2 + 80; }
-// Tiles read only as 16-row MFMA operands.
+constexpr int swizzled_row_bytes() { return D * 2; }
+template <int D>
+constexpr int padded_dual_row_bytes() { return D * 2 + 80; }
+// Tiles read only as 16-row MFMA operands: 16 bytes of padding shift
+// consecutive rows by one 16-byte bank group.
 template <int D>
 constexpr int plain_row_bytes() { return D * 2 + 16; }
 
@@ -71,17 +74,21 @@ __device__ __forceinline__ void interleave_reads() {
 
 // c[nb] += A B for nb < NB.  A: rows 32 nb .. 32 nb + 31 of an LDS tile with
 // row stride ROW bytes, 16 dims per k-step (lane (rho, h) reads the 16 bytes
-// at dims 16 ks + 8 h of row 32 nb + rho).  B: the wave's own rows, one
-// fragment per k-step, in registers.
-template <typename T, int D, int ROW, int NB>
+// at dims 16 ks + 8 h -- chunk 2 ks + h -- of row 32 nb + rho; SWZ: a
+// swizzled tile, that chunk stored at (2 ks + h) ^ swizzle_of<D>(rho), one
+// XOR per k-step).  B: the wave's own rows, one fragment per k-step, in
+// registers.
+template <typename T, int D, int ROW, int NB, bool SWZ>
 __device__ __forceinline__ void tile_rows_x_regs(const T* tile, const frag_t<T> (&b)[D / 16],
                                                  int li, int lh, f32x16 (&c)[NB]) {
-  const char* base = reinterpret_cast<const char*>(tile) + li * ROW + lh * 16;
+  const char* base = reinterpret_cast<const char*>(tile) + li * ROW;
+  const int x = SWZ ? ((lh ^ swizzle_of<D>(li)) << 4) : (lh << 4);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
+    const int off = SWZ ? (x ^ (ks * 32)) : (x + ks * 32);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const frag_t<T> a = *reinterpret_cast<const frag_t<T>*>(base + nb * 32 * ROW + ks * 32);
+      const frag_t<T> a = *reinterpret_cast<const frag_t<T>*>(base + nb * 32 * ROW + off);
       c[nb] = Mma16<T>::mma(a, b[ks], c[nb]);
     }
   }
@@ -96,16 +103,25 @@ __device__ __forceinline__ void tile_rows_x_regs(const T* tile, const frag_t<T> 
 // 64-bit words read by lanes 4 j + (i >> 2); with lane t pointing at row
 // R0 + t / 4, column C0 + 4 (t & 3), lane i receives X[R0 + j][C0 + i] for
 // j = 0..3.  Two reads (R0 = 32 nb + 16 half + 4 h and R0 + 8) give the eight
-// rows of one operand.
-template <typename T, int ROW, int NB, int DB>
+// rows of one operand.  SWZ: a swizzled tile; the byte column
+// 2 C0 + 8 (t & 3) + 64 db (below 64 before the db term) has its chunk bits
+// XORed with swizzle_of<D> of the row, which modulo 16 depends only on sub
+// and the lane: one XOR per (sub, db).
+template <typename T, int ROW, int NB, int DB, bool SWZ>
 __device__ __forceinline__ void tile_tr_x_frags(const T* tile, const frag_t<T> (&w)[NB][2],
                                                 int lane, f32x16 (&acc)[DB]) {
   using s16x4 = short __attribute__((ext_vector_type(4)));
+  constexpr int D = DB * 32;
   const int t = lane & 15;
   const int grp = lane >> 4;
   const int row_lane = (grp >> 1) * 4 + (t >> 2);
   const int col_lane = (grp & 1) * 16 + 4 * (t & 3);
-  const char* base = reinterpret_cast<const char*>(tile) + row_lane * ROW + col_lane * 2;
+  const char* base = reinterpret_cast<const char*>(tile) + row_lane * ROW;
+  int z[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    z[sub] = SWZ ? ((col_lane * 2) ^ (swizzle_of<D>(sub * 8 + row_lane) << 4)) : col_lane * 2;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -115,7 +131,8 @@ __device__ __forceinline__ void tile_tr_x_frags(const T* tile, const frag_t<T> (
         s16x4 x[2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const char* src = base + (nb * 32 + half * 16 + sub * 8) * ROW + db * 64;
+          const int col = SWZ ? (z[sub] ^ (db * 64)) : (z[sub] + db * 64);
+          const char* src = base + (nb * 32 + half * 16 + sub * 8) * ROW + col;
           x[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4*)(src));
         }
@@ -218,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
-  constexpr int kRowK = dual_row_bytes<D>();
+  constexpr int kRowK = padded_dual_row_bytes<D>();
   constexpr int kRowV = plain_row_bytes<D>();
   using KCopy = TileCopy<T, D, BN, NW, kRowK>;
   using VCopy = TileCopy<T, D, BN, NW, kRowV>;
@@ -305,9 +322,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       const T* kb = kc + nb * 32 * kRowK / static_cast<int>(sizeof(T));
       const T* vb = vc + nb * 32 * kRowV / static_cast<int>(sizeof(T));
       f32x16 st[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRowK, 1>(kb, qf, li, lh, st);
+      tile_rows_x_regs<T, D, kRowK, 1, false>(kb, qf, li, lh, st);
       f32x16 dpt[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRowV, 1>(vb, df, li, lh, dpt);
+      tile_rows_x_regs<T, D, kRowV, 1, false>(vb, df, li, lh, dpt);
       const bool need_mask = (j0 + 32 > sr.len_k) || (CAUSAL && j0 + 31 > row0);
       frag w[1][2];
 #pragma unroll
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         }
         w[0][r >> 3][r & 7] = static_cast<T>(p * (dpt[0][r] - delta));
       }
-      tile_tr_x_frags<T, kRowK, 1, DB>(kb, w, lane, acc);
+      tile_tr_x_frags<T, kRowK, 1, DB, false>(kb, w, lane, acc);
       // S^T and dP^T: 2 * D/16 products over as many reads; dQ: 2 * DB
       // products over 4 * DB transposing reads.
       interleave_reads<2 * (D / 16) + 2 * DB, 2 * (D / 16) + 4 * DB>();
@@ -364,13 +381,21 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   constexpr int BQ = 64;
   constexpr int NB = BQ / 32;
   constexpr int DB = D / 32;
-  constexpr int kRow = dual_row_bytes<D>();
-  using QCopy = TileCopy<T, D, BQ, NW, kRow>;
+  constexpr int kRow = swizzled_row_bytes<D>();
+  using QCopy = TileCopy<T, D, BQ, NW, kRow, true>;
+  // A tile's BQ workspace values (LSE * log2(e), delta) as one row of BQ
+  // floats: one buffer load into a 1 KiB LDS block, issued by one wave.
+  using WCopy = TileCopy<float, BQ, 1, 1, BQ * 4>;
+  static_assert(WCopy::kArrayBytes == 1024, "one block per workspace vector");
   using frag = frag_t<T>;
   __shared__ __attribute__((aligned(1024))) T q_lds0[QCopy::kArrayBytes / 2];
   __shared__ __attribute__((aligned(1024))) T q_lds1[QCopy::kArrayBytes / 2];
   __shared__ __attribute__((aligned(1024))) T d_lds0[QCopy::kArrayBytes / 2];
   __shared__ __attribute__((aligned(1024))) T d_lds1[QCopy::kArrayBytes / 2];
+  __shared__ __attribute__((aligned(1024))) float l_lds0[256];
+  __shared__ __attribute__((aligned(1024))) float l_lds1[256];
+  __shared__ __attribute__((aligned(1024))) float e_lds0[256];
+  __shared__ __attribute__((aligned(1024))) float e_lds1[256];
 
   // Under the causal mask the first key tiles cost the most: they go first.
   const uint32_t n = blockIdx.x;
@@ -436,35 +461,54 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
 
   QCopy qcopy;
   QCopy dcopy;
+  WCopy wcopy;
   qcopy.init(wave, lane, q_row_bytes);
   dcopy.init(wave, lane, d_row_bytes);
-  auto issue = [&](int t, T* qb, T* db_) {
+  wcopy.init(0, lane, BQ * 4);
+  // The tile's workspace values travel with its Q and dO rows (waves 0 and 1
+  // issue them): read from global memory inside the block loop, their waits
+  // would also drain the next tile's copies, issued earlier, every block.
+  // The workspace rows of a whole tile lie inside its padding.
+  auto issue = [&](int t, T* qb, T* db_, float* lb, float* eb) {
     const int q0 = qbeg + t * BQ;
     const int rows = t < n_tiles ? sr.len_q - q0 : 0;
     qcopy.issue(qp + q0 * q_row_bytes, rows, q_row_bytes, qb, wave);
     dcopy.issue(dp + q0 * d_row_bytes, rows, d_row_bytes, db_, wave);
+    const int wrows = t < n_tiles ? 1 : 0;
+    if (wave == 0) {
+      wcopy.issue(reinterpret_cast<const char*>(lse2p + q0), wrows, BQ * 4, lb, 0);
+    } else if (wave == 1) {
+      wcopy.issue(reinterpret_cast<const char*>(deltap + q0), wrows, BQ * 4, eb, 0);
+    }
   };
 
   // Query tile t, one 32-row block at a time: S = Q K^T, P,
   // dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  Register r belongs to
-  // query row q0 + 32 nb + 8 (r / 4) + 4 h + r % 4; the workspace rows of a
-  // whole tile lie inside its padding, so they are read without bounds checks.
-  auto compute = [&](int t, const T* qc, const T* dc) {
+  // query row q0 + 32 nb + 8 (r / 4) + 4 h + r % 4.
+  auto compute = [&](int t, const T* qc, const T* dc, const float* lc, const float* ec) {
 #pragma nounroll
     for (int nb = 0; nb < NB; ++nb) {
       const int q0 = qbeg + t * BQ + nb * 32;
       const T* qb = qc + nb * 32 * kRow / static_cast<int>(sizeof(T));
       const T* db_ = dc + nb * 32 * kRow / static_cast<int>(sizeof(T));
+      const float* lb = lc + nb * 32;
+      const float* eb = ec + nb * 32;
       f32x16 s[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRow, 1>(qb, kf, li, lh, s);
-      const bool need_mask = (q0 + 32 > sr.len_q) || (CAUSAL && q0 < key0 + 31);
+      tile_rows_x_regs<T, D, kRow, 1, true>(qb, kf, li, lh, s);
+      // Dense and padded rows past the sequence carry LSE * log2(e) = +inf
+      // (and delta 0) in the workspace and zero Q and dO rows, so their
+      // weights are exactly 0 unmasked; keys past it feed only the lane's own
+      // dK and dV columns, which are not stored.  Compact rows past the
+      // sequence belong to the next one (finite LSE): those are masked, as
+      // are keys past the row under the causal mask.
+      const bool need_mask =
+          (MODE == MODE_COMPACT && q0 + 32 > sr.len_q) || (CAUSAL && q0 < key0 + 31);
       float pr[16];
       frag w[1][2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = q0 + 8 * g4 + 4 * lh;
-        f32x4 l4;  // the sequence may start at any row: 4-byte aligned copy
-        __builtin_memcpy(&l4, lse2p + qr, sizeof(l4));
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 8 * g4 + 4 * lh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -477,37 +521,36 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
           w[0][r >> 3][r & 7] = static_cast<T>(p);
         }
       }
-      tile_tr_x_frags<T, kRow, 1, DB>(db_, w, lane, dv);
+      tile_tr_x_frags<T, kRow, 1, DB, true>(db_, w, lane, dv);
       f32x16 dpp[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRow, 1>(db_, vf, li, lh, dpp);
+      tile_rows_x_regs<T, D, kRow, 1, true>(db_, vf, li, lh, dpp);
       frag ws[1][2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 d4;
-        __builtin_memcpy(&d4, deltap + q0 + 8 * g4 + 4 * lh, sizeof(d4));
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(eb + 8 * g4 + 4 * lh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           ws[0][r >> 3][r & 7] = static_cast<T>(pr[r] * (dpp[0][r] - d4[e]));
         }
       }
-      tile_tr_x_frags<T, kRow, 1, DB>(qb, ws, lane, dk);
+      tile_tr_x_frags<T, kRow, 1, DB, true>(qb, ws, lane, dk);
       interleave_reads<2 * (D / 16) + 4 * DB, 2 * (D / 16) + 8 * DB>();
     }
   };
 
   if (n_tiles > 0) {
-    issue(0, q_lds0, d_lds0);
+    issue(0, q_lds0, d_lds0, l_lds0, e_lds0);
     wait_vmem();
     barrier_lds();
     for (int t = 0;; t += 2) {
-      issue(t + 1, q_lds1, d_lds1);
-      compute(t, q_lds0, d_lds0);
+      issue(t + 1, q_lds1, d_lds1, l_lds1, e_lds1);
+      compute(t, q_lds0, d_lds0, l_lds0, e_lds0);
       wait_vmem();
       barrier_lds();
       if (t + 1 >= n_tiles) break;
-      issue(t + 2, q_lds0, d_lds0);
-      compute(t + 1, q_lds1, d_lds1);
+      issue(t + 2, q_lds0, d_lds0, l_lds0, e_lds0);
+      compute(t + 1, q_lds1, d_lds1, l_lds1, e_lds1);
       wait_vmem();
       barrier_lds();
       if (t + 2 >= n_tiles) break;

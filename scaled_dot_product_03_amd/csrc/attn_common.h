@@ -109,8 +109,29 @@ __device__ __forceinline__ float tree_sum16(const float (&x)[16]) {
 // sequence read back as zeros too, with no bounds arithmetic in the loop.
 // Source offsets are 32-bit: the host limits row strides accordingly.
 
-template <typename T, int D, int BN, int NW, int ROW>
+// XOR swizzle of the 16-byte chunks of a 16-bit tile whose rows are exactly
+// D * 2 bytes long and that is read both as 16-row MFMA operands
+// (ds_read_b128: a pass reads one chunk of 16 aligned consecutive rows) and
+// transposed (ds_read_b64_tr_b16: a 32-lane pass reads one aligned 64-byte
+// block of 4 aligned consecutive rows).  Chunk c of row r is stored at chunk
+// c ^ swizzle_of<D>(r).  Over 16 aligned rows the XOR puts a chunk in 16
+// distinct bank groups (for D = 64, rows of one parity share a half of the
+// banks and take 8 distinct values each); over 4 aligned rows it gives a
+// 64-byte block 4 distinct block positions.  So both passes touch every
+// bank once.  No row padding does both: the first needs the stride / 16 to
+// be odd, the second a stride of +-64 modulo 256 bytes.
+template <int D>
+__host__ __device__ constexpr int swizzle_of(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// SWIZZLE: rows of exactly D * 2 bytes (ROW == D * 2), chunks stored as
+// swizzle_of<D> says; each lane fetches the source chunk that belongs at
+// its (lane-linear) LDS position.
+template <typename T, int D, int BN, int NW, int ROW, bool SWIZZLE = false>
 struct TileCopy {
+  static_assert(!SWIZZLE || (sizeof(T) == 2 && ROW == D * 2), "swizzled tiles: 16-bit, unpadded");
   static constexpr int kDataBytes = D * static_cast<int>(sizeof(T));  // payload per row
   static constexpr int kBlocks = (BN * ROW + 1023) / 1024;
   static constexpr int kInstPerWave = (kBlocks + NW - 1) / NW;
@@ -124,7 +145,7 @@ struct TileCopy {
     for (int i = 0; i < kInstPerWave; ++i) {
       const int pos = (i * NW + wave) * 1024 + lane * 16;
       const int r = pos / ROW;
-      const int col = pos % ROW;
+      const int col = SWIZZLE ? ((((pos % ROW) >> 4) ^ swizzle_of<D>(r)) << 4) : pos % ROW;
       const bool data = r < BN && col < kDataBytes;
       voff[i] = data ? static_cast<uint32_t>(r * row_bytes) + static_cast<uint32_t>(col) : kNowhere;
     }
