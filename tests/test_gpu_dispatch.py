@@ -2,11 +2,13 @@
 
 The table keys the kernel shape on (dtype, head_dim, sequence-length
 bucket).  For every 16-bit class and every bucket, a dense problem whose
-lengths fall in that bucket runs through attn_fwd (both masks) and, in the
-long buckets, through the forward with a bias and the split forward (which
-take the bucket's single-group shape); sampled rows are compared with the
-float64 oracle, so each compiled shape of the committed library is
-parity-checked, not only those the small parity shapes happen to reach.
+lengths fall in that bucket runs through attn_fwd (both masks), a compact
+and a padded problem whose longest sequence has those lengths run through
+the varlen calls, and in the long buckets the forward with a bias and the
+split forward (which take the bucket's single-group shape) run too; sampled
+rows are compared with the float64 oracle, so each compiled kernel of the
+committed library is parity-checked, not only those the small parity shapes
+happen to reach.
 """
 
 import sys
@@ -91,3 +93,56 @@ def test_single_group_entries_with_bias_and_split(dt, D, bucket):
     o, lse = binding.attn_fwd_splitk(q, k, v, scale=x.scale, causal=False)
     torch.cuda.synchronize()
     _sampled_check(x, o, lse, False, dt, f"split {dt} D{D} bucket {bucket}")
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 64)])
+@pytest.mark.parametrize("bucket", range(len(BUCKET_SHAPES)))
+def test_every_table_entry_varlen(dt, D, bucket):
+    """The compact and padded kernels of every entry: two sequences whose
+    longest has the bucket's lengths (the dispatch key of the varlen layouts
+    is the longest sequence), the other shorter and ragged."""
+    sq, sk = BUCKET_SHAPES[bucket]
+    lq, lk = [sq, max(1, sq // 3 + 5)], [sk, max(1, sk // 2 + 3)]
+    H = 2
+    rng = np.random.default_rng(7)
+    for causal in (False, True):
+        _log(f"dispatch varlen {dt} D{D} bucket {bucket} causal={causal}")
+        x = inputs.compact_inputs(2, H, D, dt, seed=700 + bucket, len_lo=1, len_hi=2,
+                                  lengths_q=lq, lengths_k=lk)
+        q, k, v = x.q.to(DEV), x.k.to(DEV), x.v.to(DEV)
+        o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                                 scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        go, gl, ro, rl = [], [], [], []
+        for z in range(2):
+            qs, qe = int(x.cu_seqlens_q[z]), int(x.cu_seqlens_q[z + 1])
+            ks, ke = int(x.cu_seqlens_k[z]), int(x.cu_seqlens_k[z + 1])
+            rows = sample_rows(qe - qs, rng, extra=4)
+            for h in range(H):
+                r_o, r_l = attention_head(to64(x.q[qs:qe, h]), to64(x.k[ks:ke, h]),
+                                          to64(x.v[ks:ke, h]), x.scale, causal, rows=rows)
+                go.append(to64(o[qs + rows, h]))
+                gl.append(to64(lse[0, h, qs + rows]))
+                ro.append(r_o)
+                rl.append(r_l)
+        check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl), dt,
+              label=f"compact {dt} D{D} bucket {bucket} causal={causal}")
+        # the same two sequences as padded batches of the longest lengths
+        xp = inputs.padded_inputs(2, H, sq, sk, D, dt, seed=710 + bucket, len_lo=1, len_hi=2,
+                                  lengths_q=lq, lengths_k=lk)
+        o, lse = binding.attn_fwd_padded_varlen(xp.q.to(DEV), xp.k.to(DEV), xp.v.to(DEV),
+                                                xp.cu_seqlens_q, xp.cu_seqlens_k, scale=xp.scale,
+                                                causal=causal)
+        torch.cuda.synchronize()
+        go, gl, ro, rl = [], [], [], []
+        for b in range(2):
+            rows = sample_rows(lq[b], rng, extra=4)
+            for h in range(H):
+                r_o, r_l = attention_head(to64(xp.q[b, h, :lq[b]]), to64(xp.k[b, h, :lk[b]]),
+                                          to64(xp.v[b, h, :lk[b]]), xp.scale, causal, rows=rows)
+                go.append(to64(o[b, h, rows]))
+                gl.append(to64(lse[b, h, rows]))
+                ro.append(r_o)
+                rl.append(r_l)
+        check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl), dt,
+              label=f"padded {dt} D{D} bucket {bucket} causal={causal}")
