@@ -144,6 +144,56 @@ __device__ __forceinline__ void tile_tr_x_frags(const T* tile, const frag_t<T> (
   }
 }
 
+// The same two products on a swizzled tile addressed by LDS byte address:
+// lane_addr is the address of the lane's chunk 0 (its row, chunk h ^ swizzle
+// for the plain read; its row and column, XOR the swizzle, for the
+// transposing one) in a tile whose base is aligned to twice its size, so the
+// k-step's and the D block's chunk bits join by XOR and the row offsets stay
+// immediates.
+template <typename T>
+__device__ __forceinline__ frag_t<T> lds_frag(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) frag_t<T>*)(addr);
+}
+
+template <typename T, int D, int ROW, int NB>
+__device__ __forceinline__ void addr_rows_x_regs(uint32_t lane_addr, const frag_t<T> (&b)[D / 16],
+                                                 f32x16 (&c)[NB]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint32_t a0 = lane_addr ^ static_cast<uint32_t>(ks * 32);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      c[nb] = Mma16<T>::mma(lds_frag<T>(a0 + nb * 32 * ROW), b[ks], c[nb]);
+    }
+  }
+}
+
+template <typename T, int ROW, int NB, int DB>
+__device__ __forceinline__ void addr_tr_x_frags(const uint32_t (&lane_addr)[2],
+                                                const frag_t<T> (&w)[NB][2], f32x16 (&acc)[DB]) {
+  using s16x4 = short __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        s16x4 x[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const uint32_t src = (lane_addr[sub] ^ static_cast<uint32_t>(db * 64)) +
+                               (nb * 32 + half * 16 + sub * 8) * ROW;
+          x[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(src));
+        }
+        frag_t<T> xf;
+        __builtin_memcpy(&xf, x, sizeof(xf));
+        acc[db] = Mma16<T>::mma(xf, w[nb][half], acc[db]);
+      }
+    }
+  }
+}
+
 // The wave's own 32 rows as MFMA B-operand fragments: lane (i, h) holds the
 // 8 elements at dims 16 ks + 8 h of row i (zeros for rows past the end).
 template <typename T, int D>
@@ -388,14 +438,18 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   using WCopy = TileCopy<float, BQ, 1, 1, BQ * 4>;
   static_assert(WCopy::kArrayBytes == 1024, "one block per workspace vector");
   using frag = frag_t<T>;
-  __shared__ __attribute__((aligned(1024))) T q_lds0[QCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) T q_lds1[QCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) T d_lds0[QCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) T d_lds1[QCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) float l_lds0[256];
-  __shared__ __attribute__((aligned(1024))) float l_lds1[256];
-  __shared__ __attribute__((aligned(1024))) float e_lds0[256];
-  __shared__ __attribute__((aligned(1024))) float e_lds1[256];
+  // Two stages of each tile kind in one array, kStage bytes (a power of two)
+  // apart, the array aligned to 2 kStage: stage 1's addresses are stage 0's
+  // XOR kStage.  One loop body then serves both stages (two unrolled bodies
+  // made the compiler copy the dK and dV accumulators between them every
+  // step).  The workspace vectors: per stage 1 KiB of LSE * log2(e), then
+  // 1 KiB of delta.
+  constexpr int kStage = QCopy::kArrayBytes;
+  static_assert(kStage == BQ * kRow && (kStage & (kStage - 1)) == 0, "power-of-two stages");
+  constexpr int kWStage = 2 * WCopy::kArrayBytes;
+  __shared__ __attribute__((aligned(2 * kStage))) T q_lds[kStage];  // 2 stages of kStage bytes
+  __shared__ __attribute__((aligned(2 * kStage))) T d_lds[kStage];
+  __shared__ __attribute__((aligned(2 * kWStage))) float w_lds[kWStage / 2];
 
   // Under the causal mask the first key tiles cost the most: they go first.
   const uint32_t n = blockIdx.x;
@@ -468,33 +522,64 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   // The tile's workspace values travel with its Q and dO rows (waves 0 and 1
   // issue them): read from global memory inside the block loop, their waits
   // would also drain the next tile's copies, issued earlier, every block.
-  // The workspace rows of a whole tile lie inside its padding.
-  auto issue = [&](int t, T* qb, T* db_, float* lb, float* eb) {
+  // The workspace rows of a whole tile lie inside its padding.  The copies
+  // are issued as inline assembly the compiler does not track (it could not
+  // tell the stage being filled from the one being read); every wave waits
+  // for its own copies at the end of the step, before the barrier.
+  auto issue = [&](int t, int st) {
     const int q0 = qbeg + t * BQ;
-    const int rows = t < n_tiles ? sr.len_q - q0 : 0;
-    qcopy.issue(qp + q0 * q_row_bytes, rows, q_row_bytes, qb, wave);
-    dcopy.issue(dp + q0 * d_row_bytes, rows, d_row_bytes, db_, wave);
-    const int wrows = t < n_tiles ? 1 : 0;
+    const int rows = sr.len_q - q0;
+    qcopy.issue_untracked(qp + q0 * q_row_bytes, rows, q_row_bytes, q_lds + st * (kStage / 2),
+                          wave);
+    dcopy.issue_untracked(dp + q0 * d_row_bytes, rows, d_row_bytes, d_lds + st * (kStage / 2),
+                          wave);
     if (wave == 0) {
-      wcopy.issue(reinterpret_cast<const char*>(lse2p + q0), wrows, BQ * 4, lb, 0);
+      wcopy.issue_untracked(reinterpret_cast<const char*>(lse2p + q0), 1, BQ * 4,
+                            w_lds + st * (kWStage / 4), 0);
     } else if (wave == 1) {
-      wcopy.issue(reinterpret_cast<const char*>(deltap + q0), wrows, BQ * 4, eb, 0);
+      wcopy.issue_untracked(reinterpret_cast<const char*>(deltap + q0), 1, BQ * 4,
+                            w_lds + st * (kWStage / 4) + 256, 0);
     }
   };
+
+  // Per-lane LDS addresses in stage 0: the plain reads' row li, chunk
+  // lh ^ swizzle; the transposing reads' row and column of each sub-pass.
+  const uint32_t q_base = (uint32_t)(uintptr_t)(lds_void_ptr)(q_lds);
+  const uint32_t d_base = (uint32_t)(uintptr_t)(lds_void_ptr)(d_lds);
+  const uint32_t w_base = (uint32_t)(uintptr_t)(lds_void_ptr)(w_lds);
+  const uint32_t plain_off = li * kRow + ((lh ^ swizzle_of<D>(li)) << 4);
+  uint32_t tr_off[2];
+  {
+    const int tt = lane & 15;
+    const int grp = lane >> 4;
+    const int row_lane = (grp >> 1) * 4 + (tt >> 2);
+    const int col_lane = (grp & 1) * 16 + 4 * (tt & 3);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      tr_off[sub] = row_lane * kRow + ((col_lane * 2) ^ (swizzle_of<D>(sub * 8 + row_lane) << 4));
+    }
+  }
 
   // Query tile t, one 32-row block at a time: S = Q K^T, P,
   // dV^T += dO^T P, dP = dO V^T, dS, dK^T += Q^T dS.  Register r belongs to
   // query row q0 + 32 nb + 8 (r / 4) + 4 h + r % 4.
-  auto compute = [&](int t, const T* qc, const T* dc, const float* lc, const float* ec) {
+  auto compute = [&](int t, int st) {
+    const uint32_t so = static_cast<uint32_t>(st * kStage);  // stage offset, an XOR
+    const uint32_t q_plain = (q_base + plain_off) ^ so;
+    const uint32_t d_plain = (d_base + plain_off) ^ so;
+    const uint32_t q_tr[2] = {(q_base + tr_off[0]) ^ so, (q_base + tr_off[1]) ^ so};
+    const uint32_t d_tr[2] = {(d_base + tr_off[0]) ^ so, (d_base + tr_off[1]) ^ so};
+    const uint32_t w_st = w_base + static_cast<uint32_t>(st * kWStage);
 #pragma nounroll
     for (int nb = 0; nb < NB; ++nb) {
       const int q0 = qbeg + t * BQ + nb * 32;
-      const T* qb = qc + nb * 32 * kRow / static_cast<int>(sizeof(T));
-      const T* db_ = dc + nb * 32 * kRow / static_cast<int>(sizeof(T));
-      const float* lb = lc + nb * 32;
-      const float* eb = ec + nb * 32;
+      const uint32_t row_off = static_cast<uint32_t>(nb * 32 * kRow);
+      const uint32_t qtr[2] = {q_tr[0] + row_off, q_tr[1] + row_off};
+      const uint32_t dtr[2] = {d_tr[0] + row_off, d_tr[1] + row_off};
+      const uint32_t lb = w_st + static_cast<uint32_t>(nb * 32 * 4);
+      const uint32_t eb = lb + 1024;
       f32x16 s[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRow, 1, true>(qb, kf, li, lh, s);
+      addr_rows_x_regs<T, D, kRow, 1>(q_plain + row_off, kf, s);
       // Dense and padded rows past the sequence carry LSE * log2(e) = +inf
       // (and delta 0) in the workspace and zero Q and dO rows, so their
       // weights are exactly 0 unmasked; keys past it feed only the lane's own
@@ -508,7 +593,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = q0 + 8 * g4 + 4 * lh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 8 * g4 + 4 * lh);
+        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(
+            lb + static_cast<uint32_t>((8 * g4 + 4 * lh) * 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -521,39 +607,35 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
           w[0][r >> 3][r & 7] = static_cast<T>(p);
         }
       }
-      tile_tr_x_frags<T, kRow, 1, DB, true>(db_, w, lane, dv);
+      addr_tr_x_frags<T, kRow, 1, DB>(dtr, w, dv);
       f32x16 dpp[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRow, 1, true>(db_, vf, li, lh, dpp);
+      addr_rows_x_regs<T, D, kRow, 1>(d_plain + row_off, vf, dpp);
       frag ws[1][2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(eb + 8 * g4 + 4 * lh);
+        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(
+            eb + static_cast<uint32_t>((8 * g4 + 4 * lh) * 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           ws[0][r >> 3][r & 7] = static_cast<T>(pr[r] * (dpp[0][r] - d4[e]));
         }
       }
-      tile_tr_x_frags<T, kRow, 1, DB, true>(qb, ws, lane, dk);
+      addr_tr_x_frags<T, kRow, 1, DB>(qtr, ws, dk);
       interleave_reads<2 * (D / 16) + 4 * DB, 2 * (D / 16) + 8 * DB>();
     }
   };
 
   if (n_tiles > 0) {
-    issue(0, q_lds0, d_lds0, l_lds0, e_lds0);
+    issue(0, 0);
     wait_vmem();
     barrier_lds();
-    for (int t = 0;; t += 2) {
-      issue(t + 1, q_lds1, d_lds1, l_lds1, e_lds1);
-      compute(t, q_lds0, d_lds0, l_lds0, e_lds0);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int st = t & 1;
+      if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
+      compute(t, st);
       wait_vmem();
       barrier_lds();
-      if (t + 1 >= n_tiles) break;
-      issue(t + 2, q_lds0, d_lds0, l_lds0, e_lds0);
-      compute(t + 1, q_lds1, d_lds1, l_lds1, e_lds1);
-      wait_vmem();
-      barrier_lds();
-      if (t + 2 >= n_tiles) break;
     }
   }
 
