@@ -422,11 +422,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV: one workgroup per 128 keys of one (batch, head); 4 waves of 32
 // keys; query tiles of 64 rows (Q and dO) stream through two LDS stages.
-// With D = 128 the wave's K and V rows and both accumulators take more than
-// half a SIMD's registers: one wave per SIMD.
+// Two waves per SIMD: at D = 128 the wave's K and V rows and both
+// accumulators take most of its 256 registers (the causal and compact
+// kernels spill a few; still faster than one wave per SIMD).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int MODE, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = kBwdDkvKeys / 32;
   constexpr int BQ = 64;
   constexpr int NB = BQ / 32;
