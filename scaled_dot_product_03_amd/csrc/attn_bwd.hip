@@ -37,21 +37,14 @@
 namespace sdpa03 {
 namespace {
 
-// Tiles read both as 16-row MFMA operands and transposed.  In the dK/dV
-// kernel (Q and dO) they are unpadded and chunk-swizzled (swizzle_of<D>,
-// conflict-free for both reads).  No padding serves both reads: D * 2 + 80,
-// used for K in the dQ kernel, keeps the plain reads clean, but the 4 rows
-// of a transposing pass then overlap in the bank cycle (a 2-way conflict on
-// part of every such pass).  The dQ kernel runs two waves per SIMD and has no
-// registers left for the swizzle's per-lane offsets.
+// LDS tiles are unpadded (rows of exactly D * 2 bytes) and chunk-swizzled
+// (swizzle_of<D>): conflict-free both for 16-row MFMA operand reads and for
+// transposing reads, which no row padding achieves (D * 2 + 80, say, keeps
+// the plain reads clean but makes every transposing pass of 4 rows overlap
+// itself in the bank cycle).  Unpadded rows also make a tile a power of two
+// in size, which the XOR-addressed stages need.
 template <int D>
 constexpr int swizzled_row_bytes() { return D * 2; }
-template <int D>
-constexpr int padded_dual_row_bytes() { return D * 2 + 80; }
-// Tiles read only as 16-row MFMA operands: 16 bytes of padding shift
-// consecutive rows by one 16-byte bank group.
-template <int D>
-constexpr int plain_row_bytes() { return D * 2 + 16; }
 
 template <typename T>
 using frag_t = typename Mma16<T>::frag;
@@ -72,84 +65,29 @@ __device__ __forceinline__ void interleave_reads() {
   }
 }
 
-// c[nb] += A B for nb < NB.  A: rows 32 nb .. 32 nb + 31 of an LDS tile with
-// row stride ROW bytes, 16 dims per k-step (lane (rho, h) reads the 16 bytes
-// at dims 16 ks + 8 h -- chunk 2 ks + h -- of row 32 nb + rho; SWZ: a
-// swizzled tile, that chunk stored at (2 ks + h) ^ swizzle_of<D>(rho), one
-// XOR per k-step).  B: the wave's own rows, one fragment per k-step, in
-// registers.
-template <typename T, int D, int ROW, int NB, bool SWZ>
-__device__ __forceinline__ void tile_rows_x_regs(const T* tile, const frag_t<T> (&b)[D / 16],
-                                                 int li, int lh, f32x16 (&c)[NB]) {
-  const char* base = reinterpret_cast<const char*>(tile) + li * ROW;
-  const int x = SWZ ? ((lh ^ swizzle_of<D>(li)) << 4) : (lh << 4);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const int off = SWZ ? (x ^ (ks * 32)) : (x + ks * 32);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const frag_t<T> a = *reinterpret_cast<const frag_t<T>*>(base + nb * 32 * ROW + off);
-      c[nb] = Mma16<T>::mma(a, b[ks], c[nb]);
-    }
-  }
-}
-
-// acc[db] += X^T W.  X: an LDS tile of NB * 32 rows (row stride ROW bytes)
-// read transposed; W: the rounded fragments of NB 32-row accumulators over
-// those rows, register r of lane (i, h) holding row 8 (r / 4) + 4 h + r % 4.
+// The two products on an LDS tile (swizzled, rows of ROW = D * 2 bytes),
+// addressed by LDS byte address.  The tile's stage base is aligned to twice
+// the stage size, so the lane's chunk bits join its base by XOR and the row
+// offsets stay immediates.
+//
+// addr_rows_x_regs: c[nb] += A B for nb < NB.  A: rows 32 nb .. 32 nb + 31
+// of the tile, 16 dims per k-step (lane (rho, h) reads the 16 bytes at dims
+// 16 ks + 8 h -- chunk 2 ks + h, stored at (2 ks + h) ^ swizzle_of<D>(rho));
+// lane_addr is the lane's address for ks = 0.  B: the wave's own rows, one
+// fragment per k-step, in registers.
+//
+// addr_tr_x_frags: acc[db] += X^T W.  X: the tile's NB * 32 rows read
+// transposed; W: the rounded fragments of NB 32-row accumulators over those
+// rows, register r of lane (i, h) holding row 8 (r / 4) + 4 h + r % 4, so
 // k-step (nb, half) -- registers 8 half .. 8 half + 7 -- covers rows
 // 32 nb + 16 half + {4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3}.  Within each
 // group of 16 lanes, ds_read_b64_tr_b16 gives lane i element (i & 3) of the
 // 64-bit words read by lanes 4 j + (i >> 2); with lane t pointing at row
 // R0 + t / 4, column C0 + 4 (t & 3), lane i receives X[R0 + j][C0 + i] for
-// j = 0..3.  Two reads (R0 = 32 nb + 16 half + 4 h and R0 + 8) give the eight
-// rows of one operand.  SWZ: a swizzled tile; the byte column
-// 2 C0 + 8 (t & 3) + 64 db (below 64 before the db term) has its chunk bits
-// XORed with swizzle_of<D> of the row, which modulo 16 depends only on sub
-// and the lane: one XOR per (sub, db).
-template <typename T, int ROW, int NB, int DB, bool SWZ>
-__device__ __forceinline__ void tile_tr_x_frags(const T* tile, const frag_t<T> (&w)[NB][2],
-                                                int lane, f32x16 (&acc)[DB]) {
-  using s16x4 = short __attribute__((ext_vector_type(4)));
-  constexpr int D = DB * 32;
-  const int t = lane & 15;
-  const int grp = lane >> 4;
-  const int row_lane = (grp >> 1) * 4 + (t >> 2);
-  const int col_lane = (grp & 1) * 16 + 4 * (t & 3);
-  const char* base = reinterpret_cast<const char*>(tile) + row_lane * ROW;
-  int z[2];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    z[sub] = SWZ ? ((col_lane * 2) ^ (swizzle_of<D>(sub * 8 + row_lane) << 4)) : col_lane * 2;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        s16x4 x[2];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const int col = SWZ ? (z[sub] ^ (db * 64)) : (z[sub] + db * 64);
-          const char* src = base + (nb * 32 + half * 16 + sub * 8) * ROW + col;
-          x[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(src));
-        }
-        frag_t<T> xf;
-        __builtin_memcpy(&xf, x, sizeof(xf));
-        acc[db] = Mma16<T>::mma(xf, w[nb][half], acc[db]);
-      }
-    }
-  }
-}
-
-// The same two products on a swizzled tile addressed by LDS byte address:
-// lane_addr is the address of the lane's chunk 0 (its row, chunk h ^ swizzle
-// for the plain read; its row and column, XOR the swizzle, for the
-// transposing one) in a tile whose base is aligned to twice its size, so the
-// k-step's and the D block's chunk bits join by XOR and the row offsets stay
-// immediates.
+// j = 0..3.  Two reads (sub = 0, 1: R0 = 32 nb + 16 half + 4 h and R0 + 8)
+// give the eight rows of one operand.  lane_addr[sub] is the address of the
+// lane's row and column (its chunk bits XORed with the swizzle of the row,
+// which modulo 16 depends only on sub and the lane) for nb = half = db = 0.
 template <typename T>
 __device__ __forceinline__ frag_t<T> lds_frag(uint32_t addr) {
   return *(const __attribute__((address_space(3))) frag_t<T>*)(addr);
@@ -285,15 +223,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
-  constexpr int kRowK = padded_dual_row_bytes<D>();
-  constexpr int kRowV = plain_row_bytes<D>();
-  using KCopy = TileCopy<T, D, BN, NW, kRowK>;
-  using VCopy = TileCopy<T, D, BN, NW, kRowV>;
+  // K (read plainly and transposed) and V (read plainly) tiles, both
+  // unpadded and swizzled; two stages of each in one array, a power-of-two
+  // stage apart (XOR-addressed stages, one loop body, untracked copies: as
+  // in the dK/dV kernel).
+  constexpr int kRow = swizzled_row_bytes<D>();
+  using KCopy = TileCopy<T, D, BN, NW, kRow, true>;
   using frag = frag_t<T>;
-  __shared__ __attribute__((aligned(1024))) T k_lds0[KCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) T k_lds1[KCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) T v_lds0[VCopy::kArrayBytes / 2];
-  __shared__ __attribute__((aligned(1024))) T v_lds1[VCopy::kArrayBytes / 2];
+  constexpr int kStage = KCopy::kArrayBytes;
+  static_assert(kStage == BN * kRow && (kStage & (kStage - 1)) == 0, "power-of-two stages");
+  __shared__ __attribute__((aligned(2 * kStage))) T k_lds[kStage];  // 2 stages of kStage bytes
+  __shared__ __attribute__((aligned(2 * kStage))) T v_lds[kStage];
 
   // Under the causal mask the last query tiles cost the most: they go first.
   const uint32_t n = blockIdx.x;
@@ -353,40 +293,61 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const int n_tiles = (kend + BN - 1) / BN;
 
   KCopy kcopy;
-  VCopy vcopy;
+  KCopy vcopy;
   kcopy.init(wave, lane, k_row_bytes);
   vcopy.init(wave, lane, v_row_bytes);
-  auto issue = [&](int t, T* kb, T* vb) {
+  auto issue = [&](int t, int st) {
     const int j0 = t * BN;
-    const int rows = t < n_tiles ? kend - j0 : 0;
-    kcopy.issue(kp + j0 * k_row_bytes, rows, k_row_bytes, kb, wave);
-    vcopy.issue(vp + j0 * v_row_bytes, rows, v_row_bytes, vb, wave);
+    kcopy.issue_untracked(kp + j0 * k_row_bytes, kend - j0, k_row_bytes, k_lds + st * (kStage / 2),
+                          wave);
+    vcopy.issue_untracked(vp + j0 * v_row_bytes, kend - j0, v_row_bytes, v_lds + st * (kStage / 2),
+                          wave);
   };
+
+  // Per-lane LDS addresses in stage 0 (see the dK/dV kernel).
+  const uint32_t k_base = (uint32_t)(uintptr_t)(lds_void_ptr)(k_lds);
+  const uint32_t v_base = (uint32_t)(uintptr_t)(lds_void_ptr)(v_lds);
+  const uint32_t plain_off = li * kRow + ((lh ^ swizzle_of<D>(li)) << 4);
+  uint32_t tr_off[2];
+  {
+    const int tt = lane & 15;
+    const int grp = lane >> 4;
+    const int row_lane = (grp >> 1) * 4 + (tt >> 2);
+    const int col_lane = (grp & 1) * 16 + 4 * (tt & 3);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      tr_off[sub] = row_lane * kRow + ((col_lane * 2) ^ (swizzle_of<D>(sub * 8 + row_lane) << 4));
+    }
+  }
 
   // Tile t, one 32-key block at a time (it keeps the live softmax state to
   // one block): scores, weights, dP, dS, then dQ^T += K^T dS^T.
-  auto compute = [&](int t, const T* kc, const T* vc) {
+  auto compute = [&](int t, int st) {
+    const uint32_t so = static_cast<uint32_t>(st * kStage);
+    const uint32_t k_plain = (k_base + plain_off) ^ so;
+    const uint32_t v_plain = (v_base + plain_off) ^ so;
+    const uint32_t k_tr[2] = {(k_base + tr_off[0]) ^ so, (k_base + tr_off[1]) ^ so};
 #pragma nounroll
     for (int nb = 0; nb < NB; ++nb) {
       const int j0 = t * BN + nb * 32;
-      const T* kb = kc + nb * 32 * kRowK / static_cast<int>(sizeof(T));
-      const T* vb = vc + nb * 32 * kRowV / static_cast<int>(sizeof(T));
-      f32x16 st[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRowK, 1, false>(kb, qf, li, lh, st);
+      const uint32_t row_off = static_cast<uint32_t>(nb * 32 * kRow);
+      f32x16 st_[1] = {f32x16{}};
+      addr_rows_x_regs<T, D, kRow, 1>(k_plain + row_off, qf, st_);
       f32x16 dpt[1] = {f32x16{}};
-      tile_rows_x_regs<T, D, kRowV, 1, false>(vb, df, li, lh, dpt);
+      addr_rows_x_regs<T, D, kRow, 1>(v_plain + row_off, df, dpt);
       const bool need_mask = (j0 + 32 > sr.len_k) || (CAUSAL && j0 + 31 > row0);
       frag w[1][2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(st[0][r], c2, -lse2));
+        float p = __builtin_amdgcn_exp2f(fmaf(st_[0][r], c2, -lse2));
         if (need_mask) {
           const int key = j0 + 8 * (r >> 2) + 4 * lh + (r & 3);
           if (!(key < sr.len_k && (!CAUSAL || key <= qi))) p = 0.f;
         }
         w[0][r >> 3][r & 7] = static_cast<T>(p * (dpt[0][r] - delta));
       }
-      tile_tr_x_frags<T, kRowK, 1, DB, false>(kb, w, lane, acc);
+      const uint32_t ktr[2] = {k_tr[0] + row_off, k_tr[1] + row_off};
+      addr_tr_x_frags<T, kRow, 1, DB>(ktr, w, acc);
       // S^T and dP^T: 2 * D/16 products over as many reads; dQ: 2 * DB
       // products over 4 * DB transposing reads.
       interleave_reads<2 * (D / 16) + 2 * DB, 2 * (D / 16) + 4 * DB>();
@@ -394,22 +355,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   };
 
   if (n_tiles > 0) {
-    issue(0, k_lds0, v_lds0);
+    issue(0, 0);
     wait_vmem();
     barrier_lds();
-    // Step t computes tile t from one buffer while tile t + 1 loads into the
+    // Step t computes tile t from one stage while tile t + 1 loads into the
     // other (free: its last readers passed the barrier ending step t - 1).
-    for (int t = 0;; t += 2) {
-      issue(t + 1, k_lds1, v_lds1);
-      compute(t, k_lds0, v_lds0);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int st = t & 1;
+      if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
+      compute(t, st);
       wait_vmem();
       barrier_lds();
-      if (t + 1 >= n_tiles) break;
-      issue(t + 2, k_lds0, v_lds0);
-      compute(t + 1, k_lds1, v_lds1);
-      wait_vmem();
-      barrier_lds();
-      if (t + 2 >= n_tiles) break;
     }
   }
 
