@@ -16,6 +16,17 @@ using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
 using f16x8 = _Float16 __attribute__((ext_vector_type(8)));
 using lds_void_ptr = __attribute__((address_space(3))) void*;
 
+// The LDS byte address of a workgroup-shared array, and a typed read at an
+// LDS byte address.
+template <typename E>
+__device__ __forceinline__ uint32_t lds_addr(const E* p) {
+  return (uint32_t)(uintptr_t)(lds_void_ptr)(const_cast<E*>(p));
+}
+template <typename V>
+__device__ __forceinline__ V lds_load(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) V*)(addr);
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -132,6 +143,7 @@ __host__ __device__ constexpr int swizzle_of(int r) {
 template <typename T, int D, int BN, int NW, int ROW, bool SWIZZLE = false>
 struct TileCopy {
   static_assert(!SWIZZLE || (sizeof(T) == 2 && ROW == D * 2), "swizzled tiles: 16-bit, unpadded");
+  static_assert(!SWIZZLE || D == 64 || D == 128, "swizzle_of covers head_dim 64 and 128");
   static constexpr int kDataBytes = D * static_cast<int>(sizeof(T));  // payload per row
   static constexpr int kBlocks = (BN * ROW + 1023) / 1024;
   static constexpr int kInstPerWave = (kBlocks + NW - 1) / NW;

@@ -2,8 +2,9 @@
 // and their typed launchers, included by attn_fwd.hip (dispatch, split
 // forward) and attn_fwd_{bf16,f16,f32}.hip (one element type each).
 //
-// One workgroup computes block_m = 32 * waves query rows of one
-// (batch or sequence, head); each wavefront owns 32 rows.  The workgroup
+// One workgroup computes block_m = 32 * waves * row_blocks query rows of one
+// (batch or sequence, head); each wavefront owns 32 rows (one row block) or
+// 64 (two).  The workgroup
 // walks the key axis in tiles of block_n keys.  K and V tiles go from HBM
 // straight into LDS with buffer loads (two or three LDS stages, no register
 // staging, rows past the sequence read back as zeros).  Every wave keeps its
@@ -25,12 +26,17 @@
 // B operand directly.  Accumulator register r of lane l holds key
 // 8*(r/4) + 4*(l/32) + r%4 of its 32-key block.
 //
-// LDS layout.  Tiles are row-major [key][dim] with padded rows, chosen for
-// gfx950's 64 banks of 4 bytes: the 16 consecutive K rows that one 128-bit
-// fragment read touches land in 16 distinct 16-byte bank groups, and the 4
-// V rows of one transposing read land in 4 distinct 64-byte bank blocks.
-// Padding (not an XOR swizzle) keeps every fragment address "one per-lane
-// base + an immediate offset", which saves dozens of address registers.
+// LDS layout.  Tiles are row-major [key][dim].  16-bit tiles of head dim
+// 128 are unpadded and XOR-swizzled: the 16-byte chunk c of row r sits at chunk
+// c ^ swizzle_of<D>(r) (attn_common.h), which keeps both the 128-bit K reads
+// (one chunk of 16 consecutive rows per pass) and the transposing V reads
+// (a 64-byte block of 4 rows per pass) free of bank conflicts on gfx950's 64
+// banks of 4 bytes, while a tile takes exactly BN * D * 2 bytes.  A lane's
+// chunk offsets then differ by XOR, not by a constant, so each lane keeps
+// its address for every K k-step and V dim block in registers (stage 0),
+// and the stage and row offsets ride in the instructions' immediates.
+// Head dim 64 and fp32 tiles use padded rows instead (k_lds_row_bytes
+// below), which measured faster at head dim 64.
 //
 // Software pipeline.  Step t turns the scores of tile t into probabilities
 // (VALU) while the matrix cores compute the scores of tile t+1, then
@@ -53,8 +59,8 @@ namespace sdpa03 {
 // rescale.
 constexpr float kSumLimit = 4096.0f;
 
-// LDS row strides (bytes) of K and V tiles for element size ES and head
-// dim D.  K: 16 bytes of padding per row shifts consecutive rows by one
+// LDS row strides (bytes) of padded K and V tiles for element size ES and
+// head dim D.  K: 16 bytes of padding per row shifts consecutive rows by one
 // 16-byte bank group.  V (16-bit): 64 bytes shift consecutive rows by a
 // quarter of the 256-byte bank cycle.  V (fp32): 32 bytes put rows r and
 // r+4, which one fp32 read pairs, in opposite halves of the banks.
@@ -84,24 +90,85 @@ struct Path16 {
     }
   }
 
-  static constexpr int kRowK = k_lds_row_bytes<2, D>();
-  static constexpr int kRowV = v_lds_row_bytes<2, D>();
+  // Head dim 128: swizzled, unpadded tiles (rows of D * 2 bytes).  Head dim
+  // 64: padded rows (k_lds_row_bytes / v_lds_row_bytes), where every
+  // fragment is one per-lane base plus an immediate.
+  static constexpr bool kSwizzle = (D == 128);
+  static constexpr int kRowK = kSwizzle ? D * 2 : k_lds_row_bytes<2, D>();
+  static constexpr int kRowV = kSwizzle ? D * 2 : v_lds_row_bytes<2, D>();
+  template <int BN, int NW>
+  using KCopy = TileCopy<T, D, BN, NW, kRowK, kSwizzle>;
+  template <int BN, int NW>
+  using VCopy = TileCopy<T, D, BN, NW, kRowV, kSwizzle>;
 
-  // A operand of k-step ks: lane (rho, h) reads K[32nb + rho][16ks + 8h ..+8]
-  // -- rho is the lane's li, so the address is a per-lane base plus an
-  // immediate.
-  template <int NB>
-  __device__ static __forceinline__ void qk(const T* k_tile, const QRegs& q, int li, int lh,
-                                            f32x16 (&s)[NB]) {
-    const char* base = reinterpret_cast<const char*>(k_tile) + li * kRowK + lh * 16;
+  // Per-lane LDS byte addresses in stage 0 of the K and V arrays.
+  //  k[ks]: the K fragment of k-step ks for key block 0 -- lane (rho, h)
+  //    reads chunk 2 ks + h of row rho (stored at (2 ks + h) ^ swizzle(rho)
+  //    in a swizzled tile); key block nb adds nb * 32 rows (the swizzle
+  //    repeats every 16 rows).
+  //  v[sub][db]: transposing read `sub` of dim block db for k-step
+  //    (nb, half) = (0, 0) -- see pv(); later k-steps add whole 16-row groups.
+  // The array bases are 1024-aligned and the row offsets are multiples of
+  // the row size, so the chunk bits join them by XOR.  In a padded tile
+  // the entries differ by constants, which the compiler folds into the
+  // instructions' offsets.
+  struct Lanes {
+    uint32_t k[kQFrags];
+    uint32_t v[2][D / 32];
+  };
+  __device__ static __forceinline__ Lanes lanes(uint32_t k_base, uint32_t v_base, int lane) {
+    Lanes L;
+    const int li = lane & 31;
+    const int lh = lane >> 5;
+    const int t = lane & 15;
+    const int grp = lane >> 4;
+    const int row_lane = (grp >> 1) * 4 + (t >> 2);
+    const int col_bytes = (grp & 1) * 32 + 8 * (t & 3);
+    if constexpr (kSwizzle) {
+      const uint32_t kl = k_base + li * kRowK + ((lh ^ swizzle_of<D>(li)) << 4);
+#pragma unroll
+      for (int ks = 0; ks < kQFrags; ++ks) L.k[ks] = kl ^ static_cast<uint32_t>(ks << 5);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int r = sub * 8 + row_lane;
+        const uint32_t vl = v_base + r * kRowV + (col_bytes ^ (swizzle_of<D>(r) << 4));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) L.v[sub][db] = vl ^ static_cast<uint32_t>(db << 6);
+      }
+    } else {
+      const uint32_t kl = k_base + li * kRowK + lh * 16;
+#pragma unroll
+      for (int ks = 0; ks < kQFrags; ++ks) L.k[ks] = kl + ks * 32;
+      const uint32_t vl = v_base + row_lane * kRowV + col_bytes;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) L.v[sub][db] = vl + sub * 8 * kRowV + db * 64;
+      }
+    }
+    return L;
+  }
+
+  // S^T += K Q^T over one tile whose K stage starts `k_off` bytes into the
+  // array, for RB row blocks (each K fragment read once, used RB times).  A
+  // operand of k-step ks: lane (rho, h) holds K[32nb + rho][16ks + 8h ..+8].
+  template <int NB, int RB>
+  __device__ static __forceinline__ void qk(const Lanes& L, uint32_t k_off, const QRegs (&q)[RB],
+                                            f32x16 (&s)[RB][NB]) {
 #pragma unroll
     for (int ks = 0; ks < kQFrags; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const frag a = *reinterpret_cast<const frag*>(base + nb * 32 * kRowK + ks * 32);
-        s[nb] = Mma16<T>::mma(a, q.f[ks], s[nb]);
+        const frag a = lds_load<frag>(L.k[ks] + k_off + nb * 32 * kRowK);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][nb] = Mma16<T>::mma(a, q[rb].f[ks], s[rb][nb]);
       }
     }
+  }
+  template <int NB>
+  __device__ static __forceinline__ void qk(const Lanes& L, uint32_t k_off, const QRegs& q,
+                                            f32x16 (&s)[NB]) {
+    qk<NB, 1>(L, k_off, reinterpret_cast<const QRegs(&)[1]>(q), reinterpret_cast<f32x16(&)[1][NB]>(s));
   }
 
   // An empty asm statement that takes the P fragments as operands: the
@@ -118,28 +185,28 @@ struct Path16 {
 
   // Scheduling requests for the two pipeline phases (sched_group_barrier
   // masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU).  Phase A: keep a few K
-  // fragment reads ahead, then one MFMA, one read and a share of the softmax
-  // VALU work.  Phase B: two transposing V reads and a little VALU per MFMA.
-  template <int NB>
+  // fragment reads ahead, then per MFMA a share of the softmax VALU work and
+  // one read per RB MFMAs.  Phase B: two transposing V reads per RB MFMAs.
+  template <int NB, int RB = 1>
   __device__ static __forceinline__ void interleave_qk() {
-    constexpr int n_mfma = NB * kQFrags;
-    constexpr int valu_per = (NB * 16 * 3 + n_mfma - 1) / n_mfma;
+    constexpr int n_mfma = RB * NB * kQFrags;
+    constexpr int valu_per = (RB * NB * 16 * 3 + n_mfma - 1) / n_mfma;
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
     for (int i = 0; i < n_mfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i % RB == RB - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, valu_per, 0);
     }
   }
-  template <int NB, int DB>
+  template <int NB, int DB, int RB = 1>
   __device__ static __forceinline__ void interleave_pv() {
-    constexpr int n_mfma = NB * 2 * DB;
+    constexpr int n_mfma = RB * NB * 2 * DB;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < n_mfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i % RB == RB - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
 
@@ -191,15 +258,11 @@ struct Path16 {
   // R0 + t/4, column C0 + 4(t & 3), lane i therefore receives V[R0 + j][C0 + i]
   // for j = 0..3: four consecutive keys of its own column.  Two such reads
   // (R0 = 32nb + 16half + 4h and R0 + 8) give the eight keys of one operand.
-  template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const T* v_tile, const PRegs<NB>& p, int lane,
-                                            f32x16 (&acc)[DB]) {
+  // The V stage starts `v_off` bytes into the array.
+  template <int NB, int DB, int RB>
+  __device__ static __forceinline__ void pv(const Lanes& L, uint32_t v_off, const PRegs<NB> (&p)[RB],
+                                            f32x16 (&acc)[RB][DB]) {
     using s16x4 = short __attribute__((ext_vector_type(4)));
-    const int t = lane & 15;
-    const int grp = lane >> 4;
-    const int row_lane = (grp >> 1) * 4 + (t >> 2);
-    const int col_lane = (grp & 1) * 16 + 4 * (t & 3);
-    const char* base = reinterpret_cast<const char*>(v_tile) + row_lane * kRowV + col_lane * 2;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -209,16 +272,25 @@ struct Path16 {
           s16x4 w[2];
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            const char* src = base + (nb * 32 + half * 16 + sub * 8) * kRowV + db * 64;
+            const uint32_t src = L.v[sub][db] + v_off + (nb * 32 + half * 16) * kRowV;
             w[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(src));
           }
           frag vf;
           __builtin_memcpy(&vf, w, sizeof(vf));
-          acc[db] = Mma16<T>::mma(vf, p.f[nb][half], acc[db]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc[rb][db] = Mma16<T>::mma(vf, p[rb].f[nb][half], acc[rb][db]);
+          }
         }
       }
     }
+  }
+  template <int NB, int DB>
+  __device__ static __forceinline__ void pv(const Lanes& L, uint32_t v_off, const PRegs<NB>& p,
+                                            f32x16 (&acc)[DB]) {
+    pv<NB, DB, 1>(L, v_off, reinterpret_cast<const PRegs<NB>(&)[1]>(p),
+                  reinterpret_cast<f32x16(&)[1][DB]>(acc));
   }
 };
 
@@ -242,21 +314,40 @@ struct Path32 {
     }
   }
 
+  static constexpr bool kSwizzle = false;
   static constexpr int kRowK = k_lds_row_bytes<4, D>();
   static constexpr int kRowV = v_lds_row_bytes<4, D>();
+  template <int BN, int NW>
+  using KCopy = TileCopy<float, D, BN, NW, kRowK>;
+  template <int BN, int NW>
+  using VCopy = TileCopy<float, D, BN, NW, kRowV>;
 
-  template <int NB>
-  __device__ static __forceinline__ void qk(const float* k_tile, const QRegs& q, int li, int lh,
-                                            f32x16 (&s)[NB]) {
-    const char* base = reinterpret_cast<const char*>(k_tile) + li * kRowK + lh * 16;
+  // Per-lane LDS byte addresses in stage 0: K row li at dims 4h.., V rows
+  // 4h.. at column li; every fragment is one of these plus an immediate.
+  struct Lanes {
+    uint32_t k;
+    uint32_t v;
+  };
+  __device__ static __forceinline__ Lanes lanes(uint32_t k_base, uint32_t v_base, int lane) {
+    const int li = lane & 31;
+    const int lh = lane >> 5;
+    return Lanes{k_base + li * kRowK + lh * 16, v_base + lh * 4 * kRowV + li * 4};
+  }
+
+  template <int NB, int RB>
+  __device__ static __forceinline__ void qk(const Lanes& L, uint32_t k_off, const QRegs (&q)[RB],
+                                            f32x16 (&s)[RB][NB]) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(base + nb * 32 * kRowK + g * 32);
+        const f32x4 a = lds_load<f32x4>(L.k + k_off + nb * 32 * kRowK + g * 32);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q.f[g][e], s[nb], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            s[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q[rb].f[g][e], s[rb][nb], 0, 0, 0);
+          }
         }
       }
     }
@@ -266,9 +357,9 @@ struct Path32 {
   __device__ static __forceinline__ void pin(PRegs<NB>&) {}
 
   // fp32 is a correctness path: no scheduling requests.
-  template <int NB>
+  template <int NB, int RB = 1>
   __device__ static __forceinline__ void interleave_qk() {}
-  template <int NB, int DB>
+  template <int NB, int DB, int RB = 1>
   __device__ static __forceinline__ void interleave_pv() {}
 
   template <int NB>
@@ -290,21 +381,21 @@ struct Path32 {
 
   // O^T += V^T P^T with one key per k-step: lane (i, h) supplies p[nb][r]
   // (key 32nb + 8(r/4) + 4h + r%4) and V at that key in column 32db + i.
-  template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const float* v_tile, const PRegs<NB>& p, int lane,
-                                            f32x16 (&acc)[DB]) {
-    const int li = lane & 31;
-    const int lh = lane >> 5;
-    const char* base = reinterpret_cast<const char*>(v_tile) + lh * 4 * kRowV + li * 4;
+  template <int NB, int DB, int RB>
+  __device__ static __forceinline__ void pv(const Lanes& L, uint32_t v_off, const PRegs<NB> (&p)[RB],
+                                            f32x16 (&acc)[RB][DB]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const char* vrow = base + (nb * 32 + 8 * (r >> 2) + (r & 3)) * kRowV;
+        const uint32_t vrow = L.v + v_off + (nb * 32 + 8 * (r >> 2) + (r & 3)) * kRowV;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const float vv = *reinterpret_cast<const float*>(vrow + db * 128);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p.f[nb][r], acc[db], 0, 0, 0);
+          const float vv = lds_load<float>(vrow + db * 128);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p[rb].f[nb][r], acc[rb][db], 0, 0, 0);
+          }
         }
       }
     }
@@ -437,9 +528,24 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 // The kernel
 // ---------------------------------------------------------------------------
 
-// STAGES LDS buffers each for K and V tiles (2 or 3).  With 3, a tile load
-// issued at step t is first needed at step t+2, so it has two steps of
-// compute to hide its latency behind.
+// A compile-time LDS stage index (the step bodies are unrolled by stage, so
+// every stage offset is an instruction immediate).
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
+
+// STAGES LDS stages each for K and V tiles (2 to 4), one array per operand,
+// tile t in stage t % STAGES.  With S stages a tile load issued at step t is
+// first needed at step t + S - 1, so it has S - 1 steps of compute to hide
+// its latency behind.  The copies are untracked by the compiler (it cannot
+// tell the stage being filled from the ones being read within one array);
+// each wave waits for its own with explicit vmcnt counts before the step's
+// barrier.
+// RB: row blocks of 32 query rows per wave (1 or 2).  With two, every K and V
+// fragment read from LDS feeds two products, halving the LDS reads per
+// matrix-core operation (the transposing V reads are the slow ones); the
+// wave's registers double, so such a kernel runs one wave per SIMD.
 // SPLIT: key-parallel dense forward.  The workgroup covers the key tiles of
 // its split only and writes a normalised fp32 partial output and its
 // logsumexp to the workspace; a second kernel merges the splits.
@@ -448,22 +554,25 @@ __device__ __forceinline__ SeqRange seq_range(const FwdArgs& a, int z) {
 // P.V, so the loads have the whole step to land; the scores then hold
 // scale * q.k + bias (natural-log units) and the softmax multiplies by
 // log2(e) alone.
-template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
+template <typename T, int D, int NW, int RB, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
           bool BIAS>
-__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_lds1, T* k_lds2,
-                                              T* v_lds0, T* v_lds1, T* v_lds2) {
-  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_lds) {
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+  static_assert(RB == 1 || RB == 2, "one or two row blocks per wave");
   static_assert(!SPLIT || MODE == MODE_DENSE, "the split forward serves the dense mode");
   static_assert(!(SPLIT && BIAS), "the split forward has no bias");
   using Path = typename PathFor<T, D>::type;
-  using KCopy = TileCopy<T, D, BN, NW, Path::kRowK>;
-  using VCopy = TileCopy<T, D, BN, NW, Path::kRowV>;
+  using KCopy = typename Path::template KCopy<BN, NW>;
+  using VCopy = typename Path::template VCopy<BN, NW>;
   using PRegs = typename Path::template PRegs<BN / 32>;
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * 32 * RB;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
-  // Loads one step issues per wave; with three stages they may still be in
-  // flight when the step ends.
+  constexpr int kKStage = KCopy::kArrayBytes;  // bytes per stage
+  constexpr int kVStage = VCopy::kArrayBytes;
+  // Loads one step issues per wave; those of the last STAGES - 2 steps may
+  // still be in flight when a step ends (the next step reads K(t+2) and
+  // V(t+1), issued STAGES - 2 steps before this one ends).
   constexpr int kLoadsPerStep = KCopy::kInstPerWave + VCopy::kInstPerWave;
   constexpr int kInFlightAtStepEnd = (STAGES - 2) * kLoadsPerStep;
 
@@ -491,9 +600,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
           static_cast<int64_t>(sr.q_start) * a.o_ss;
   float* lsep = a.lse + sr.b * a.lse_sb + h * a.lse_sh + sr.q_start;
 
-  const int row0 = m0 + wave * 32;  // first query row of this wave
-  const int qi = row0 + li;         // this lane's query row
-  const bool row_ok = qi < sr.len_q;
+  const int row0 = m0 + wave * 32 * RB;  // first query row of this wave
+  int qi[RB];                            // this lane's query row in each block
+  bool row_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    qi[rb] = row0 + 32 * rb + li;
+    row_ok[rb] = qi[rb] < sr.len_q;
+  }
 
   int kend = sr.len_k;
   if constexpr (CAUSAL) kend = min(kend, min(m0 + BM, sr.len_q));
@@ -512,61 +626,79 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   VCopy vcopy;
   kcopy.init(wave, lane, k_row_bytes);
   vcopy.init(wave, lane, v_row_bytes);
-  // Tile t lives in buffer t % STAGES.  Every call below names its buffers
-  // directly (the loop is unrolled by STAGES), so after inlining each LDS
-  // access refers to a known array.  Rows at or past `end` are not fetched
-  // (they read back as zeros); a load past the last tile fetches nothing.
-  auto issue_k = [&](int t, T* buf, int end) {
+  // Rows at or past `end` are not fetched (they read back as zeros); a load
+  // past the last tile fetches nothing.
+  auto issue_k = [&](int t, int stage, int end) {
     const int j0 = (tile0 + t) * BN;
-    kcopy.issue(kp + j0 * k_row_bytes, end - j0, k_row_bytes, buf, wave);
+    kcopy.issue_untracked(kp + j0 * k_row_bytes, end - j0, k_row_bytes,
+                          k_lds + stage * (kKStage / static_cast<int>(sizeof(T))), wave);
   };
-  auto issue_v = [&](int t, T* buf, int end) {
+  auto issue_v = [&](int t, int stage, int end) {
     const int j0 = (tile0 + t) * BN;
-    vcopy.issue(vp + j0 * v_row_bytes, end - j0, v_row_bytes, buf, wave);
+    vcopy.issue_untracked(vp + j0 * v_row_bytes, end - j0, v_row_bytes,
+                          v_lds + stage * (kVStage / static_cast<int>(sizeof(T))), wave);
   };
+  const typename Path::Lanes lanes = Path::lanes(lds_addr(k_lds), lds_addr(v_lds), lane);
 
-  typename Path::QRegs qr;
-  Path::load_q(qp + static_cast<int64_t>(qi) * a.q_ss, row_ok, lh, qr);
-
-  f32x16 acc[DB];
+  typename Path::QRegs qr[RB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;  // reference (stale) max of scale*log2(e)*s, this row
-  float l_run = 0.f;      // running sum of this half-wave's weights
+  for (int rb = 0; rb < RB; ++rb) {
+    Path::load_q(qp + static_cast<int64_t>(qi[rb]) * a.q_ss, row_ok[rb], lh, qr[rb]);
+  }
+
+  f32x16 acc[RB][DB];
+  float m_run[RB];  // reference (stale) max of scale*log2(e)*s, per row
+  float l_run[RB];  // running sum of this half-wave's weights, per row
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x16{};
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+  }
   const float c2 = BIAS ? kLog2e : a.scale_log2;
 
-  // This lane's bias row (the sequence's block of the bias view).  Vector
+  // This lane's bias rows (the sequence's block of the bias view).  Vector
   // loads need the block to start on a 4-element boundary; the strides are
   // multiples of 4 elements, so only the key offset decides.
   using Bias = BiasTile<T, NB>;
-  const T* bias_row = nullptr;
+  const T* bias_row[RB] = {};
   bool bias_vec = false;
   if constexpr (BIAS) {
-    bias_row = static_cast<const T*>(a.bias) + sr.b * a.bias_sb + h * a.bias_sh +
-               (static_cast<int64_t>(sr.q_start) + qi) * a.bias_sq + sr.k_start;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      bias_row[rb] = static_cast<const T*>(a.bias) + sr.b * a.bias_sb + h * a.bias_sh +
+                     (static_cast<int64_t>(sr.q_start) + qi[rb]) * a.bias_sq + sr.k_start;
+    }
     bias_vec = (sr.k_start & 3) == 0;
   }
-  auto load_bias = [&](int t, Bias& bt) {
-    if (row_ok) {
-      bt.load(bias_row, (tile0 + t) * BN, sr.len_k, lh, bias_vec);
-    } else {
-      bt.zero();
+  auto load_bias = [&](int t, Bias (&bt)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (row_ok[rb]) {
+        bt[rb].load(bias_row[rb], (tile0 + t) * BN, sr.len_k, lh, bias_vec);
+      } else {
+        bt[rb].zero();
+      }
     }
   };
 
   // Masks the scores of tile t where keys run past the sequence or, under
   // the causal mask, past the lane's row (only tail and diagonal tiles).
-  auto mask_tile = [&](int t, f32x16 (&s)[NB]) {
+  auto mask_tile = [&](int t, f32x16 (&s)[RB][NB]) {
     const int j0 = (tile0 + t) * BN;
-    const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0);
-    if (need_mask) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0 + 32 * rb);
+      if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + nb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const bool ok = key < sr.len_k && (!CAUSAL || key <= qi);
-          if (!ok) s[nb][r] = kNegInf;
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + nb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const bool ok = key < sr.len_k && (!CAUSAL || key <= qi[rb]);
+            if (!ok) s[rb][nb][r] = kNegInf;
+          }
         }
       }
     }
@@ -582,46 +714,56 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
     }
     return max_across_halves(mx) * c2;
   };
-  // Probabilities of score tile s against the running reference m_run,
-  // into p; returns this lane's share of the tile's row sum.  The reference
-  // only has to keep every p bounded, not to equal the row max: while a
-  // tile's sums stay <= 2^12 (so every p <= 2^12) nothing else is done.
-  // Otherwise -- and on the first tile a row sees -- the exact row max is
-  // taken, acc and l are rescaled to it, and p is recomputed (p <= 1).  The
-  // result is unchanged: O = acc / l and LSE = m + log2 l for any m.
-  auto probabilities = [&](const f32x16 (&s)[NB], PRegs& p) {
-    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
-    float tile_sum = Path::template softmax_p<NB>(s, c2, m_sub, p);
-    const bool redo = !(tile_sum <= kSumLimit) || m_run == kNegInf;
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-      const float m_new = fmaxf(m_run, tile_max(s));
-      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+  // Probabilities of a score tile against the running reference, into p;
+  // returns this lane's share of the tile's row sum.  The reference only has
+  // to keep every p bounded, not to equal the row max: while a tile's sums
+  // stay <= 2^12 (so every p <= 2^12) nothing else is done.  Otherwise -- and
+  // on the first tile a row sees -- the exact row max is taken, acc and l are
+  // rescaled to it, and p is recomputed (p <= 1).  The result is unchanged:
+  // O = acc / l and LSE = m + log2 l for any m.  The check is wave-uniform
+  // per row block.
+  auto first_pass = [&](int rb, const f32x16 (&s)[NB], PRegs& p) {
+    return Path::template softmax_p<NB>(s, c2, (m_run[rb] == kNegInf) ? 0.f : m_run[rb], p);
+  };
+  auto settle = [&](int rb, const f32x16 (&s)[NB], PRegs& p, float tile_sum) {
+    const bool redo = !(tile_sum <= kSumLimit) || m_run[rb] == kNegInf;
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {  // rare
+      const float m_new = fmaxf(m_run[rb], tile_max(s));
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+      l_run[rb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      m_run = m_new;
-      tile_sum = Path::template softmax_p<NB>(s, c2, (m_run == kNegInf) ? 0.f : m_run, p);
+      for (int db = 0; db < DB; ++db) acc[rb][db] *= alpha;
+      m_run[rb] = m_new;
+      tile_sum = first_pass(rb, s, p);
     }
-    return tile_sum;
+    l_run[rb] += tile_sum;
   };
 
-  f32x16 s[NB];
-  Bias bias_next;
+  f32x16 s[RB][NB];
+  Bias bias_next[RB];
   if (n_tiles > 0) {
+    // K(0), then K(i) and V(i-1) for i < STAGES: the order the step-end
+    // waits count on.  (The full wait also settles Q's loads, which are the
+    // compiler's.)
     if constexpr (BIAS) load_bias(0, bias_next);
-    issue_k(0, k_lds0, kend);
-    issue_k(1, k_lds1, 1 < n_tiles ? kend : 0);
-    issue_v(0, v_lds0, kend);
-    if constexpr (STAGES > 2) {
-      issue_k(2, k_lds2, 2 < n_tiles ? kend : 0);
-      issue_v(1, v_lds1, 1 < n_tiles ? kend : 0);
+    issue_k(0, 0, kend);
+#pragma unroll
+    for (int i = 1; i < STAGES; ++i) {
+      issue_k(i, i, i < n_tiles ? kend : 0);
+      issue_v(i - 1, i - 1, i - 1 < n_tiles ? kend : 0);
     }
     wait_vmem();
     barrier_lds();
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-    Path::template qk<NB>(k_lds0, qr, li, lh, s);
-    if constexpr (BIAS) bias_next.fold(s, a.scale);
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[rb][nb] = f32x16{};
+    }
+    Path::template qk<NB, RB>(lanes, 0, qr, s);
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bias_next[rb].fold(s[rb], a.scale);
+    }
     mask_tile(0, s);
     barrier_lds();  // every wave is done with K(0) before K(STAGES) replaces it
   }
@@ -632,134 +774,149 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
   // and meets every barrier, but skips the products and the softmax (a
   // wave-uniform branch).  The result is unchanged: the skipped weights are
   // exactly 0 and a tile without weights never triggers a rescale.  With
-  // 256-row workgroups this removes 12 of the 32 wave-tiles of each diagonal
-  // block.
-  auto wave_done = [&](int t) { return CAUSAL && (tile0 + t) * BN > row0 + 31; };
+  // 256-row workgroups of 32-row waves this removes 12 of the 32 wave-tiles
+  // of each diagonal block.
+  auto wave_done = [&](int t) { return CAUSAL && (tile0 + t) * BN > row0 + 32 * RB - 1; };
 
-  // Pipeline step for tile t when tile t+1 exists.  k_cur holds K(t) (done
-  // with; K(t+STAGES) is loaded into it), k_nxt holds K(t+1), v_cur holds V(t)
-  // and v_pre receives V(t+STAGES-1).  Phase A is straight-line code, so the
-  // scheduler can interleave the softmax VALU work with the next tile's
-  // score MFMAs.
-  auto step = [&](int t, T* k_cur, T* k_nxt, T* v_cur, T* v_pre) {
-    // The next tile's bias goes out before the tile copies, so waiting for it
-    // never waits for them (also when this wave skips the tile: a
-    // conditional load would keep two copies of the bias registers alive).
+  // Pipeline step for tile t (in stage ST = t % STAGES) when tile t+1 exists.
+  // K(t)'s stage is done with and receives K(t+STAGES); K(t+1) is in the next
+  // stage; V(t) is in stage ST and V(t-1)'s stage receives V(t+STAGES-1).
+  // Phase A is straight-line code, so the scheduler can interleave the
+  // softmax VALU work with the next tile's score MFMAs.
+  auto step = [&](int t, auto stage) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr uint32_t k_nxt = ((ST + 1) % STAGES) * kKStage;
+    constexpr uint32_t v_cur = ST * kVStage;
+    // The next tile's bias is loaded first (also when this wave skips the
+    // tile: a conditional load would keep two copies of the bias registers
+    // alive).
     if constexpr (BIAS) load_bias(t + 1, bias_next);
-    issue_k(t + STAGES, k_cur, t + STAGES < n_tiles ? kend : 0);
-    issue_v(t + STAGES - 1, v_pre, t + STAGES - 1 < n_tiles ? kend : 0);
+    // The tile copies into K(t)'s and V(t-1)'s stages (their last readers
+    // passed the previous barrier).  They are inline assembly, which inside
+    // the products' scheduling region makes the compiler drop the interleave
+    // that interleave_qk / interleave_pv request: a scheduling barrier closes
+    // their region.  The compiler does not count these copies, so its wait
+    // for the bias also waits for them.
+    issue_k(t + STAGES, ST, t + STAGES < n_tiles ? kend : 0);
+    issue_v(t + STAGES - 1, (ST + STAGES - 1) % STAGES, t + STAGES - 1 < n_tiles ? kend : 0);
+    __builtin_amdgcn_sched_barrier(0);
     if (!wave_done(t)) {
 
     // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
-    PRegs p;
-    f32x16 s_next[NB];
+    PRegs p[RB];
+    f32x16 s_next[RB][NB];
+    float tile_sum[RB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s_next[nb] = f32x16{};
-    const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
-    float tile_sum = Path::template softmax_p<NB>(s, c2, m_sub, p);
-    Path::template qk<NB>(k_nxt, qr, li, lh, s_next);
-    Path::pin(p);  // P is computed here, beside the MFMAs, not after the branch
-    Path::template interleave_qk<NB>();
-    const bool redo = !(tile_sum <= kSumLimit) || m_run == kNegInf;
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {  // rare: see probabilities()
-      const float m_new = fmaxf(m_run, tile_max(s));
-      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      m_run = m_new;
-      tile_sum = Path::template softmax_p<NB>(s, c2, (m_run == kNegInf) ? 0.f : m_run, p);
+      for (int nb = 0; nb < NB; ++nb) s_next[rb][nb] = f32x16{};
+      tile_sum[rb] = first_pass(rb, s[rb], p[rb]);
     }
-    l_run += tile_sum;
+    Path::template qk<NB, RB>(lanes, k_nxt, qr, s_next);
+    // P is computed here, beside the MFMAs, not after the branches
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) Path::pin(p[rb]);
+    Path::template interleave_qk<NB, RB>();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) settle(rb, s[rb], p[rb], tile_sum[rb]);
     if constexpr (!BIAS) mask_tile(t + 1, s_next);
 
     // Phase B: O += P(t) V(t) on the matrix cores.
-    Path::template pv<NB, DB>(v_cur, p, lane, acc);
-    Path::template interleave_pv<NB, DB>();
+    Path::template pv<NB, DB, RB>(lanes, v_cur, p, acc);
+    Path::template interleave_pv<NB, DB, RB>();
     if constexpr (BIAS) {
-      bias_next.fold(s_next, a.scale);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bias_next[rb].fold(s_next[rb], a.scale);
       mask_tile(t + 1, s_next);
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[rb][nb] = s_next[rb][nb];
+    }
     }  // !wave_done(t)
 
-    // K(t+2) and V(t+1) -- issued one step earlier with three stages, in
-    // this step with two -- must have landed before the next step.
+    // K(t+2) and V(t+1) -- issued STAGES - 2 steps before this one -- must
+    // have landed before the next step.
     wait_vmem_allow<kInFlightAtStepEnd>();
     barrier_lds();
   };
-  // The last tile: probabilities and P.V only.
-  auto last_step = [&](const T* v_cur) {
-    if (wave_done(n_tiles - 1)) return;
-    PRegs p;
-    l_run += probabilities(s, p);
-    Path::template pv<NB, DB>(v_cur, p, lane, acc);
+  // The last tile: probabilities and P.V only.  It issues no loads, but
+  // the zero-row copies of earlier steps may still be in flight: every
+  // wave settles its own before leaving.
+  auto last_step = [&](uint32_t v_cur) {
+    if (!wave_done(n_tiles - 1)) {
+      PRegs p[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) settle(rb, s[rb], p[rb], first_pass(rb, s[rb], p[rb]));
+      Path::template pv<NB, DB, RB>(lanes, v_cur, p, acc);
+    }
+    wait_vmem();
   };
 
-  // Each step body exists once (unrolled by STAGES so that every step names
-  // its buffers at compile time); the loop leaves as soon as the next tile
-  // would be the last one, and the last tile's V buffer is picked at run time
-  // (the last step issues no loads, so nothing can be in flight into it).
+  // Each step body exists once per stage (unrolled by STAGES so that every
+  // step's stage offsets are constants); the loop leaves as soon as the next
+  // tile would be the last one, and the last tile's V stage is picked at run
+  // time.
   if (n_tiles > 0) {
     for (int t = 0;; t += STAGES) {
       if (t + 1 >= n_tiles) break;
-      step(t, k_lds0, k_lds1, v_lds0, STAGES == 2 ? v_lds1 : v_lds2);
+      step(t, Stage<0>{});
       if (t + 2 >= n_tiles) break;
-      if constexpr (STAGES == 2) {
-        step(t + 1, k_lds1, k_lds0, v_lds1, v_lds0);
-      } else {
-        step(t + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+      step(t + 1, Stage<1>{});
+      if constexpr (STAGES > 2) {
         if (t + 3 >= n_tiles) break;
-        step(t + 2, k_lds2, k_lds0, v_lds2, v_lds1);
+        step(t + 2, Stage<2>{});
+      }
+      if constexpr (STAGES > 3) {
+        if (t + 4 >= n_tiles) break;
+        step(t + 3, Stage<3>{});
       }
     }
-    const int last = (n_tiles - 1) % STAGES;
-    last_step(last == 0 ? v_lds0 : (last == 1 ? v_lds1 : v_lds2));
+    last_step(static_cast<uint32_t>((n_tiles - 1) % STAGES) * kVStage);
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
-  const float l_tot = sum_across_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if constexpr (SPLIT) {
-    if (row_ok) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = sum_across_halves(l_run[rb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_run[rb] + log2f(l_tot)) * kLn2 : kNegInf;
+    if (!row_ok[rb]) continue;
+    if constexpr (SPLIT) {
       const int64_t row = (static_cast<int64_t>(split) * a.num_z + z) * a.num_heads * sr.len_q +
-                          static_cast<int64_t>(h) * sr.len_q + qi;
+                          static_cast<int64_t>(h) * sr.len_q + qi[rb];
       float* wrow = a.ws_o + row * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const f32x16& o = acc[rb][db];
           *reinterpret_cast<f32x4*>(wrow + db * 32 + g * 8 + lh * 4) =
-              f32x4{acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
-                    acc[db][4 * g + 3] * inv};
+              f32x4{o[4 * g] * inv, o[4 * g + 1] * inv, o[4 * g + 2] * inv, o[4 * g + 3] * inv};
         }
       }
-      if (lh == 0) a.ws_lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
-    }
-    return;
-  }
-  if (row_ok) {
-    T* orow = op + static_cast<int64_t>(qi) * a.o_ss;
+      if (lh == 0) a.ws_lse[row] = lse;
+    } else {
+      T* orow = op + static_cast<int64_t>(qi[rb]) * a.o_ss;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        T out4[4];
+        for (int g = 0; g < 4; ++g) {
+          T out4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out4[e] = static_cast<T>(acc[db][4 * g + e] * inv);
-        T* dst = orow + db * 32 + g * 8 + lh * 4;
-        if constexpr (sizeof(T) == 4) {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{out4[0], out4[1], out4[2], out4[3]};
-        } else {
-          uint2 packed;
-          __builtin_memcpy(&packed, out4, 8);
-          *reinterpret_cast<uint2*>(dst) = packed;
+          for (int e = 0; e < 4; ++e) out4[e] = static_cast<T>(acc[rb][db][4 * g + e] * inv);
+          T* dst = orow + db * 32 + g * 8 + lh * 4;
+          if constexpr (sizeof(T) == 4) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{out4[0], out4[1], out4[2], out4[3]};
+          } else {
+            uint2 packed;
+            __builtin_memcpy(&packed, out4, 8);
+            *reinterpret_cast<uint2*>(dst) = packed;
+          }
         }
       }
-    }
-    if (lh == 0) {
-      lsep[qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+      if (lh == 0) lsep[qi[rb]] = lse;
     }
   }
 }
@@ -778,24 +935,24 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds0, T* k_
 // With global interval j (group 0 runs its local interval u at j = u, group
 // 1 at j = u + 1; u = 0 is the first tile's scores, then S(n) at u = 2n+1
 // and C(n) at u = 2n+2), K(n) is read at j = 2n and 2n+1, V(n) at j = 2n+2
-// and 2n+3.  Tiles rotate through STAGES buffers (tile n in buffer
+// and 2n+3.  Tiles rotate through STAGES stages (tile n in stage
 // n % STAGES).  At the start of C(n) each wave issues its share of K(n +
-// STAGES) into K(n)'s buffer and of V(n + STAGES - 1) into V(n - 1)'s: the
+// STAGES) into K(n)'s stage and of V(n + STAGES - 1) into V(n - 1)'s: the
 // last readers of both finished by global interval 2n+1, and C(n) starts at
 // j >= 2n+2.  At the end of C(n) each wave waits until only the loads it
 // issued in the last STAGES - 2 C intervals are in flight, so a tile issued
 // in C(n) has landed after C(n + STAGES - 2) -- before its first reader at
 // j = 2(n + STAGES) (K) or 2(n + STAGES - 1) + 2 (V).
 template <typename T, int D, int BN, int STAGES, int MODE, bool CAUSAL>
-__device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_lds0, T* k_lds1,
-                                                       T* k_lds2, T* v_lds0, T* v_lds1,
-                                                       T* v_lds2) {
+__device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_lds, T* v_lds) {
   static_assert(sizeof(T) == 2, "the ping-pong schedule serves 16-bit inputs");
-  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
   constexpr int NW = 8;
   using Path = Path16<T, D>;
-  using KCopy = TileCopy<T, D, BN, NW, Path::kRowK>;
-  using VCopy = TileCopy<T, D, BN, NW, Path::kRowV>;
+  using KCopy = typename Path::template KCopy<BN, NW>;
+  using VCopy = typename Path::template VCopy<BN, NW>;
+  constexpr int kKStage = KCopy::kArrayBytes;
+  constexpr int kVStage = VCopy::kArrayBytes;
   using PRegs = typename Path::template PRegs<BN / 32>;
   constexpr int BM = NW * 32;
   constexpr int NB = BN / 32;
@@ -842,16 +999,17 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
   VCopy vcopy;
   kcopy.init(wave, lane, k_row_bytes);
   vcopy.init(wave, lane, v_row_bytes);
-  auto issue_k = [&](int t, T* buf) {
+  auto issue_k = [&](int t, int stage) {
     const int j0 = t * BN;
-    kcopy.issue_untracked(kp + j0 * k_row_bytes, t < n_tiles ? kend - j0 : 0, k_row_bytes, buf,
-                          wave);
+    kcopy.issue_untracked(kp + j0 * k_row_bytes, t < n_tiles ? kend - j0 : 0, k_row_bytes,
+                          k_lds + stage * (kKStage / 2), wave);
   };
-  auto issue_v = [&](int t, T* buf) {
+  auto issue_v = [&](int t, int stage) {
     const int j0 = t * BN;
-    vcopy.issue_untracked(vp + j0 * v_row_bytes, t < n_tiles ? kend - j0 : 0, v_row_bytes, buf,
-                          wave);
+    vcopy.issue_untracked(vp + j0 * v_row_bytes, t < n_tiles ? kend - j0 : 0, v_row_bytes,
+                          v_lds + stage * (kVStage / 2), wave);
   };
+  const typename Path::Lanes lanes = Path::lanes(lds_addr(k_lds), lds_addr(v_lds), lane);
 
   typename Path::QRegs qr;
   Path::load_q(qp + static_cast<int64_t>(qi) * a.q_ss, row_ok, lh, qr);
@@ -911,21 +1069,20 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
     // K(i) and V(i-1), i < STAGES, stay in flight behind the first scores.
     // (Q's loads are the compiler's: the full wait settles them before any
     // untracked tile load is issued.)
-    issue_k(0, k_lds0);
+    issue_k(0, 0);
     wait_vmem();
     barrier_lds();
-    issue_k(1, k_lds1);
-    issue_v(0, v_lds0);
-    if constexpr (STAGES > 2) {
-      issue_k(2, k_lds2);
-      issue_v(1, v_lds1);
+#pragma unroll
+    for (int i = 1; i < STAGES; ++i) {
+      issue_k(i, i);
+      issue_v(i - 1, i - 1);
     }
     if (group == 1) barrier_lds();  // group 1 sits out global interval 0
 
     // u = 0: scores of tile 0.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-    Path::template qk<NB>(k_lds0, qr, li, lh, s);
+    Path::template qk<NB>(lanes, 0, qr, s);
     wait_vmem_allow<kInFlight>();  // K(1) and V(0) have landed
     barrier_lds();
 
@@ -935,20 +1092,21 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
       l_run += probabilities(s, p);
       barrier_lds();
     };
-    // C(n) for n + 1 < n_tiles.  k_cur: K(n)'s buffer (receives K(n+STAGES));
-    // k_nxt: K(n+1); v_cur: V(n); v_pre: receives V(n+STAGES-1).
-    // The loads are issued unconditionally (tiles past the end fetch zero
-    // rows into buffers nobody reads again): a branch around them would make
-    // the compiler lose track of which buffer each load writes and wait for
-    // all of them before the first fragment read.
-    auto c_interval = [&](int n, T* k_cur, T* k_nxt, T* v_cur, T* v_pre) {
-      issue_k(n + STAGES, k_cur);
-      issue_v(n + STAGES - 1, v_pre);
+    // C(n) for n + 1 < n_tiles, tile n in stage ST.  K(n)'s stage receives
+    // K(n+STAGES), K(n+1) is in the next stage, V(n) in stage ST, and V(n-1)'s
+    // stage receives V(n+STAGES-1).  The loads are issued unconditionally
+    // (tiles past the end fetch zero rows into stages nobody reads again), so
+    // every wave issues the same count the waits rely on.
+    auto c_interval = [&](int n, auto stage) {
+      constexpr int ST = decltype(stage)::value;
+      issue_k(n + STAGES, ST);
+      issue_v(n + STAGES - 1, (ST + STAGES - 1) % STAGES);
+      __builtin_amdgcn_sched_barrier(0);  // keep the inline-asm copies out of the products' region
       f32x16 s_next[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s_next[nb] = f32x16{};
-      Path::template qk<NB>(k_nxt, qr, li, lh, s_next);
-      Path::template pv<NB, DB>(v_cur, p, lane, acc);
+      Path::template qk<NB>(lanes, ((ST + 1) % STAGES) * kKStage, qr, s_next);
+      Path::template pv<NB, DB>(lanes, ST * kVStage, p, acc);
       Path::template interleave_c<NB, DB>();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
@@ -959,25 +1117,27 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
     for (int n = 0;; n += STAGES) {
       if (n + 1 >= n_tiles) break;
       s_interval(n);
-      c_interval(n, k_lds0, k_lds1, v_lds0, STAGES == 2 ? v_lds1 : v_lds2);
+      c_interval(n, Stage<0>{});
       if (n + 2 >= n_tiles) break;
       s_interval(n + 1);
-      if constexpr (STAGES == 2) {
-        c_interval(n + 1, k_lds1, k_lds0, v_lds1, v_lds0);
-      } else {
-        c_interval(n + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+      c_interval(n + 1, Stage<1>{});
+      if constexpr (STAGES > 2) {
         if (n + 3 >= n_tiles) break;
         s_interval(n + 2);
-        c_interval(n + 2, k_lds2, k_lds0, v_lds2, v_lds1);
+        c_interval(n + 2, Stage<2>{});
+      }
+      if constexpr (STAGES > 3) {
+        if (n + 4 >= n_tiles) break;
+        s_interval(n + 3);
+        c_interval(n + 3, Stage<3>{});
       }
     }
     // Last tile: S(T-1), then C(T-1) = P.V only.  Group 1's last interval is
     // the workgroup's last, so it ends without a barrier (every wave passes
     // the same number of barriers).
     s_interval(n_tiles - 1);
-    const int last = (n_tiles - 1) % STAGES;
-    const T* v_last = last == 0 ? v_lds0 : (last == 1 ? v_lds1 : v_lds2);
-    Path::template pv<NB, DB>(v_last, p, lane, acc);
+    Path::template pv<NB, DB>(lanes, static_cast<uint32_t>((n_tiles - 1) % STAGES) * kVStage, p,
+                              acc);
     wait_vmem();
     if (group == 0) barrier_lds();
   }
@@ -1005,50 +1165,29 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
   }
 }
 
+// The kernels declare one LDS array per operand holding all STAGES stages.
 template <typename T, int D, int BN, int STAGES, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_fwd_pingpong_kernel(FwdArgs a) {
   using Path = Path16<T, D>;
-  constexpr int kKElems = TileCopy<T, D, BN, 8, Path::kRowK>::kArrayBytes / 2;
-  constexpr int kVElems = TileCopy<T, D, BN, 8, Path::kRowV>::kArrayBytes / 2;
-  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
-  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
-  if constexpr (STAGES > 2) {
-    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
-    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
-    attn_fwd_pingpong_body<T, D, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds2, v_lds0,
-                                                           v_lds1, v_lds2);
-  } else {
-    attn_fwd_pingpong_body<T, D, BN, STAGES, MODE, CAUSAL>(a, k_lds0, k_lds1, k_lds0, v_lds0,
-                                                           v_lds1, v_lds0);
-  }
+  constexpr int kKElems = STAGES * Path::template KCopy<BN, 8>::kArrayBytes / 2;
+  constexpr int kVElems = STAGES * Path::template VCopy<BN, 8>::kArrayBytes / 2;
+  __shared__ __attribute__((aligned(1024))) T k_lds[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds[kVElems];
+  attn_fwd_pingpong_body<T, D, BN, STAGES, MODE, CAUSAL>(a, k_lds, v_lds);
 }
 
-// The kernel: declares the LDS buffers its stage count needs and runs the
-// body.  Separate LDS arrays per buffer (not one [STAGES][...] array): each
-// gets its own alias scope, so the compiler can see that fragment reads of
-// one buffer do not depend on the buffer loads still landing in another,
-// and need not wait for them.
-template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
+// Two waves per SIMD with one row block per wave (at most 256 registers
+// each); one wave per SIMD with two (up to 512).
+template <typename T, int D, int NW, int RB, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
           bool BIAS>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, RB == 2 ? 1 : 2) void attn_fwd_kernel(FwdArgs a) {
   using Path = typename PathFor<T, D>::type;
-  constexpr int kKElems = TileCopy<T, D, BN, NW, Path::kRowK>::kArrayBytes / static_cast<int>(sizeof(T));
-  constexpr int kVElems = TileCopy<T, D, BN, NW, Path::kRowV>::kArrayBytes / static_cast<int>(sizeof(T));
-  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
-  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
-  if constexpr (STAGES > 2) {
-    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
-    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
-    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(a, k_lds0, k_lds1, k_lds2,
-                                                                   v_lds0, v_lds1, v_lds2);
-  } else {
-    attn_fwd_body<T, D, NW, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(a, k_lds0, k_lds1, k_lds0,
-                                                                   v_lds0, v_lds1, v_lds0);
-  }
+  constexpr int kES = static_cast<int>(sizeof(T));
+  constexpr int kKElems = STAGES * Path::template KCopy<BN, NW>::kArrayBytes / kES;
+  constexpr int kVElems = STAGES * Path::template VCopy<BN, NW>::kArrayBytes / kES;
+  __shared__ __attribute__((aligned(1024))) T k_lds[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds[kVElems];
+  attn_fwd_body<T, D, NW, RB, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(a, k_lds, v_lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1113,14 +1252,14 @@ template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
 int launch_bucket(const FwdArgs& a, hipStream_t stream) {
   constexpr TableEntry e = launch_entry<T, D, BUCKET, BIAS>();
   const uint32_t grid = static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z;
-  if constexpr (e.pingpong != 0) {
+  if constexpr (e.schedule == kSchedPingPong) {
     static_assert(e.waves == 8 && sizeof(T) == 2, "ping-pong: 8 waves, 16-bit inputs");
     hipLaunchKernelGGL((attn_fwd_pingpong_kernel<T, D, e.block_n, e.stages, MODE, CAUSAL>),
                        dim3(grid), dim3(512), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(
-        (attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL, false, BIAS>),
-        dim3(grid), dim3(e.waves * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, row_blocks(e), e.block_n, e.stages, MODE,
+                                        CAUSAL, false, BIAS>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
   }
   return static_cast<int>(hipGetLastError());
 }
@@ -1146,7 +1285,8 @@ int launch_split_bucket(const FwdArgs& a, const MergeArgs& mg, hipStream_t strea
   constexpr TableEntry e = launch_entry<T, D, BUCKET, true>();
   const uint32_t grid =
       static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z * static_cast<uint32_t>(a.num_splits);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, e.block_n, e.stages, MODE_DENSE, CAUSAL, true, false>),
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, row_blocks(e), e.block_n, e.stages, MODE_DENSE,
+                                      CAUSAL, true, false>),
                      dim3(grid), dim3(e.waves * 64), 0, stream, a);
   int err = static_cast<int>(hipGetLastError());
   if (err != 0) return err;

@@ -6,10 +6,12 @@ longer), as
 AOTriton's tuning database probes sequence lengths, head dim and dtype
 (AOTriton issue #12, the maintainer's replies).  For every class (dtype,
 head_dim) a set of candidate kernel shapes (waves per workgroup, keys per
-tile, LDS stages, schedule: 0 single group, 1 ping-pong of two wave groups)
+tile, LDS stages, schedule: 0 single group, 1 ping-pong of two wave groups,
+2 single group with two 32-row blocks per wave)
 is compiled into its own build of libsdpa03.so, the shape applied to every
 bucket of the class.  A candidate counts only if its build has no register
-spills, keeps two waves per SIMD, and then passes the GPU parity tests
+spills, keeps the occupancy its schedule is built for (two waves per SIMD;
+one for two row blocks per wave), and then passes the GPU parity tests
 (tests/test_gpu_parity.py, run against that build): the same page warns that
 a kernel built with some configurations runs but gives wrong results.  Only
 then is it timed, on workloads of every bucket.  Per bucket, the passing
@@ -39,12 +41,14 @@ RESULTS = os.path.join(SWEEP_DIR, "results.json")
 TABLE = os.path.join(CSRC, "dispatch_table.inc")
 DTYPE_CODES = {"fp32": 0, "fp16": 1, "bf16": 2}
 
-# Candidate (waves, block_n, stages, pingpong) per class.
+# Candidate (waves, block_n, stages, schedule) per class; schedule 0 single
+# group, 1 ping-pong, 2 single group with two 32-row blocks per wave.
 CANDIDATES = {
     ("bf16", 128): [(2, 32, 2, 0), (4, 32, 2, 0), (4, 64, 2, 0), (4, 32, 3, 0), (8, 64, 2, 0),
-                    (8, 64, 3, 0), (8, 32, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1)],
-    ("fp16", 64): [(2, 32, 2, 0), (4, 32, 2, 0), (4, 64, 2, 0), (4, 64, 3, 0), (4, 32, 3, 0),
-                   (8, 64, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1)],
+                    (8, 64, 3, 0), (8, 64, 4, 0), (8, 32, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1),
+                    (4, 32, 3, 2)],
+    ("fp16", 64): [(2, 32, 2, 0), (4, 32, 2, 0), (4, 64, 2, 0), (4, 64, 3, 0), (4, 64, 4, 0),
+                   (4, 32, 3, 0), (8, 64, 3, 0), (8, 64, 3, 1), (8, 128, 2, 1), (4, 64, 3, 2)],
 }
 
 BUCKETS = ["q<=128,k<=512", "q<=128,k>512", "q<=512,k<=512", "q<=512,k>512",
@@ -84,8 +88,8 @@ def _cand4(cand):
 
 
 def _name(cls, cand):
-    w, n, st, pp = _cand4(cand)
-    return f"{cls[0]}_d{cls[1]}_w{w}_n{n}_s{st}" + ("_pp" if pp else "")
+    w, n, st, sched = _cand4(cand)
+    return f"{cls[0]}_d{cls[1]}_w{w}_n{n}_s{st}" + {0: "", 1: "_pp", 2: "_rb2"}[sched]
 
 
 def _lib_path(cls, cand):
@@ -102,9 +106,10 @@ def _resources(cls, cand):
            "-Rpass-analysis=kernel-resource-usage", *defs]
     out = subprocess.run(cmd, capture_output=True, text=True).stderr
     dt_tag = {"bf16": "DF16b", "fp16": "DF16_", "fp32": "f"}[cls[0]]
-    w, n, st, pp = _cand4(cand)
-    want = (f"attn_fwd_pingpong_kernelI{dt_tag}Li{cls[1]}ELi{n}ELi{st}E" if pp else
-            f"attn_fwd_kernelI{dt_tag}Li{cls[1]}ELi{w}ELi{n}ELi{st}E")
+    w, n, st, sched = _cand4(cand)
+    rb = 2 if sched == 2 else 1
+    want = (f"attn_fwd_pingpong_kernelI{dt_tag}Li{cls[1]}ELi{n}ELi{st}E" if sched == 1 else
+            f"attn_fwd_kernelI{dt_tag}Li{cls[1]}ELi{w}ELi{rb}ELi{n}ELi{st}E")
     vg, sp, occ, cur = 0, 0, 99, None
     for line in out.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
@@ -126,10 +131,10 @@ def _resources(cls, cand):
 
 
 def _defines(cls, cand):
-    w, n, st, pp = _cand4(cand)
+    w, n, st, sched = _cand4(cand)
     return [f"-DSDPA03_SWEEP_DTYPE={DTYPE_CODES[cls[0]]}", f"-DSDPA03_SWEEP_HEAD_DIM={cls[1]}",
             f"-DSDPA03_SWEEP_WAVES={w}", f"-DSDPA03_SWEEP_BLOCK_N={n}",
-            f"-DSDPA03_SWEEP_STAGES={st}", f"-DSDPA03_SWEEP_PINGPONG={pp}"]
+            f"-DSDPA03_SWEEP_STAGES={st}", f"-DSDPA03_SWEEP_SCHEDULE={sched}"]
 
 
 def build(only=None):
@@ -146,7 +151,7 @@ def build(only=None):
             if only and not any(o in _name(cls, cand) for o in only):
                 continue
             vg, sp, occ = _resources(cls, cand)
-            ok = sp == 0 and occ >= 2
+            ok = sp == 0 and occ >= (1 if _cand4(cand)[3] == 2 else 2)
             print(f"{_name(cls, cand):28s} vgpr={vg} spill={sp} waves/simd={occ} "
                   f"{'build' if ok else 'skip'}", flush=True)
             if ok:
@@ -275,8 +280,8 @@ def run(only=None):
 
 
 def _entry(cand):
-    w, n, st, pp = cand
-    return f"{{{w}, {n}, {st}, {pp}}}"
+    w, n, st, sched = cand
+    return f"{{{w}, {n}, {st}, {sched}}}"
 
 
 def write(results_path=RESULTS, table_path=TABLE):
@@ -315,7 +320,7 @@ def write(results_path=RESULTS, table_path=TABLE):
              "  // buckets: " + ", ".join(f"({b})" for b in BUCKETS)]
     for (dt, d, b), (score, cand) in sorted(best.items()):
         n_calls = sum(1 for k in fastest if k[:3] == (dt, d, b))
-        lines.append(f"  // {dt} d{d} bucket {b}: (waves, block_n, stages, pingpong) = {cand}; "
+        lines.append(f"  // {dt} d{d} bucket {b}: (waves, block_n, stages, schedule) = {cand}; "
                      f"score {score:.3f} over {n_calls} timed calls (1 per call is best)")
     lines += ["  if constexpr (sizeof(T) == 4) {", "    return TableEntry{4, 32, 2, 0};"]
     for dt in ("bf16", "fp16"):
