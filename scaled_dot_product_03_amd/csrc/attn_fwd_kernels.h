@@ -101,22 +101,22 @@ struct Path16 {
   template <int BN, int NW>
   using VCopy = TileCopy<T, D, BN, NW, kRowV, kSwizzle>;
 
-  // Per-lane LDS byte addresses in stage 0 of the K and V arrays.
+  // Per-lane byte offsets into a K and a V tile.
   //  k[ks]: the K fragment of k-step ks for key block 0 -- lane (rho, h)
   //    reads chunk 2 ks + h of row rho (stored at (2 ks + h) ^ swizzle(rho)
   //    in a swizzled tile); key block nb adds nb * 32 rows (the swizzle
   //    repeats every 16 rows).
   //  v[sub][db]: transposing read `sub` of dim block db for k-step
   //    (nb, half) = (0, 0) -- see pv(); later k-steps add whole 16-row groups.
-  // The array bases are 1024-aligned and the row offsets are multiples of
-  // the row size, so the chunk bits join them by XOR.  In a padded tile
-  // the entries differ by constants, which the compiler folds into the
-  // instructions' offsets.
+  // The row offsets are multiples of the row size, so the chunk bits join
+  // them by XOR; a tile's base (1024-aligned) and the block's row offset
+  // are added at the read and fold into the instruction's immediate.  In a
+  // padded tile the entries differ by constants, which fold the same way.
   struct Lanes {
     uint32_t k[kQFrags];
     uint32_t v[2][D / 32];
   };
-  __device__ static __forceinline__ Lanes lanes(uint32_t k_base, uint32_t v_base, int lane) {
+  __device__ static __forceinline__ Lanes lanes(int lane) {
     Lanes L;
     const int li = lane & 31;
     const int lh = lane >> 5;
@@ -125,21 +125,21 @@ struct Path16 {
     const int row_lane = (grp >> 1) * 4 + (t >> 2);
     const int col_bytes = (grp & 1) * 32 + 8 * (t & 3);
     if constexpr (kSwizzle) {
-      const uint32_t kl = k_base + li * kRowK + ((lh ^ swizzle_of<D>(li)) << 4);
+      const uint32_t kl = li * kRowK + ((lh ^ swizzle_of<D>(li)) << 4);
 #pragma unroll
       for (int ks = 0; ks < kQFrags; ++ks) L.k[ks] = kl ^ static_cast<uint32_t>(ks << 5);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int r = sub * 8 + row_lane;
-        const uint32_t vl = v_base + r * kRowV + (col_bytes ^ (swizzle_of<D>(r) << 4));
+        const uint32_t vl = r * kRowV + (col_bytes ^ (swizzle_of<D>(r) << 4));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) L.v[sub][db] = vl ^ static_cast<uint32_t>(db << 6);
       }
     } else {
-      const uint32_t kl = k_base + li * kRowK + lh * 16;
+      const uint32_t kl = li * kRowK + lh * 16;
 #pragma unroll
       for (int ks = 0; ks < kQFrags; ++ks) L.k[ks] = kl + ks * 32;
-      const uint32_t vl = v_base + row_lane * kRowV + col_bytes;
+      const uint32_t vl = row_lane * kRowV + col_bytes;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
@@ -149,26 +149,30 @@ struct Path16 {
     return L;
   }
 
-  // S^T += K Q^T over one tile whose K stage starts `k_off` bytes into the
-  // array, for RB row blocks (each K fragment read once, used RB times).  A
-  // operand of k-step ks: lane (rho, h) holds K[32nb + rho][16ks + 8h ..+8].
+  // S^T += K Q^T over the K tile at `k_tile`, for RB row blocks (each K
+  // fragment read once, used RB times).  A operand of k-step ks: lane
+  // (rho, h) holds K[32nb + rho][16ks + 8h ..+8].  The reads go through a
+  // pointer into the tile's own LDS array, so the compiler can tell them
+  // from tile copies into other arrays.
   template <int NB, int RB>
-  __device__ static __forceinline__ void qk(const Lanes& L, uint32_t k_off, const QRegs (&q)[RB],
+  __device__ static __forceinline__ void qk(const T* k_tile, const Lanes& L, const QRegs (&q)[RB],
                                             f32x16 (&s)[RB][NB]) {
+    const char* base = reinterpret_cast<const char*>(k_tile);
 #pragma unroll
     for (int ks = 0; ks < kQFrags; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const frag a = lds_load<frag>(L.k[ks] + k_off + nb * 32 * kRowK);
+        const frag a = *reinterpret_cast<const frag*>(base + L.k[ks] + nb * 32 * kRowK);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[rb][nb] = Mma16<T>::mma(a, q[rb].f[ks], s[rb][nb]);
       }
     }
   }
   template <int NB>
-  __device__ static __forceinline__ void qk(const Lanes& L, uint32_t k_off, const QRegs& q,
+  __device__ static __forceinline__ void qk(const T* k_tile, const Lanes& L, const QRegs& q,
                                             f32x16 (&s)[NB]) {
-    qk<NB, 1>(L, k_off, reinterpret_cast<const QRegs(&)[1]>(q), reinterpret_cast<f32x16(&)[1][NB]>(s));
+    qk<NB, 1>(k_tile, L, reinterpret_cast<const QRegs(&)[1]>(q),
+              reinterpret_cast<f32x16(&)[1][NB]>(s));
   }
 
   // An empty asm statement that takes the P fragments as operands: the
@@ -258,11 +262,11 @@ struct Path16 {
   // R0 + t/4, column C0 + 4(t & 3), lane i therefore receives V[R0 + j][C0 + i]
   // for j = 0..3: four consecutive keys of its own column.  Two such reads
   // (R0 = 32nb + 16half + 4h and R0 + 8) give the eight keys of one operand.
-  // The V stage starts `v_off` bytes into the array.
   template <int NB, int DB, int RB>
-  __device__ static __forceinline__ void pv(const Lanes& L, uint32_t v_off, const PRegs<NB> (&p)[RB],
+  __device__ static __forceinline__ void pv(const T* v_tile, const Lanes& L, const PRegs<NB> (&p)[RB],
                                             f32x16 (&acc)[RB][DB]) {
     using s16x4 = short __attribute__((ext_vector_type(4)));
+    const char* base = reinterpret_cast<const char*>(v_tile);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -272,9 +276,9 @@ struct Path16 {
           s16x4 w[2];
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            const uint32_t src = L.v[sub][db] + v_off + (nb * 32 + half * 16) * kRowV;
+            const char* src = base + L.v[sub][db] + (nb * 32 + half * 16) * kRowV;
             w[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(src));
+                (__attribute__((address_space(3))) s16x4*)(lds_void_ptr)(const_cast<char*>(src)));
           }
           frag vf;
           __builtin_memcpy(&vf, w, sizeof(vf));
@@ -287,9 +291,9 @@ struct Path16 {
     }
   }
   template <int NB, int DB>
-  __device__ static __forceinline__ void pv(const Lanes& L, uint32_t v_off, const PRegs<NB>& p,
+  __device__ static __forceinline__ void pv(const T* v_tile, const Lanes& L, const PRegs<NB>& p,
                                             f32x16 (&acc)[DB]) {
-    pv<NB, DB, 1>(L, v_off, reinterpret_cast<const PRegs<NB>(&)[1]>(p),
+    pv<NB, DB, 1>(v_tile, L, reinterpret_cast<const PRegs<NB>(&)[1]>(p),
                   reinterpret_cast<f32x16(&)[1][DB]>(acc));
   }
 };
@@ -322,26 +326,28 @@ struct Path32 {
   template <int BN, int NW>
   using VCopy = TileCopy<float, D, BN, NW, kRowV>;
 
-  // Per-lane LDS byte addresses in stage 0: K row li at dims 4h.., V rows
-  // 4h.. at column li; every fragment is one of these plus an immediate.
+  // Per-lane byte offsets into a tile: K row li at dims 4h.., V rows 4h..
+  // at column li; every fragment is one of these plus an immediate.
   struct Lanes {
     uint32_t k;
     uint32_t v;
   };
-  __device__ static __forceinline__ Lanes lanes(uint32_t k_base, uint32_t v_base, int lane) {
+  __device__ static __forceinline__ Lanes lanes(int lane) {
     const int li = lane & 31;
     const int lh = lane >> 5;
-    return Lanes{k_base + li * kRowK + lh * 16, v_base + lh * 4 * kRowV + li * 4};
+    return Lanes{static_cast<uint32_t>(li * kRowK + lh * 16),
+                 static_cast<uint32_t>(lh * 4 * kRowV + li * 4)};
   }
 
   template <int NB, int RB>
-  __device__ static __forceinline__ void qk(const Lanes& L, uint32_t k_off, const QRegs (&q)[RB],
-                                            f32x16 (&s)[RB][NB]) {
+  __device__ static __forceinline__ void qk(const float* k_tile, const Lanes& L,
+                                            const QRegs (&q)[RB], f32x16 (&s)[RB][NB]) {
+    const char* base = reinterpret_cast<const char*>(k_tile) + L.k;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const f32x4 a = lds_load<f32x4>(L.k + k_off + nb * 32 * kRowK + g * 32);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(base + nb * 32 * kRowK + g * 32);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
@@ -382,16 +388,17 @@ struct Path32 {
   // O^T += V^T P^T with one key per k-step: lane (i, h) supplies p[nb][r]
   // (key 32nb + 8(r/4) + 4h + r%4) and V at that key in column 32db + i.
   template <int NB, int DB, int RB>
-  __device__ static __forceinline__ void pv(const Lanes& L, uint32_t v_off, const PRegs<NB> (&p)[RB],
-                                            f32x16 (&acc)[RB][DB]) {
+  __device__ static __forceinline__ void pv(const float* v_tile, const Lanes& L,
+                                            const PRegs<NB> (&p)[RB], f32x16 (&acc)[RB][DB]) {
+    const char* base = reinterpret_cast<const char*>(v_tile) + L.v;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t vrow = L.v + v_off + (nb * 32 + 8 * (r >> 2) + (r & 3)) * kRowV;
+        const char* vrow = base + (nb * 32 + 8 * (r >> 2) + (r & 3)) * kRowV;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const float vv = lds_load<float>(vrow + db * 128);
+          const float vv = *reinterpret_cast<const float*>(vrow + db * 128);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p[rb].f[nb][r], acc[rb][db], 0, 0, 0);
@@ -535,13 +542,38 @@ struct Stage {
   static constexpr int value = S;
 };
 
-// STAGES LDS stages each for K and V tiles (2 to 4), one array per operand,
-// tile t in stage t % STAGES.  With S stages a tile load issued at step t is
-// first needed at step t + S - 1, so it has S - 1 steps of compute to hide
-// its latency behind.  The copies are untracked by the compiler (it cannot
-// tell the stage being filled from the ones being read within one array);
-// each wave waits for its own with explicit vmcnt counts before the step's
-// barrier.
+// The LDS arrays of the K and V stages.  Separate arrays (not one
+// [STAGES][...] array): each is its own alias scope, so the compiler can see
+// that fragment reads of one stage do not depend on the tile copies still
+// landing in another, and need not wait for them.  Entries past STAGES
+// repeat earlier ones and are never used.
+template <typename T>
+struct StageArrays {
+  T* k[4];
+  T* v[4];
+};
+// Filled field by field: an initializer list of these addresses would be
+// emitted as a constant in global memory, which cannot hold LDS addresses.
+template <typename T>
+__device__ __forceinline__ StageArrays<T> stage_arrays(T* k0, T* k1, T* k2, T* k3, T* v0, T* v1,
+                                                       T* v2, T* v3) {
+  StageArrays<T> st;
+  st.k[0] = k0;
+  st.k[1] = k1;
+  st.k[2] = k2;
+  st.k[3] = k3;
+  st.v[0] = v0;
+  st.v[1] = v1;
+  st.v[2] = v2;
+  st.v[3] = v3;
+  return st;
+}
+
+// STAGES LDS stages each for K and V tiles (2 to 4), tile t in stage
+// t % STAGES.  With S stages a tile load issued at step t is first needed at
+// step t + S - 1, so it has S - 1 steps of compute to hide its latency
+// behind.  Every stage index below is a compile-time constant (the step
+// bodies are unrolled by stage), so every copy and read names its array.
 // RB: row blocks of 32 query rows per wave (1 or 2).  With two, every K and V
 // fragment read from LDS feeds two products, halving the LDS reads per
 // matrix-core operation (the transposing V reads are the slow ones); the
@@ -556,7 +588,7 @@ struct Stage {
 // log2(e) alone.
 template <typename T, int D, int NW, int RB, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
           bool BIAS>
-__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_lds) {
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArrays<T>& st) {
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
   static_assert(RB == 1 || RB == 2, "one or two row blocks per wave");
   static_assert(!SPLIT || MODE == MODE_DENSE, "the split forward serves the dense mode");
@@ -568,8 +600,6 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
   constexpr int BM = NW * 32 * RB;
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
-  constexpr int kKStage = KCopy::kArrayBytes;  // bytes per stage
-  constexpr int kVStage = VCopy::kArrayBytes;
   // Loads one step issues per wave; those of the last STAGES - 2 steps may
   // still be in flight when a step ends (the next step reads K(t+2) and
   // V(t+1), issued STAGES - 2 steps before this one ends).
@@ -630,15 +660,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
   // past the last tile fetches nothing.
   auto issue_k = [&](int t, int stage, int end) {
     const int j0 = (tile0 + t) * BN;
-    kcopy.issue_untracked(kp + j0 * k_row_bytes, end - j0, k_row_bytes,
-                          k_lds + stage * (kKStage / static_cast<int>(sizeof(T))), wave);
+    kcopy.issue(kp + j0 * k_row_bytes, end - j0, k_row_bytes, st.k[stage], wave);
   };
   auto issue_v = [&](int t, int stage, int end) {
     const int j0 = (tile0 + t) * BN;
-    vcopy.issue_untracked(vp + j0 * v_row_bytes, end - j0, v_row_bytes,
-                          v_lds + stage * (kVStage / static_cast<int>(sizeof(T))), wave);
+    vcopy.issue(vp + j0 * v_row_bytes, end - j0, v_row_bytes, st.v[stage], wave);
   };
-  const typename Path::Lanes lanes = Path::lanes(lds_addr(k_lds), lds_addr(v_lds), lane);
+  const typename Path::Lanes lanes = Path::lanes(lane);
 
   typename Path::QRegs qr[RB];
 #pragma unroll
@@ -759,7 +787,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[rb][nb] = f32x16{};
     }
-    Path::template qk<NB, RB>(lanes, 0, qr, s);
+    Path::template qk<NB, RB>(st.k[0], lanes, qr, s);
     if constexpr (BIAS) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) bias_next[rb].fold(s[rb], a.scale);
@@ -785,21 +813,19 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
   // softmax VALU work with the next tile's score MFMAs.
   auto step = [&](int t, auto stage) {
     constexpr int ST = decltype(stage)::value;
-    constexpr uint32_t k_nxt = ((ST + 1) % STAGES) * kKStage;
-    constexpr uint32_t v_cur = ST * kVStage;
-    // The next tile's bias is loaded first (also when this wave skips the
-    // tile: a conditional load would keep two copies of the bias registers
-    // alive).
+    const T* k_nxt = st.k[(ST + 1) % STAGES];
+    const T* v_cur = st.v[ST];
+    // The next tile's bias goes out before the tile copies, so waiting for it
+    // never waits for them (also when this wave skips the tile: a
+    // conditional load would keep two copies of the bias registers alive).
     if constexpr (BIAS) load_bias(t + 1, bias_next);
     // The tile copies into K(t)'s and V(t-1)'s stages (their last readers
-    // passed the previous barrier).  They are inline assembly, which inside
-    // the products' scheduling region makes the compiler drop the interleave
-    // that interleave_qk / interleave_pv request: a scheduling barrier closes
-    // their region.  The compiler does not count these copies, so its wait
-    // for the bias also waits for them.
+    // passed the previous barrier).  They are the compiler's buffer-load
+    // builtins: it interleaves them with the first fragment reads and the
+    // products (inline assembly there would make it drop the interleave
+    // that interleave_qk / interleave_pv request).
     issue_k(t + STAGES, ST, t + STAGES < n_tiles ? kend : 0);
     issue_v(t + STAGES - 1, (ST + STAGES - 1) % STAGES, t + STAGES - 1 < n_tiles ? kend : 0);
-    __builtin_amdgcn_sched_barrier(0);
     if (!wave_done(t)) {
 
     // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
@@ -812,7 +838,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
       for (int nb = 0; nb < NB; ++nb) s_next[rb][nb] = f32x16{};
       tile_sum[rb] = first_pass(rb, s[rb], p[rb]);
     }
-    Path::template qk<NB, RB>(lanes, k_nxt, qr, s_next);
+    Path::template qk<NB, RB>(k_nxt, lanes, qr, s_next);
     // P is computed here, beside the MFMAs, not after the branches
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) Path::pin(p[rb]);
@@ -822,7 +848,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
     if constexpr (!BIAS) mask_tile(t + 1, s_next);
 
     // Phase B: O += P(t) V(t) on the matrix cores.
-    Path::template pv<NB, DB, RB>(lanes, v_cur, p, acc);
+    Path::template pv<NB, DB, RB>(v_cur, lanes, p, acc);
     Path::template interleave_pv<NB, DB, RB>();
     if constexpr (BIAS) {
 #pragma unroll
@@ -844,12 +870,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
   // The last tile: probabilities and P.V only.  It issues no loads, but
   // the zero-row copies of earlier steps may still be in flight: every
   // wave settles its own before leaving.
-  auto last_step = [&](uint32_t v_cur) {
+  auto last_step = [&](const T* v_cur) {
     if (!wave_done(n_tiles - 1)) {
       PRegs p[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) settle(rb, s[rb], p[rb], first_pass(rb, s[rb], p[rb]));
-      Path::template pv<NB, DB, RB>(lanes, v_cur, p, acc);
+      Path::template pv<NB, DB, RB>(v_cur, lanes, p, acc);
     }
     wait_vmem();
   };
@@ -873,7 +899,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, T* k_lds, T* v_l
         step(t + 3, Stage<3>{});
       }
     }
-    last_step(static_cast<uint32_t>((n_tiles - 1) % STAGES) * kVStage);
+    const int last = (n_tiles - 1) % STAGES;
+    last_step(last == 0 ? st.v[0] : (last == 1 ? st.v[1] : (last == 2 ? st.v[2] : st.v[3])));
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
@@ -1009,7 +1036,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
     vcopy.issue_untracked(vp + j0 * v_row_bytes, t < n_tiles ? kend - j0 : 0, v_row_bytes,
                           v_lds + stage * (kVStage / 2), wave);
   };
-  const typename Path::Lanes lanes = Path::lanes(lds_addr(k_lds), lds_addr(v_lds), lane);
+  const typename Path::Lanes lanes = Path::lanes(lane);
 
   typename Path::QRegs qr;
   Path::load_q(qp + static_cast<int64_t>(qi) * a.q_ss, row_ok, lh, qr);
@@ -1082,7 +1109,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
     // u = 0: scores of tile 0.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-    Path::template qk<NB>(lanes, 0, qr, s);
+    Path::template qk<NB>(k_lds, lanes, qr, s);
     wait_vmem_allow<kInFlight>();  // K(1) and V(0) have landed
     barrier_lds();
 
@@ -1105,8 +1132,8 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
       f32x16 s_next[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s_next[nb] = f32x16{};
-      Path::template qk<NB>(lanes, ((ST + 1) % STAGES) * kKStage, qr, s_next);
-      Path::template pv<NB, DB>(lanes, ST * kVStage, p, acc);
+      Path::template qk<NB>(k_lds + ((ST + 1) % STAGES) * (kKStage / 2), lanes, qr, s_next);
+      Path::template pv<NB, DB>(v_lds + ST * (kVStage / 2), lanes, p, acc);
       Path::template interleave_c<NB, DB>();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[nb] = s_next[nb];
@@ -1136,8 +1163,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
     // the workgroup's last, so it ends without a barrier (every wave passes
     // the same number of barriers).
     s_interval(n_tiles - 1);
-    Path::template pv<NB, DB>(lanes, static_cast<uint32_t>((n_tiles - 1) % STAGES) * kVStage, p,
-                              acc);
+    Path::template pv<NB, DB>(v_lds + ((n_tiles - 1) % STAGES) * (kVStage / 2), lanes, p, acc);
     wait_vmem();
     if (group == 0) barrier_lds();
   }
@@ -1183,11 +1209,28 @@ template <typename T, int D, int NW, int RB, int BN, int STAGES, int MODE, bool 
 __global__ __launch_bounds__(NW * 64, RB == 2 ? 1 : 2) void attn_fwd_kernel(FwdArgs a) {
   using Path = typename PathFor<T, D>::type;
   constexpr int kES = static_cast<int>(sizeof(T));
-  constexpr int kKElems = STAGES * Path::template KCopy<BN, NW>::kArrayBytes / kES;
-  constexpr int kVElems = STAGES * Path::template VCopy<BN, NW>::kArrayBytes / kES;
-  __shared__ __attribute__((aligned(1024))) T k_lds[kKElems];
-  __shared__ __attribute__((aligned(1024))) T v_lds[kVElems];
-  attn_fwd_body<T, D, NW, RB, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(a, k_lds, v_lds);
+  constexpr int kKElems = Path::template KCopy<BN, NW>::kArrayBytes / kES;
+  constexpr int kVElems = Path::template VCopy<BN, NW>::kArrayBytes / kES;
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  if constexpr (STAGES == 2) {
+    attn_fwd_body<T, D, NW, RB, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds0, k_lds1, v_lds0, v_lds1, v_lds0, v_lds1));
+  } else if constexpr (STAGES == 3) {
+    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+    attn_fwd_body<T, D, NW, RB, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds2, k_lds0, v_lds0, v_lds1, v_lds2, v_lds0));
+  } else {
+    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+    __shared__ __attribute__((aligned(1024))) T k_lds3[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds3[kVElems];
+    attn_fwd_body<T, D, NW, RB, BN, STAGES, MODE, CAUSAL, SPLIT, BIAS>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds2, k_lds3, v_lds0, v_lds1, v_lds2, v_lds3));
+  }
 }
 
 // ---------------------------------------------------------------------------
