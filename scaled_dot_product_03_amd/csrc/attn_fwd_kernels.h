@@ -429,8 +429,41 @@ template <typename T, int NB>
 struct BiasTile {
   T b[NB][16];
 
-  __device__ __forceinline__ void load(const T* row, int j0, int len_k, int lh, bool vec) {
-    if (vec && j0 + NB * 32 <= len_k) {
+  // Loads of a whole tile come in two widths.  Wide (16-bit types, 16-byte
+  // aligned rows): lane (i, h) loads keys 16 j + 8 h .. + 7 of its row for
+  // j = 0, 1 -- its own four keys of one group and the four its partner lane
+  // (i, 1 - h) needs of the other -- and the two swap those halves, so a
+  // tile takes 2 NB loads of 16 bytes instead of 4 NB of 8.  Narrow: 4 NB
+  // loads of 4 keys (8-byte aligned rows).  mode: 2 wide, 1 narrow, 0 key
+  // by key.
+  __device__ __forceinline__ void load(const T* row, int j0, int len_k, int lh, int mode) {
+    if constexpr (sizeof(T) == 2) {
+      if (mode == 2 && j0 + NB * 32 <= len_k) {
+        using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            u32x4 v;
+            __builtin_memcpy(&v,
+                             __builtin_assume_aligned(row + j0 + nb * 32 + 16 * j + 8 * lh, 16), 16);
+            // h = 0 holds keys 16j .. 16j+7 and keeps the first four (group
+            // 2j); h = 1 holds 16j+8 .. 16j+15 and keeps the last four
+            // (group 2j+1).  Each sends the other half to its partner.
+            const uint32_t s0 = lh ? v[0] : v[2];
+            const uint32_t s1 = lh ? v[1] : v[3];
+            const uint32_t r0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), 32));
+            const uint32_t r1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), 32));
+            const uint32_t lo[2] = {lh ? r0 : v[0], lh ? r1 : v[1]};  // group 2j
+            const uint32_t hi[2] = {lh ? v[2] : r0, lh ? v[3] : r1};  // group 2j+1
+            __builtin_memcpy(&b[nb][8 * j], lo, 8);
+            __builtin_memcpy(&b[nb][8 * j + 4], hi, 8);
+          }
+        }
+        return;
+      }
+    }
+    if (mode >= 1 && j0 + NB * 32 <= len_k) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -686,25 +719,28 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
   }
   const float c2 = BIAS ? kLog2e : a.scale_log2;
 
-  // This lane's bias rows (the sequence's block of the bias view).  Vector
-  // loads need the block to start on a 4-element boundary; the strides are
-  // multiples of 4 elements, so only the key offset decides.
+  // This lane's bias rows (the sequence's block of the bias view).
   using Bias = BiasTile<T, NB>;
   const T* bias_row[RB] = {};
-  bool bias_vec = false;
+  int bias_mode = 0;
   if constexpr (BIAS) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       bias_row[rb] = static_cast<const T*>(a.bias) + sr.b * a.bias_sb + h * a.bias_sh +
                      (static_cast<int64_t>(sr.q_start) + qi[rb]) * a.bias_sq + sr.k_start;
     }
-    bias_vec = (sr.k_start & 3) == 0;
+    // Narrow vector loads need the block to start on a 4-element boundary
+    // (the strides are multiples of 4 elements); wide ones a 16-byte
+    // aligned base and 8-element strides and start.
+    const bool wide = (reinterpret_cast<uintptr_t>(a.bias) & 15) == 0 && (a.bias_sb & 7) == 0 &&
+                      (a.bias_sh & 7) == 0 && (a.bias_sq & 7) == 0 && (sr.k_start & 7) == 0;
+    bias_mode = wide ? 2 : ((sr.k_start & 3) == 0 ? 1 : 0);
   }
   auto load_bias = [&](int t, Bias (&bt)[RB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (row_ok[rb]) {
-        bt[rb].load(bias_row[rb], (tile0 + t) * BN, sr.len_k, lh, bias_vec);
+        bt[rb].load(bias_row[rb], (tile0 + t) * BN, sr.len_k, lh, bias_mode);
       } else {
         bt[rb].zero();
       }
