@@ -16,17 +16,6 @@ using bf16x8 = __bf16 __attribute__((ext_vector_type(8)));
 using f16x8 = _Float16 __attribute__((ext_vector_type(8)));
 using lds_void_ptr = __attribute__((address_space(3))) void*;
 
-// The LDS byte address of a workgroup-shared array, and a typed read at an
-// LDS byte address.
-template <typename E>
-__device__ __forceinline__ uint32_t lds_addr(const E* p) {
-  return (uint32_t)(uintptr_t)(lds_void_ptr)(const_cast<E*>(p));
-}
-template <typename V>
-__device__ __forceinline__ V lds_load(uint32_t addr) {
-  return *(const __attribute__((address_space(3))) V*)(addr);
-}
-
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -73,7 +62,8 @@ __device__ __forceinline__ void wait_vmem_allow() {
 // Matrix-core paths.  Each provides: Q fragments held in registers, the
 // S^T = K Q^T product from a K tile in LDS, the probabilities P of a score
 // tile, and O^T += V^T P^T from a V tile in LDS.  Tiles in LDS are row-major
-// [key][dim] with 16-byte chunks XOR-swizzled per row.
+// [key][dim]: 16-bit tiles of head dim 128 with their 16-byte chunks
+// XOR-swizzled per row (swizzle_of below), the others with padded rows.
 // ---------------------------------------------------------------------------
 
 template <typename T>

@@ -4,10 +4,10 @@
 //
 // One workgroup computes block_m = 32 * waves * row_blocks query rows of one
 // (batch or sequence, head); each wavefront owns 32 rows (one row block) or
-// 64 (two).  The workgroup
-// walks the key axis in tiles of block_n keys.  K and V tiles go from HBM
-// straight into LDS with buffer loads (two or three LDS stages, no register
-// staging, rows past the sequence read back as zeros).  Every wave keeps its
+// 64 (two).  The workgroup walks the key axis in tiles of block_n keys.  K
+// and V tiles go from HBM straight into LDS with buffer loads (two to four
+// LDS stages, no register staging, rows past the sequence read back as
+// zeros).  Every wave keeps its
 // Q rows in VGPRs for the whole loop, multiplies them against the K tile on
 // the matrix cores, folds the tile into a running reference max and running
 // sum (online softmax) and accumulates P.V on the matrix cores.  The score
@@ -33,10 +33,10 @@
 // (a 64-byte block of 4 rows per pass) free of bank conflicts on gfx950's 64
 // banks of 4 bytes, while a tile takes exactly BN * D * 2 bytes.  A lane's
 // chunk offsets then differ by XOR, not by a constant, so each lane keeps
-// its address for every K k-step and V dim block in registers (stage 0),
-// and the stage and row offsets ride in the instructions' immediates.
+// its offset for every K k-step and V dim block in registers, and the stage
+// array's base and the row offsets ride in the instructions' immediates.
 // Head dim 64 and fp32 tiles use padded rows instead (k_lds_row_bytes
-// below), which measured faster at head dim 64.
+// below); at head dim 64 the swizzle measured no faster.
 //
 // Software pipeline.  Step t turns the scores of tile t into probabilities
 // (VALU) while the matrix cores compute the scores of tile t+1, then
