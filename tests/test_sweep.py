@@ -89,3 +89,31 @@ def test_written_table_compiles_into_the_committed_format():
     for cond in ("dtype_code<T>() == DT_BF16 && D == 128", "dtype_code<T>() == DT_F16 && D == 64",
                  "dtype_code<T>() == DT_BF16 && D == 64", "dtype_code<T>() == DT_F16 && D == 128"):
         assert len(_table_entries(text, cond)) == len(sweep.BUCKETS)
+
+
+def test_schedule_field_names_defines_and_table_entries(tmp_path):
+    # schedule 2 (two 32-row blocks per wave) is named, built and written like the others
+    assert sweep._name(("bf16", 128), (4, 32, 3, 2)) == "bf16_d128_w4_n32_s3_rb2"
+    assert sweep._name(("fp16", 64), (4, 64, 2, 0)) == "fp16_d64_w4_n64_s2"
+    assert "-DSDPA03_SWEEP_SCHEDULE=2" in sweep._defines(("bf16", 128), (4, 32, 3, 2))
+    assert "-DSDPA03_SWEEP_SCHEDULE=0" in sweep._defines(("fp16", 64), (4, 64, 2))
+    results = [
+        {"dtype": "bf16", "head_dim": 128, "cand": [4, 32, 3, 2], "parity": True,
+         "ms": {"5": {"w": [0.1]}}},
+        {"dtype": "bf16", "head_dim": 128, "cand": [4, 64, 2, 0], "parity": True,
+         "ms": {"5": {"w": [0.2]}}},
+    ]
+    rp = tmp_path / "results.json"
+    rp.write_text(json.dumps(results))
+    table = tmp_path / "dispatch_table.inc"
+    shutil.copy(sweep.TABLE, table)
+    pick = sweep.write(str(rp), str(table))
+    assert pick[("bf16", 128, 5)] == (4, 32, 3, 2)
+    assert _table_entries(table.read_text(), "dtype_code<T>() == DT_BF16 && D == 128")[5] == \
+        (4, 32, 3, 2)
+
+
+def test_every_candidate_class_offers_each_schedule():
+    for cls, cands in sweep.CANDIDATES.items():
+        scheds = {sweep._cand4(c)[3] for c in cands}
+        assert scheds == {0, 1, 2}, (cls, scheds)
