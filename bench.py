@@ -23,10 +23,8 @@ Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
-import re
 import sys
 import time
 
@@ -38,37 +36,12 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16 BHSD S=2048 D=128; varlen THD)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/attn_fwd.hip",
-                  "scaled_dot_product_03_amd/csrc/attn_fwd_bf16.hip",
-                  "scaled_dot_product_03_amd/csrc/attn_fwd_kernels.h",
-                  "scaled_dot_product_03_amd/csrc/attn_common.h",
-                  "scaled_dot_product_03_amd/csrc/dispatch_table.inc"]
+
+from scaled_dot_product_03_amd.rocprof import kernel_source_hash, traffic_from_profiles  # noqa: E402
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_from_profiles(kernel_tag: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel_tag}.md")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    src = re.search(r"kernel_source_sha:\s*(\w+)", text)
-    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
-        return None
-    return float(val.group(1))
 
 
 def dense_flops(B, H, Sq, Sk, D, causal):
