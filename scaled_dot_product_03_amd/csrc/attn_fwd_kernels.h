@@ -516,18 +516,36 @@ struct BiasTile {
 // follow each other, so the workgroups that read one key range of a head
 // share an XCD too.
 //
-// Under a causal mask query tile m costs m + 1 key tiles.  Heaviest-first
-// within each head still leaves long tiles starting late (a model of 64
-// workgroup slots puts the makespan at 1.5 times the average load); here the
-// launch index runs over (batch, head[, split]) fastest and over query tiles
-// from the last one down, so all the heaviest tiles start first.  Consecutive
-// launch indices walk the heads and land on consecutive XCDs, so every XCD
-// gets the same mix of tile costs, and with a multiple of 8 (batch, head)
-// groups each head stays on one XCD.
+// Under a causal mask query tile m costs m + 1 key tiles, so the order runs
+// over query tiles from the last one down (heaviest first).  Workgroup n goes
+// to XCD n % 8 and is that XCD's (n / 8)-th; the (batch, head[, split])
+// groups are dealt to the XCDs round-robin (group g to XCD g % 8), so each
+// head stays on one XCD.  An XCD's groups are taken in parts of `span`
+// groups, one part after the other, each part heaviest tile first with its
+// groups fastest: a part finishes its long tiles before the next part's
+// start, so fewer heads' keys and values are in flight in the XCD's L2 at a
+// time, while a part of at least four times the waves an XCD holds (the
+// launcher's choice of span) still balances its workgroups' unequal costs.
+// span 0 (split launches, or a group count that is not a multiple of 8)
+// runs over the groups fastest across the whole grid instead.
 template <bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void decode_tile(int m_tiles, int num_heads, int num_z, int num_splits,
-                                            int& z, int& h, int& m, int& split) {
+                                            int span, int& z, int& h, int& m, int& split) {
   const uint32_t n = blockIdx.x;
+  if constexpr (CAUSAL && !SPLIT) {
+    if (span > 0) {
+      const uint32_t xcd = n & 7u, i = n >> 3;
+      const uint32_t per_part = static_cast<uint32_t>(span);
+      const uint32_t part_wgs = per_part * static_cast<uint32_t>(m_tiles);
+      const uint32_t part = i / part_wgs, r = i % part_wgs;
+      m = m_tiles - 1 - static_cast<int>(r / per_part);
+      const uint32_t g = xcd + 8u * (part * per_part + r % per_part);
+      split = 0;
+      h = static_cast<int>(g % static_cast<uint32_t>(num_heads));
+      z = static_cast<int>(g / static_cast<uint32_t>(num_heads));
+      return;
+    }
+  }
   if constexpr (CAUSAL) {
     const uint32_t per_split = static_cast<uint32_t>(num_heads) * static_cast<uint32_t>(num_z);
     const uint32_t groups = SPLIT ? per_split * static_cast<uint32_t>(num_splits) : per_split;
@@ -640,7 +658,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
   constexpr int kInFlightAtStepEnd = (STAGES - 2) * kLoadsPerStep;
 
   int z, h, m, split;
-  decode_tile<CAUSAL, SPLIT>(a.m_tiles, a.num_heads, a.num_z, a.num_splits, z, h, m, split);
+  decode_tile<CAUSAL, SPLIT>(a.m_tiles, a.num_heads, a.num_z, a.num_splits, a.causal_span, z, h,
+                             m, split);
   const SeqRange sr = seq_range<MODE>(a, z);
   const int m0 = m * BM;
   if (m0 >= sr.len_q) return;  // uniform over the workgroup
@@ -1024,7 +1043,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_body(const FwdArgs& a, T* k_ld
   constexpr int kInFlight = (STAGES - 2) * kLoadsPerTile;
 
   int z, h, m, split;
-  decode_tile<CAUSAL, false>(a.m_tiles, a.num_heads, a.num_z, 1, z, h, m, split);
+  decode_tile<CAUSAL, false>(a.m_tiles, a.num_heads, a.num_z, 1, a.causal_span, z, h, m, split);
   const SeqRange sr = seq_range<MODE>(a, z);
   const int m0 = m * BM;
   if (m0 >= sr.len_q) return;  // uniform over the workgroup
@@ -1327,9 +1346,32 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeArgs a) {
 
 namespace {
 
+// An XCD holds 256 waves at two per SIMD (32 CUs x 4 SIMDs).  A part of the
+// causal launch order gets at least four times that many waves of
+// workgroups; measured on the causal workloads (S 2048 dense, THD varlen
+// with sequences up to 4096, padded varlen up to 8192), more parts than
+// that left the long tiles of the last part unbalanced, fewer kept more
+// heads' keys in flight.
+constexpr int64_t kCausalPartWaves = 1024;
+
+// Groups per part (a divisor of the groups each XCD gets) for a causal
+// launch of `groups` (batch or sequence, head) groups of m_tiles workgroups
+// of `waves` waves; 0 when the groups do not split evenly over 8 XCDs.
+inline int32_t causal_span(int64_t groups, int32_t m_tiles, int waves) {
+  if (groups <= 0 || groups % 8 != 0 || m_tiles <= 0) return 0;
+  const int64_t per_xcd = groups / 8;
+  for (int64_t d = 1; d < per_xcd; ++d) {
+    if (per_xcd % d == 0 && d * m_tiles * waves >= kCausalPartWaves) return static_cast<int32_t>(d);
+  }
+  return static_cast<int32_t>(per_xcd);
+}
+
 template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
-int launch_bucket(const FwdArgs& a, hipStream_t stream) {
+int launch_bucket(const FwdArgs& args, hipStream_t stream) {
   constexpr TableEntry e = launch_entry<T, D, BUCKET, BIAS>();
+  FwdArgs a = args;
+  a.causal_span = CAUSAL ? causal_span(static_cast<int64_t>(a.num_heads) * a.num_z, a.m_tiles, e.waves)
+                         : 0;
   const uint32_t grid = static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z;
   if constexpr (e.schedule == kSchedPingPong) {
     static_assert(e.waves == 8 && sizeof(T) == 2, "ping-pong: 8 waves, 16-bit inputs");

@@ -44,6 +44,9 @@ struct FwdArgs {
   float* ws_o;            // [split][z][h][row][head_dim]
   float* ws_lse;          // [split][z][h][row]
   int64_t ws_rows;        // rows per split: num_z * num_heads * seqlen_q
+  // Causal launch order (unsplit): (batch or sequence, head) groups per part
+  // of an XCD's work; 0 keeps the order without parts.  Set by the launcher.
+  int32_t causal_span = 0;
 };
 
 // Arguments of the kernel that merges the partial results of a split
