@@ -236,17 +236,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(2 * kStage))) T v_lds[kStage];
 
   // Under the causal mask the last query tiles cost the most: they go first.
-  const uint32_t n = blockIdx.x;
   const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
-  int m;
-  uint32_t g;
-  if constexpr (CAUSAL) {
-    g = n % groups;
-    m = a.q_tiles - 1 - static_cast<int>(n / groups);
-  } else {
-    m = static_cast<int>(n % static_cast<uint32_t>(a.q_tiles));
-    g = n / static_cast<uint32_t>(a.q_tiles);
-  }
+  uint32_t g, rank;
+  bwd_launch_order(CAUSAL, static_cast<uint32_t>(a.q_tiles), groups, a.span_q, g, rank);
+  const int m = CAUSAL ? a.q_tiles - 1 - static_cast<int>(rank) : static_cast<int>(rank);
   const int h = static_cast<int>(g % static_cast<uint32_t>(a.num_heads));
   const int z = static_cast<int>(g / static_cast<uint32_t>(a.num_heads));
   const SeqRange sr =
@@ -409,17 +402,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(2 * kWStage))) float w_lds[kWStage / 2];
 
   // Under the causal mask the first key tiles cost the most: they go first.
-  const uint32_t n = blockIdx.x;
   const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
-  int kt;
-  uint32_t g;
-  if constexpr (CAUSAL) {
-    g = n % groups;
-    kt = static_cast<int>(n / groups);
-  } else {
-    kt = static_cast<int>(n % static_cast<uint32_t>(a.k_tiles));
-    g = n / static_cast<uint32_t>(a.k_tiles);
-  }
+  uint32_t g, rank;
+  bwd_launch_order(CAUSAL, static_cast<uint32_t>(a.k_tiles), groups, a.span_k, g, rank);
+  const int kt = static_cast<int>(rank);
   const int h = static_cast<int>(g % static_cast<uint32_t>(a.num_heads));
   const int z = static_cast<int>(g / static_cast<uint32_t>(a.num_heads));
   const SeqRange sr =
@@ -605,9 +591,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 template <typename T, int D, int MODE, bool CAUSAL>
-int launch_typed(const BwdArgs& a, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(a.num_b) * a.num_heads * a.ws_rows_pad;
+int launch_typed(const BwdArgs& args, hipStream_t s) {
+  BwdArgs a = args;
   const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
+  a.span_q = CAUSAL ? causal_span(groups, a.q_tiles, kBwdDqRows * 2 / 64) : 0;
+  a.span_k = CAUSAL ? causal_span(groups, a.k_tiles, kBwdDkvKeys * 2 / 64) : 0;
+  const int64_t rows = static_cast<int64_t>(a.num_b) * a.num_heads * a.ws_rows_pad;
   if (a.q_tiles > 0) {
     constexpr int64_t kRowsPerBlock = 256 / (D / 8);
     hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D, MODE>),

@@ -275,4 +275,54 @@ __device__ __forceinline__ SeqRange seq_range_of(const int32_t* cu_q, const int3
   return r;
 }
 
+// An XCD holds 256 waves at two per SIMD (32 CUs x 4 SIMDs).  A part of the
+// causal launch order gets at least four times that many waves of
+// workgroups; measured on the causal forward workloads (S 2048 dense, THD varlen
+// with sequences up to 4096, padded varlen up to 8192), more parts than
+// that left the long tiles of the last part unbalanced, fewer kept more
+// heads' keys in flight.
+constexpr int64_t kCausalPartWaves = 1024;
+
+// Groups per part (a divisor of the groups each XCD gets) for a causal
+// launch of `groups` (batch or sequence, head) groups of m_tiles workgroups
+// of `waves` waves; 0 when the groups do not split evenly over 8 XCDs.
+// Workgroup n runs on XCD n % 8; the forward and backward launch orders
+// deal group g to XCD g % 8 and take each XCD's groups `span` at a time.
+inline int32_t causal_span(int64_t groups, int32_t m_tiles, int waves) {
+  if (groups <= 0 || groups % 8 != 0 || m_tiles <= 0) return 0;
+  const int64_t per_xcd = groups / 8;
+  for (int64_t d = 1; d < per_xcd; ++d) {
+    if (per_xcd % d == 0 && d * m_tiles * waves >= kCausalPartWaves) return static_cast<int32_t>(d);
+  }
+  return static_cast<int32_t>(per_xcd);
+}
+
+// Launch order of the backward kernels: workgroup n of groups x tiles
+// workgroups -> (group g, tile rank t).  Without a causal mask each XCD runs
+// a contiguous range of groups-major ranks (whole heads share its L2).
+// Under the mask rank 0 is a group's most expensive tile; ranks run from 0
+// up, over the XCD's groups in parts of `span` as in the forward (span 0:
+// over all groups fastest).
+__device__ __forceinline__ void bwd_launch_order(bool causal, uint32_t tiles, uint32_t groups,
+                                                 int span, uint32_t& g, uint32_t& t) {
+  const uint32_t n = blockIdx.x;
+  if (!causal) {
+    const uint32_t per_xcd = gridDim.x >> 3;
+    uint32_t logical = n;
+    if (n < (per_xcd << 3)) logical = (n & 7u) * per_xcd + (n >> 3);
+    t = logical % tiles;
+    g = logical / tiles;
+  } else if (span > 0) {
+    const uint32_t xcd = n & 7u, i = n >> 3;
+    const uint32_t per_part = static_cast<uint32_t>(span);
+    const uint32_t part_wgs = per_part * tiles;
+    const uint32_t part = i / part_wgs, r = i % part_wgs;
+    t = r / per_part;
+    g = xcd + 8u * (part * per_part + r % per_part);
+  } else {
+    g = n % groups;
+    t = n / groups;
+  }
+}
+
 }  // namespace sdpa03

@@ -1346,26 +1346,6 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeArgs a) {
 
 namespace {
 
-// An XCD holds 256 waves at two per SIMD (32 CUs x 4 SIMDs).  A part of the
-// causal launch order gets at least four times that many waves of
-// workgroups; measured on the causal workloads (S 2048 dense, THD varlen
-// with sequences up to 4096, padded varlen up to 8192), more parts than
-// that left the long tiles of the last part unbalanced, fewer kept more
-// heads' keys in flight.
-constexpr int64_t kCausalPartWaves = 1024;
-
-// Groups per part (a divisor of the groups each XCD gets) for a causal
-// launch of `groups` (batch or sequence, head) groups of m_tiles workgroups
-// of `waves` waves; 0 when the groups do not split evenly over 8 XCDs.
-inline int32_t causal_span(int64_t groups, int32_t m_tiles, int waves) {
-  if (groups <= 0 || groups % 8 != 0 || m_tiles <= 0) return 0;
-  const int64_t per_xcd = groups / 8;
-  for (int64_t d = 1; d < per_xcd; ++d) {
-    if (per_xcd % d == 0 && d * m_tiles * waves >= kCausalPartWaves) return static_cast<int32_t>(d);
-  }
-  return static_cast<int32_t>(per_xcd);
-}
-
 template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
 int launch_bucket(const FwdArgs& args, hipStream_t stream) {
   constexpr TableEntry e = launch_entry<T, D, BUCKET, BIAS>();

@@ -43,6 +43,10 @@ struct BwdArgs {
   int32_t k_tiles;    // key tiles of the dK/dV kernel
   float scale;        // dQ and dK carry the softmax scale
   float scale_log2;   // scale * log2(e)
+  // Causal launch order: groups per part of an XCD's work for the dQ and
+  // the dK/dV kernels (0: no parts).  Set by the launcher.
+  int32_t span_q = 0;
+  int32_t span_k = 0;
 };
 
 // Workspace rows per (b, h) for a rank-4 view of `rows` query rows.
