@@ -304,9 +304,17 @@ def test_bwd_workload_compact_thd_pairs():
     q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
     o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
                                              scale=x.scale, causal=True)
-    grads = binding.attn_bwd_compact_varlen(q, k, v, o, dod, lse, x.cu_seqlens_q,
-                                            x.cu_seqlens_k, scale=x.scale, causal=True)
+    # NaN-filled gradients: the sequences cover every token, so every row of
+    # dQ, dK and dV must be written (both kernels' causal launches take each
+    # XCD's heads in parts here).
+    grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
+    binding.attn_bwd_compact_varlen(q, k, v, o, dod, lse, x.cu_seqlens_q, x.cu_seqlens_k,
+                                    scale=x.scale, causal=True, dq=grads[0], dk=grads[1],
+                                    dv=grads[2])
     torch.cuda.synchronize()
+    assert int(x.cu_seqlens_q[-1]) == q.shape[0]
+    for g in grads:
+        assert torch.isfinite(g).all()
     cu = x.cu_seqlens_q
     order = np.argsort(lengths)
     picks = list(dict.fromkeys([int(order[-1]), int(order[0]), int(order[len(order) // 2]), 5]))

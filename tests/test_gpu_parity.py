@@ -145,9 +145,15 @@ def test_workload_compact_thd_sampled():
     x = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
     _log(f"compact THD lengths {x.meta['lengths_q']}")
     q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    # NaN-filled outputs: the sequences cover every token, so every output
+    # row must be written (a launch order that dropped or repeated a query
+    # tile would leave NaN rows; this launch takes each XCD's heads in parts).
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, q.shape[1], q.shape[0]), float("nan"), device=DEV)
     o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
-                                             scale=x.scale, causal=True)
+                                             scale=x.scale, causal=True, out=o, lse=lse)
     torch.cuda.synchronize()
+    assert int(x.cu_seqlens_q[-1]) == q.shape[0]
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     cu = x.cu_seqlens_q
     rng = np.random.default_rng(4)
