@@ -8,7 +8,9 @@ workload B=4, H=16, Sq=Sk=2048, D=128 with scale 1/sqrt(128): the
 non-causal forward followed by the causal forward (both masks of that
 workload), inputs resident in HBM.  FLOPs are 4*Sq*Sk*D*H*B per forward,
 halved for causal.  The line also carries the compact varlen THD workload
-(16 sequences, lengths U{1..4096} from seed 4, H=16, D=128, bf16, causal)
+(16 sequences, lengths U{1..4096} from seed 4, H=16, D=128, bf16, causal), the
+padded varlen workload (B=8, H=32, 8192-row slabs, true lengths U{2048..8192}
+from seed 5, D=128, bf16, causal; FLOPs over the true lengths)
 and the fp16 B=2, H=32, Sq=512, Sk=8192, D=64 workload (through attn_fwd
 and through the key-parallel attn_fwd_splitk), the dense workload with a full
 (B, H, Sq, Sk) additive bias, and the backward of the dense workload timed
@@ -124,6 +126,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-padded", action="store_true",
+                    help="skip the padded varlen workload (B8 H32 Smax 8192 D128)")
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-bias", action="store_true")
@@ -213,20 +217,22 @@ def main():
                    "pct_mfma_peak": 100 * f_c / (c_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
 
-    def block_ms(call):
-        """Average ms of `call` over args.steps back-to-back calls (after warmup
-        and a clock-settling phase), from two HIP events on the launch stream."""
+    def block_ms(call, n=None):
+        """Average ms of `call` over n (default args.steps) back-to-back calls
+        (after warmup and a clock-settling phase), from two HIP events on the
+        launch stream."""
+        n = n or args.steps
         for _ in range(args.warmup):
             call()
         settle(call, torch)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         e[0].record(stream)
-        for _ in range(args.steps):
+        for _ in range(n):
             call()
         e[1].record(stream)
         torch.cuda.synchronize()
-        return e[0].elapsed_time(e[1]) / args.steps
+        return e[0].elapsed_time(e[1]) / n
 
     if not args.no_varlen:
         vx = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
@@ -244,6 +250,25 @@ def main():
             "flops": vf, "avg_ms": v_avg, "tflops": vf / (v_avg * 1e-3) / 1e12,
             "pct_mfma_peak": 100 * vf / (v_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del vq, vk, vv, vo, vlse
+
+    if not args.no_padded:
+        px = inputs.workload("padded_bf16_b8h32smax8192d128_len2048to8192_causal")
+        pq, pk, pv = px.q.to(dev), px.k.to(dev), px.v.to(dev)
+        pcu = torch.from_numpy(px.cu_seqlens_q).to(dev)
+        plen, pscale = px.meta["lengths_q"], px.scale
+        del px
+        po = torch.empty_like(pq)
+        plse = torch.empty(pq.shape[:3], dtype=torch.float32, device=dev)
+        p_avg = block_ms(lambda: binding.attn_fwd_padded_varlen(
+            pq, pk, pv, pcu, pcu, scale=pscale, causal=True, out=po, lse=plse),
+            min(args.steps, 10))
+        pf = varlen_flops(plen, pq.shape[1], pq.shape[3], True)
+        breakdown["padded_varlen_causal"] = {
+            "workload": "padded_bf16_b8h32smax8192d128_len2048to8192_causal (seed 5, true "
+                        "lengths %s)" % list(int(v) for v in plen),
+            "flops": pf, "avg_ms": p_avg, "tflops": pf / (p_avg * 1e-3) / 1e12,
+            "pct_mfma_peak": 100 * pf / (p_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del pq, pk, pv, po, plse
 
     if not args.no_splitk:
         sx = inputs.workload("dense_fp16_b2h32sq512sk8192d64")

@@ -54,7 +54,7 @@ B, H, S, D, ELEM = 4, 16, 2048, 128, 2
 SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
                "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES", "SQ_BUSY_CYCLES",
                "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
-FWD_ONLY = ["--no-cpu-baseline", "--no-varlen", "--no-splitk", "--no-bwd"]
+FWD_ONLY = ["--no-cpu-baseline", "--no-varlen", "--no-padded", "--no-splitk", "--no-bwd"]
 TEMPLATE_NOTE = ("Forward template arguments: <element type, head_dim, waves, row blocks per wave, "
                  "block_n, stages, mode (0 dense, 1 compact, 2 padded), causal, split, bias>; "
                  "merge and backward kernels: <element type, head_dim[, mode, causal]>.")
