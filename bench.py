@@ -39,7 +39,8 @@ METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16 BHSD S=2048 D=128; varlen THD)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0
 
-from scaled_dot_product_03_amd.rocprof import kernel_source_hash, traffic_from_profiles  # noqa: E402
+from scaled_dot_product_03_amd.rocprof import (  # noqa: E402
+    clock_from_profiles, kernel_source_hash, traffic_from_profiles)
 
 
 def log(msg):
@@ -57,6 +58,7 @@ def varlen_flops(lengths, H, D, causal):
 
 
 SETTLE_S = 0.25  # untimed sustained load before each timed block
+COLD_MIB = 512  # written between cold launches: twice the 256 MB MALL
 
 
 def settle(call, torch, seconds=SETTLE_S):
@@ -73,6 +75,29 @@ def settle(call, torch, seconds=SETTLE_S):
         if n % 8 == 0:
             torch.cuda.synchronize()  # keep the host within a few launches of the GPU
     torch.cuda.synchronize()
+
+
+def launch_stats(call, torch, stream, n, cold_buf=None):
+    """Median and minimum duration (ms) of n launches of `call`, each between
+    its own pair of HIP events on the launch stream, after 10 untimed ones.
+    The events add their own processing to every sample, so these sit a few
+    microseconds above the block averages.  With `cold_buf`, the buffer is
+    overwritten before every launch (outside its events), so neither the
+    L2 caches nor the MALL hold any of the inputs when the launch starts."""
+    for _ in range(10):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        if cold_buf is not None:
+            cold_buf.fill_(i & 0xFF)
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    return {"launches": n, "median_ms": float(np.median(t)), "min_ms": t[0], "max_ms": t[-1]}
 
 
 def cpu_baseline(x, budget_s=12.0):
@@ -131,6 +156,11 @@ def main():
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-bias", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed back-to-back calls before each timed block")
+    ap.add_argument("--launch-stats", type=int, default=50,
+                    help="launches per mask for the per-launch median/min (warm and cold MALL) "
+                         "of the headline kernels; 0 skips them")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (a kernel of "
                          "known HBM traffic, for scaling counter readings)")
@@ -180,10 +210,10 @@ def main():
         log(f"calibration copy: {n} bytes read + {n} bytes written per launch, 3 launches")
         del src, dst
 
-    log(f"warmup {args.warmup} steps on {wl}, then {SETTLE_S} s of untimed steps")
+    log(f"warmup {args.warmup} steps on {wl}, then {args.settle_s} s of untimed steps")
     for _ in range(args.warmup):
         step()
-    settle(step, torch)
+    settle(step, torch, args.settle_s)
 
     # The timed region runs the K steps' non-causal forwards back to back, then
     # their causal forwards, with HIP events on the launch stream only at the
@@ -208,7 +238,8 @@ def main():
     nc_avg = ev[0].elapsed_time(ev[1]) / args.steps
     c_avg = ev[1].elapsed_time(ev[2]) / args.steps
     achieved = f_nc / (nc_avg * 1e-3) / 1e12
-    traffic = traffic_from_profiles("dense_bf16_b4h16s2048d128_noncausal")
+    traffic = traffic_from_profiles()
+    clock = clock_from_profiles()
 
     breakdown = {
         "noncausal": {"flops": f_nc, "avg_ms": nc_avg, "tflops": achieved,
@@ -224,7 +255,7 @@ def main():
         n = n or args.steps
         for _ in range(args.warmup):
             call()
-        settle(call, torch)
+        settle(call, torch, args.settle_s)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         e[0].record(stream)
@@ -233,6 +264,17 @@ def main():
         e[1].record(stream)
         torch.cuda.synchronize()
         return e[0].elapsed_time(e[1]) / n
+
+    if args.launch_stats > 0:
+        # Per-launch statistics of the headline kernels: warm (inputs resident
+        # in the caches as far as they fit, as in the timed steps) and cold.
+        cold = torch.empty(COLD_MIB << 20, dtype=torch.uint8, device=dev)
+        for name, call in (("noncausal", fwd_noncausal), ("causal", fwd_causal)):
+            settle(call, torch, args.settle_s)
+            warm = launch_stats(call, torch, stream, args.launch_stats)
+            cold_s = launch_stats(call, torch, stream, args.launch_stats, cold_buf=cold)
+            breakdown[name]["per_launch"] = {"warm": warm, f"cold_after_{COLD_MIB}MiB_write": cold_s}
+        del cold
 
     if not args.no_varlen:
         vx = inputs.workload("thd_bf16_16seq_len1to4096_h16d128_causal")
@@ -375,10 +417,16 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
+                     "shader_clock_ghz": clock,
+                     "frac_at_shader_clock": (achieved / (PEAK_BF16_TFLOPS * clock / 2.4)
+                                              if clock else None),
+                     "clock_source": "GRBM_GUI_ACTIVE per XCD over the dispatch duration in the "
+                                     "committed rocprofv3 counter pass of these kernel sources "
+                                     "(null when the sources changed since)",
                      "kernel": "attn_fwd_kernel<bf16, D=128, dense, non-causal>",
                      "flops_per_launch": f_nc, "avg_launch_ms": nc_avg},
         "breakdown": breakdown,
-        "settle_s_before_each_block": SETTLE_S,
+        "settle_s_before_each_block": args.settle_s,
         "kernel_source_sha": kernel_source_hash(),
         "cpu_baseline": None,
     }

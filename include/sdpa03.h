@@ -375,7 +375,7 @@ sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t tot
  * ahead-of-time autotune probing sequence lengths, head dim and dtype that
  * guides which kernel serves an input): seqlen_q and seqlen_k are the dense
  * lengths, the varlen calls'
- * max_seqlen_q / max_seqlen_k, or the padded calls' seqlen_*_max, in three
+ * max_seqlen_q / max_seqlen_k, or the padded calls' seqlen_*_max, in four
  * query buckets (<= 128, <= 512, <= 4096, longer) and two key buckets (<= 512,
  * longer).  causal and mode are accepted for a finer key later and do not
  * change the choice today (mode: 0 dense, 1 compact, 2 padded).

@@ -181,6 +181,28 @@ def check_cu_seqlens_host(cu, total: int, max_len: int) -> None:
     _check(load_library().sdpa_check_cu_seqlens_host(ptr, arr.size - 1, int(total), int(max_len)))
 
 
+def _outputs(q, out, lse, lse_shape):
+    """The output O (q's shape, dtype and device; any strides the library
+    accepts) and the fp32 logsumexp (contiguous, lse_shape) of a forward
+    call: the caller's, checked before anything is launched, or new ones.
+    The kernels write through these pointers, so a wrong size or type would
+    write out of bounds or garble the result."""
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out must have the shape, dtype and device of q: got "
+                         f"{tuple(out.shape)} {out.dtype} {out.device}, want {tuple(q.shape)} "
+                         f"{q.dtype} {q.device}")
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != tuple(lse_shape) or lse.dtype != torch.float32
+          or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)} on "
+                         f"{q.device}: got {tuple(lse.shape)} {lse.dtype} {lse.device}"
+                         f"{'' if lse.is_contiguous() else ' (not contiguous)'}")
+    return out, lse
+
+
 def _bias_view(bias, q, shape):
     """The bias broadcast (stride 0, no copy) to the rank-4 score view."""
     if not bias.is_cuda or bias.device != q.device:
@@ -203,8 +225,7 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, bias=None):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse = _outputs(q, out, lse, (B, H, Sq))
     if bias is None:
         _check(lib.attn_fwd(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -251,8 +272,7 @@ def attn_fwd_splitk(q, k, v, scale=None, causal=False, num_splits=0, out=None, l
     _, nbytes = splitk_plan(q.dtype, B, H, Sq, Sk, D, num_splits)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse = _outputs(q, out, lse, (B, H, Sq))
     _check(lib.attn_fwd_splitk(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
         _dtype_code(q), B, H, Sq, Sk, D,
@@ -354,8 +374,7 @@ def attn_fwd_compact_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=No
     if cu_q.numel() != cu_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k need the same length")
     num_seqs = cu_q.numel() - 1
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((1, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse = _outputs(q, out, lse, (1, H, Tq))
     # (T, H, D) token memory seen as the rank-4 view (1, H, T, D).
     qv, kv, vv, ov = (t.transpose(0, 1).unsqueeze(0) for t in (q, k, v, o))
     if bias is None:
@@ -395,8 +414,7 @@ def attn_fwd_padded_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, caus
     cu_k = _device_cu(cu_seqlens_k, q.device, B * Sk, Sk, check)
     if cu_q.numel() != B + 1 or cu_k.numel() != B + 1:
         raise ValueError("padded varlen needs B + 1 cu_seqlens entries")
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse = _outputs(q, out, lse, (B, H, Sq))
     if bias is None:
         _check(lib.attn_fwd_padded_varlen(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),

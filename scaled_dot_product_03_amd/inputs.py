@@ -175,3 +175,16 @@ def workload(name: str, seed: int | None = None) -> AttnInputs:
     if seed is not None:
         kwargs["seed"] = seed
     return builder(**kwargs)
+
+
+def workload_lengths(name: str, seed: int | None = None) -> list:
+    """The per-sequence (or per-batch) true lengths of a variable-length
+    workload without drawing its tensors: step 1 of the recipe alone (the
+    lengths come first out of the generator, so they equal those of
+    ``workload(name, seed)``)."""
+    builder, kwargs = WORKLOADS[name]
+    if builder is dense_inputs:
+        raise ValueError(f"{name} is a dense workload")
+    n = kwargs["n_seqs"] if builder is compact_inputs else kwargs["B"]
+    rng = np.random.default_rng(kwargs["seed"] if seed is None else seed)
+    return rng.integers(kwargs["len_lo"], kwargs["len_hi"], size=n, endpoint=True).tolist()

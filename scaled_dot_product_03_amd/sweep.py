@@ -253,23 +253,35 @@ def run(only=None):
         env = dict(os.environ, SDPA03_LIBRARY=lib, SDPA03_SWEEP_CLASS=json.dumps(list(cls)))
         print(f"== {_name(cls, cand)}: parity", flush=True)
         t0 = time.time()
-        par = subprocess.run([sys.executable, "-u", "-m", "pytest", "-x", "-q", "-m", "gpu",
-                              "--timeout", "300", "--timeout-method", "thread",
-                              os.path.join(ROOT, "tests", "test_gpu_parity.py")],
-                             cwd=ROOT, env=env, capture_output=True, text=True)
+        try:
+            par = subprocess.run([sys.executable, "-u", "-m", "pytest", "-x", "-q", "-m", "gpu",
+                                  "--timeout", "300", "--timeout-method", "thread",
+                                  os.path.join(ROOT, "tests", "test_gpu_parity.py")],
+                                 cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+        except subprocess.TimeoutExpired as e:
+            raise SweepFault(f"parity run of {_name(cls, cand)} exceeded 900 s") from e
         tail = par.stdout.strip().splitlines()[-1:] if par.stdout else []
         print(f"   parity rc={par.returncode} {tail} ({time.time() - t0:.0f} s)", flush=True)
+        if child_faulted(par.returncode, par.stdout + par.stderr):
+            print(par.stdout[-3000:] + par.stderr[-3000:], flush=True)
+            raise SweepFault(f"parity run of {_name(cls, cand)} ended abnormally "
+                             f"(rc {par.returncode}); no further candidate is run")
         entry = {"dtype": cls[0], "head_dim": cls[1], "cand": list(cand),
                  "parity": par.returncode == 0, "ms": None}
         if par.returncode == 0:
-            tim = subprocess.run([sys.executable, "-u", "-c",
-                                  "import sys; sys.path.insert(0, %r); "
-                                  "from scaled_dot_product_03_amd import sweep; "
-                                  "sweep._timing_child(%r)" % (ROOT, lib)],
-                                 cwd=ROOT, env=env, capture_output=True, text=True)
+            try:
+                tim = subprocess.run([sys.executable, "-u", "-c",
+                                      "import sys; sys.path.insert(0, %r); "
+                                      "from scaled_dot_product_03_amd import sweep; "
+                                      "sweep._timing_child(%r)" % (ROOT, lib)],
+                                     cwd=ROOT, env=env, capture_output=True, text=True,
+                                     timeout=600)
+            except subprocess.TimeoutExpired as e:
+                raise SweepFault(f"timing of {_name(cls, cand)} exceeded 600 s") from e
             m = re.search(r"SWEEP_TIMINGS (.*)", tim.stdout)
             if tim.returncode != 0 or not m:
-                raise RuntimeError(f"timing of {_name(cls, cand)} failed: {tim.stderr[-2000:]}")
+                raise SweepFault(f"timing of {_name(cls, cand)} failed (rc {tim.returncode}): "
+                                 f"{tim.stderr[-2000:]}")
             entry["ms"] = json.loads(m.group(1))
             print(f"   ms {entry['ms']}", flush=True)
         else:
@@ -277,6 +289,27 @@ def run(only=None):
         results.append(entry)
         with open(RESULTS, "w") as f:
             json.dump(results, f, indent=1)
+
+
+# Text that marks a child run as ended by the GPU or the runtime rather than
+# by a failed comparison.
+_FAULT_MARKS = ("Memory access fault", "GPU core dump", "hipError", "HIP error",
+                "Segmentation fault", "Aborted", "core dumped", "Timeout", "timed out",
+                "HSA_STATUS_ERROR")
+
+
+def child_faulted(returncode, text):
+    """True when a child process (a parity or timing run) ended by a signal, a
+    time limit, a return code other than pytest's 0 (passed) and 1 (tests
+    failed), or with fault text in its output: the sweep must stop there and
+    launch no further GPU work.  Plain test failures are not faults."""
+    if returncode is None or returncode < 0 or returncode not in (0, 1):
+        return True
+    return any(m in (text or "") for m in _FAULT_MARKS)
+
+
+class SweepFault(RuntimeError):
+    """A candidate's GPU run ended abnormally; the sweep stops."""
 
 
 def _entry(cand):

@@ -369,6 +369,46 @@ def test_errors_leave_outputs_untouched(case):
     assert (o == 3.0).all() and (lse == 5.0).all()
 
 
+@pytest.mark.parametrize("entry", ["dense", "splitk", "compact", "padded"])
+@pytest.mark.parametrize("bad", ["lse_short", "lse_dtype", "lse_strided", "out_shape",
+                                 "out_dtype"])
+def test_wrong_output_buffers_are_refused_before_launch(entry, bad):
+    """A caller's out or lse of the wrong shape, type or layout is refused by
+    the binding before anything is launched (the kernels write through those
+    pointers), and neither buffer changes."""
+    B, H, S, D = 2, 2, 64, 64
+    q = torch.randn((B, H, S, D), device=DEV).bfloat16()
+    if entry == "compact":
+        q = torch.randn((B * S, H, D), device=DEV).bfloat16()
+        lse_shape = (1, H, B * S)
+    else:
+        lse_shape = (B, H, S)
+    o = torch.full_like(q, 3.0)
+    lse = torch.full(lse_shape, 5.0, device=DEV)
+    if bad == "lse_short":
+        lse = torch.full(lse_shape[:-1] + (lse_shape[-1] - 1,), 5.0, device=DEV)
+    elif bad == "lse_dtype":
+        lse = torch.full(lse_shape, 5.0, device=DEV, dtype=torch.float64)
+    elif bad == "lse_strided":
+        lse = torch.full(lse_shape[:-1] + (2 * lse_shape[-1],), 5.0, device=DEV)[..., ::2]
+    elif bad == "out_shape":
+        o = torch.full(q.shape[:-1] + (D // 2,), 3.0, device=DEV).bfloat16()
+    else:
+        o = torch.full_like(q, 3.0, dtype=torch.float32)
+    cu = np.array([0, S, 2 * S], dtype=np.int32)
+    with pytest.raises(ValueError):
+        if entry == "dense":
+            binding.attn_fwd(q, q, q, out=o, lse=lse)
+        elif entry == "splitk":
+            binding.attn_fwd_splitk(q, q, q, out=o, lse=lse)
+        elif entry == "compact":
+            binding.attn_fwd_compact_varlen(q, q, q, cu, cu, out=o, lse=lse)
+        else:
+            binding.attn_fwd_padded_varlen(q, q, q, cu, cu, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (o == 3.0).all() and (lse == 5.0).all()
+
+
 def test_native_library_is_loaded():
     """The compute path is the in-tree HIP library, nothing else."""
     from scaled_dot_product_03_amd.build import LIB_PATH

@@ -47,11 +47,61 @@ def test_algorithmic_bytes_closed_forms():
     # its 128 rows, i.e. 128^2 * (1 + ... + 16) entries per (batch, head).
     c_bias = rocprof.algorithmic_bytes(rocprof.short_name(MANGLED_C_BIAS))
     assert c_bias == qkvo + B * H * 128 * 128 * (16 * 17 // 2) * 2
-    # Split launches and other head dims are not this workload's.
-    assert rocprof.algorithmic_bytes("attn_fwd_kernel<bf16, 128, 4, 1, 64, 2, 0, false, true, "
+    # A split launch needs the split count for its workspace bytes.
+    assert rocprof.algorithmic_bytes("attn_fwd_kernel<fp16, 64, 4, 1, 64, 2, 0, false, true, "
                                      "false>") is None
-    assert rocprof.algorithmic_bytes("attn_fwd_kernel<fp16, 64, 4, 1, 64, 2, 0, false, false, "
+    # Kernels of no bench workload.
+    assert rocprof.kernel_accounting("attn_fwd_kernel<fp32, 64, 4, 1, 32, 2, 0, false, false, "
                                      "false>") is None
+    assert rocprof.kernel_accounting("__amd_rocclr_copyBuffer") is None
+
+
+def test_accounting_of_every_bench_kernel():
+    # fp16 Sq 512 Sk 8192 D 64, B 2 H 32: unsplit, split in two, merge.
+    rq, rk, d = 2 * 32 * 512, 2 * 32 * 8192, 64
+    plain = rocprof.kernel_accounting("attn_fwd_kernel<fp16, 64, 4, 1, 64, 2, 0, false, false, "
+                                      "false>")
+    assert plain["workload"] == "dense_fp16_b2h32sq512sk8192d64"
+    assert plain["bytes"] == rq * (2 * d * 2 + 4) + rk * 2 * d * 2
+    assert plain["flops"] == 4.0 * 512 * 8192 * 64 * 32 * 2
+    split = rocprof.kernel_accounting("attn_fwd_kernel<fp16, 64, 4, 1, 64, 2, 0, false, true, "
+                                      "false>", splits=2)
+    assert split["bytes"] == rq * d * 2 + rk * 2 * d * 2 + 2 * rq * (d + 1) * 4
+    assert split["flops"] == plain["flops"]
+    merge = rocprof.kernel_accounting("attn_fwd_merge_kernel<fp16, 64>", splits=2)
+    assert merge["bytes"] == 2 * rq * (d + 1) * 4 + rq * (d * 2 + 4)
+    assert merge["flops"] is None
+    # THD: 16 sequences of seed 4 (T = 40,702 tokens), H 16, causal.
+    thd = rocprof.kernel_accounting("attn_fwd_kernel<bf16, 128, 4, 1, 64, 2, 1, true, false, "
+                                    "false>")
+    assert thd["bytes"] == 16 * 40702 * (4 * 128 * 2 + 4)
+    assert thd["flops"] == pytest.approx(5.116e11, rel=1e-3)
+    # Padded: true lengths of seed 5 only (sum 42,230 rows), H 32, causal.
+    pad = rocprof.kernel_accounting("attn_fwd_kernel<bf16, 128, 8, 1, 64, 2, 2, true, false, "
+                                    "false>")
+    assert pad["bytes"] == 32 * 42230 * (4 * 128 * 2 + 4)
+    assert pad["flops"] == pytest.approx(1.982e12, rel=1e-3)
+    # Backward on the dense bf16 S2048 workload.
+    B, H, S, D = 4, 16, 2048, 128
+    r = B * H * S
+    prep = rocprof.kernel_accounting("attn_bwd_prep_kernel<bf16, 128, 0>")
+    assert prep["bytes"] == r * (2 * D * 2 + 4) + r * 8
+    dq = rocprof.kernel_accounting("attn_bwd_dq_kernel<bf16, 128, 0, false>")
+    assert dq["bytes"] == r * 3 * D * 2 + r * 2 * D * 2 + r * 8
+    assert dq["flops"] == 3 * 2.0 * S * S * D * B * H
+    dkdv = rocprof.kernel_accounting("attn_bwd_dkdv_kernel<bf16, 128, 0, true>")
+    assert dkdv["bytes"] == r * 2 * D * 2 + r * 8 + r * 4 * D * 2
+    assert dkdv["flops"] == 4 * 2.0 * S * S * D * B * H / 2
+
+
+def test_derived_counter_metrics():
+    c = {"SQ_VALU_MFMA_BUSY_CYCLES": 512.0, "SQ_ACTIVE_INST_VALU": 128.0,
+         "SQ_LDS_IDX_ACTIVE": 64.0, "GRBM_GUI_ACTIVE": 8.0, "_duration_ns": 0.5}
+    assert rocprof.mfma_busy_pct(c) == pytest.approx(50.0)   # 512 / (1 x 1024)
+    assert rocprof.valu_busy_pct(c) == pytest.approx(50.0)   # 128 / 256 / 1
+    assert rocprof.lds_util_pct(c) == pytest.approx(25.0)    # 64 / (1 x 256)
+    assert rocprof.clock_ghz(c) == pytest.approx(2.0)        # 1 cycle per 0.5 ns
+    assert rocprof.clock_ghz({"GRBM_GUI_ACTIVE": 8.0}) is None
 
 
 def _write_csv(path, header, rows):
@@ -92,6 +142,21 @@ def test_counter_parsing_sums_rows_of_a_dispatch_then_averages(tmp_path):
     assert rocprof.mfma_busy_pct(c[k]) == pytest.approx(100 * 500 / 1024)
 
 
+def test_counter_parsing_takes_dispatch_durations_from_the_same_run(tmp_path):
+    d = tmp_path / "sq"
+    _write_csv(str(d / "host" / "sq_counter_collection.csv"), COUNTER_HEADER, _counter_rows([
+        (1, MANGLED_NC, "GRBM_GUI_ACTIVE", 8.0e5),
+        (2, MANGLED_NC, "GRBM_GUI_ACTIVE", 8.0e5),
+    ]))
+    _write_csv(str(d / "host" / "sq_kernel_trace.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+               [[1, MANGLED_NC, 1000, 51000], [2, MANGLED_NC, 90000, 140000],
+                [3, COPY, 0, 10]])
+    c = rocprof.parse_counters(str(d))[rocprof.short_name(MANGLED_NC)]
+    assert c["_duration_ns"] == pytest.approx(50000.0)
+    assert rocprof.clock_ghz(c) == pytest.approx(2.0)  # 1e5 cycles per XCD in 50 us
+
+
 def test_stats_parsing(tmp_path):
     d = tmp_path / "trace"
     _write_csv(str(d / "host" / "trace_kernel_stats.csv"),
@@ -112,7 +177,7 @@ def test_traffic_summary_round_trips_into_bench(tmp_path, monkeypatch):
     write = {COPY: {"WRITE_SIZE": float(n_kib)}, k: {"WRITE_SIZE": 33000.0}}
     stats = {k: (10, 130.0, 127.0, 166.0, 60.0)}
     assert rocprof.copy_factors(fetch, write)[:2] == pytest.approx((2.0, 1.0))
-    path = tmp_path / f"hbm_traffic_{rocprof.TRAFFIC_TAG}.md"
+    path = tmp_path / rocprof.TRAFFIC_FILE
     rocprof.write_traffic(fetch, write, stats, ["rocprofv3 --pmc FETCH_SIZE -- python3 bench.py"],
                           str(path))
     want = (2 * 50000.0 + 33000.0) * 1024
@@ -132,7 +197,7 @@ def test_missing_calibration_copy_is_an_error():
 def test_committed_traffic_summary_parses():
     # bench.py's roofline.traffic comes from this file; it must stay readable
     # (it is None only when the kernel sources changed since it was taken).
-    path = os.path.join(rocprof.ROOT, "profiles", f"hbm_traffic_{rocprof.TRAFFIC_TAG}.md")
+    path = os.path.join(rocprof.ROOT, "profiles", rocprof.TRAFFIC_FILE)
     text = open(path).read()
     assert "kernel_source_sha:" in text and "hbm_bytes_per_launch:" in text
 

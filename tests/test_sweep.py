@@ -117,3 +117,17 @@ def test_every_candidate_class_offers_each_schedule():
     for cls, cands in sweep.CANDIDATES.items():
         scheds = {sweep._cand4(c)[3] for c in cands}
         assert scheds == {0, 1, 2}, (cls, scheds)
+
+
+def test_child_faults_stop_the_sweep_but_failed_comparisons_do_not():
+    # pytest's own outcomes: 0 passed, 1 some test failed (a wrong result).
+    assert not sweep.child_faulted(0, "12 passed")
+    assert not sweep.child_faulted(1, "1 failed, 11 passed")
+    # Signals, time limits, other exit codes and fault text end the sweep.
+    assert sweep.child_faulted(-11, "")
+    assert sweep.child_faulted(-6, "")
+    assert sweep.child_faulted(134, "")
+    assert sweep.child_faulted(None, "")
+    assert sweep.child_faulted(1, "Memory access fault by GPU node-2")
+    assert sweep.child_faulted(1, "+++ Timeout +++")
+    assert sweep.child_faulted(0, "hipErrorLaunchFailure")
