@@ -342,8 +342,8 @@ def parse_stats(d):
 
 
 def parse_counters(d):
-    """{short kernel name: {counter: mean over dispatches}}; a counter's rows
-    of one dispatch are summed first.  With a kernel trace in the same
+    """{short kernel name: {counter: mean over dispatches, counter#max: the
+    largest dispatch's}}; a counter's rows of one dispatch are summed first.  With a kernel trace in the same
     directory, '_duration_ns' is the mean dispatch duration."""
     per_dispatch = defaultdict(float)
     names = {}
@@ -362,7 +362,11 @@ def parse_counters(d):
     acc = defaultdict(lambda: defaultdict(list))
     for (disp, counter), val in per_dispatch.items():
         acc[names[disp]][counter].append(val)
-    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+    out = {}
+    for k, cs in acc.items():
+        out[k] = {c: sum(v) / len(v) for c, v in cs.items()}
+        out[k].update({c + "#max": max(v) for c, v in cs.items()})
+    return out
 
 
 def mfma_busy_pct(c):
@@ -461,10 +465,14 @@ def write_counters(counters, stats, cmd, path, splits=None):
 
 
 def copy_factors(fetch, write):
-    """Bytes per KiB of counter reading, from the plain copy's known traffic."""
+    """Bytes per KiB of counter reading, from the plain copy's known traffic.
+    The copy kernel also serves small uploads (cu_seqlens) in the same run,
+    so its largest dispatch -- the calibration copy -- is the one used."""
     n_kib = COPY_MIB * 1024
-    fc = [c["FETCH_SIZE"] for k, c in fetch.items() if "copyBuffer" in k and "FETCH_SIZE" in c]
-    wc = [c["WRITE_SIZE"] for k, c in write.items() if "copyBuffer" in k and "WRITE_SIZE" in c]
+    fc = [c.get("FETCH_SIZE#max", c.get("FETCH_SIZE")) for k, c in fetch.items()
+          if "copyBuffer" in k and "FETCH_SIZE" in c]
+    wc = [c.get("WRITE_SIZE#max", c.get("WRITE_SIZE")) for k, c in write.items()
+          if "copyBuffer" in k and "WRITE_SIZE" in c]
     if not fc or not wc:
         raise RuntimeError("the calibration copy kernel is missing from the counter results")
     return n_kib / max(fc), n_kib / max(wc), max(fc), max(wc)
@@ -534,6 +542,9 @@ def parse_args(argv=None):
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--limit", type=int, default=240, help="seconds per rocprofv3 run")
+    ap.add_argument("--summarize", action="store_true",
+                    help="run nothing: write the summaries from the results an earlier run "
+                         "left under --out (a GPU box returns only that directory)")
     args = ap.parse_args(argv)
     bad = [p for p in args.passes if p not in PASSES]
     if bad:
@@ -542,31 +553,54 @@ def parse_args(argv=None):
     return args
 
 
+def _runs(steps):
+    """(profiler options, output prefix, bench arguments) of every pass."""
+    short = ["--steps", "3", "--warmup", "1"] + PROFILED
+    cal = short + ["--calibrate-copy-mib", str(COPY_MIB)]
+    return {
+        "trace": [(["--kernel-trace", "--stats"], "trace",
+                   ["--steps", str(steps), "--warmup", "5", "--no-cpu-baseline"])],
+        "counters": [(["--kernel-trace", "--pmc"] + SQ_COUNTERS, "sq", short)],
+        "traffic": [(["--pmc", "FETCH_SIZE"], "fetch", cal), (["--pmc", "WRITE_SIZE"], "write", cal)],
+    }
+
+
+def _command_text(opts, out_dir, prefix, bench_args):
+    d = os.path.join(out_dir, prefix)
+    return " ".join(["rocprofv3"] + opts + ["--output-format", "csv", "-d",
+                                            os.path.relpath(d, ROOT), "-o", prefix, "--",
+                                            "python3", "bench.py"] + bench_args)
+
+
 def main(argv=None):
     args = parse_args(argv)
     out = os.path.abspath(args.out)
     os.makedirs(out, exist_ok=True)
     os.makedirs(args.profiles, exist_ok=True)
+    runs = _runs(args.steps)
+    if not args.summarize:
+        for p in args.passes:
+            for opts, prefix, bench_args in runs[p]:
+                _rocprof(opts, out, prefix, bench_args, args.limit)
+
+    def dir_cmd_log(opts, prefix, bench_args):
+        return (os.path.join(out, prefix), _command_text(opts, out, prefix, bench_args),
+                os.path.join(out, f"{prefix}.log"))
 
     stats, splits = None, None
-    if "trace" in args.passes:
-        d, cmd, log = _rocprof(["--kernel-trace", "--stats"], out, "trace",
-                               ["--steps", str(args.steps), "--warmup", "5", "--no-cpu-baseline"],
-                               args.limit)
+    if "trace" in args.passes or os.path.isdir(os.path.join(out, "trace")):
+        d, cmd, log = dir_cmd_log(*runs["trace"][0])
         stats = parse_stats(d)
-        splits = split_count(bench_record(log))
-        write_trace(stats, cmd, os.path.join(args.profiles, TRACE_FILE))
-    short = ["--steps", "3", "--warmup", "1"] + PROFILED
+        splits = split_count(bench_record(log)) if os.path.exists(log) else None
+        if "trace" in args.passes:
+            write_trace(stats, cmd, os.path.join(args.profiles, TRACE_FILE))
     if "counters" in args.passes:
-        d, cmd, log = _rocprof(["--kernel-trace", "--pmc"] + SQ_COUNTERS, out, "sq", short,
-                               args.limit)
+        d, cmd, log = dir_cmd_log(*runs["counters"][0])
         splits = splits or split_count(bench_record(log))
         write_counters(parse_counters(d), stats, cmd, os.path.join(args.profiles, COUNTERS_FILE),
                        splits)
     if "traffic" in args.passes:
-        cal = short + ["--calibrate-copy-mib", str(COPY_MIB)]
-        df, cf, logf = _rocprof(["--pmc", "FETCH_SIZE"], out, "fetch", cal, args.limit)
-        dw, cw, _ = _rocprof(["--pmc", "WRITE_SIZE"], out, "write", cal, args.limit)
+        (df, cf, logf), (dw, cw, _) = [dir_cmd_log(*r) for r in runs["traffic"]]
         splits = splits or split_count(bench_record(logf))
         write_traffic(parse_counters(df), parse_counters(dw), stats, [cf, cw],
                       os.path.join(args.profiles, TRAFFIC_FILE), splits)

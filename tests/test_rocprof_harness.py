@@ -189,6 +189,20 @@ def test_traffic_summary_round_trips_into_bench(tmp_path, monkeypatch):
     assert rocprof.traffic_from_profiles(profiles_dir=str(tmp_path)) is None
 
 
+def test_calibration_uses_the_largest_copy_dispatch(tmp_path):
+    # Small uploads share the copy kernel's name; their dispatches must not
+    # dilute the calibration copy's reading.
+    n_kib = rocprof.COPY_MIB * 1024
+    d = tmp_path / "fetch"
+    _write_csv(str(d / "host" / "fetch_counter_collection.csv"), COUNTER_HEADER, _counter_rows([
+        (1, COPY, "FETCH_SIZE", 0.1), (2, COPY, "FETCH_SIZE", n_kib / 2),
+        (3, COPY, "FETCH_SIZE", 0.1), (4, COPY, "FETCH_SIZE", n_kib / 2),
+    ]))
+    fetch = rocprof.parse_counters(str(d))
+    write = {COPY: {"WRITE_SIZE": 1.0, "WRITE_SIZE#max": float(n_kib)}}
+    assert rocprof.copy_factors(fetch, write)[:2] == pytest.approx((2.0, 1.0))
+
+
 def test_missing_calibration_copy_is_an_error():
     with pytest.raises(RuntimeError):
         rocprof.copy_factors({"x": {"FETCH_SIZE": 1.0}}, {"x": {"WRITE_SIZE": 1.0}})
