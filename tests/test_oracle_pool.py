@@ -1,0 +1,61 @@
+"""The process-pool driver of the full-size GPU comparisons, on the CPU: it
+must reproduce the oracle head by head (zero error when handed the oracle's
+own outputs) in every layout and element type, and must see an error planted
+in one element of the compared output."""
+
+import numpy as np
+import torch
+
+from oracle import sdpa_compact_varlen, sdpa_dense, sdpa_padded_varlen
+from oracle_pool import compare_all_heads
+from scaled_dot_product_03_amd import inputs
+
+
+def _as(t, like):
+    return torch.from_numpy(np.ascontiguousarray(t)).to(like.dtype)
+
+
+def test_dense_bf16_zero_error_and_planted_error():
+    x = inputs.dense_inputs(2, 2, 40, 70, 64, "bf16", seed=5)
+    ro, rl = sdpa_dense(x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy(),
+                        x.scale, True)
+    tasks = [(b, h) for b in range(2) for h in range(2)]
+    # The oracle's O in float64 (no rounding): zero error everywhere.
+    s = compare_all_heads("dense", dict(q=x.q, k=x.k, v=x.v, o=ro, lse=rl), tasks, x.scale, True)
+    assert s["max_o"] == 0.0 and s["max_lse"] == 0.0 and s["elements"] == 2 * 2 * 40 * 64
+    assert s["all_finite"]
+    bad = ro.copy()
+    bad[1, 0, 17, 5] += 0.25
+    s = compare_all_heads("dense", dict(q=x.q, k=x.k, v=x.v, o=bad, lse=rl), tasks, x.scale, True)
+    assert abs(s["max_o"] - 0.25) < 1e-12
+    # bf16-rounded outputs are read back as bf16, exactly.
+    o16 = _as(ro, x.q)
+    s = compare_all_heads("dense", dict(q=x.q, k=x.k, v=x.v, o=o16, lse=rl), tasks, x.scale, True)
+    assert s["max_o"] == float(np.abs(o16.double().numpy() - ro).max())
+
+
+def test_compact_and_padded_layouts():
+    y = inputs.compact_inputs(3, 2, 64, "fp16", seed=6, len_lo=1, len_hi=50)
+    ro, rl = sdpa_compact_varlen(y.q.double().numpy(), y.k.double().numpy(),
+                                 y.v.double().numpy(), y.cu_seqlens_q, y.cu_seqlens_k, y.scale,
+                                 True)
+    cu = y.cu_seqlens_q
+    tasks = [(h, int(cu[z]), int(cu[z + 1])) for z in range(3) for h in range(2)]
+    lse = rl[None].astype(np.float32)  # (1, H, T) like the library's output
+    s = compare_all_heads("compact", dict(q=y.q, k=y.k, v=y.v, o=ro, lse=lse), tasks, y.scale,
+                          True)
+    assert s["max_o"] == 0.0 and s["max_lse"] < 1e-5 and s["elements"] == int(cu[-1]) * 2 * 64
+
+    p = inputs.padded_inputs(2, 2, 48, 48, 128, "bf16", seed=7, len_lo=5, len_hi=48)
+    ro, rl = sdpa_padded_varlen(p.q.double().numpy(), p.k.double().numpy(), p.v.double().numpy(),
+                                p.cu_seqlens_q, p.cu_seqlens_k, p.scale, True)
+    L = p.meta["lengths_q"]
+    o = np.full(p.q.shape, np.nan)
+    lse = np.full(p.q.shape[:3], np.nan)
+    for b in range(2):  # rows past the true lengths stay NaN and are never compared
+        o[b, :, :L[b]] = ro[b, :, :L[b]]
+        lse[b, :, :L[b]] = rl[b, :, :L[b]]
+    tasks = [(b, h, int(L[b])) for b in range(2) for h in range(2)]
+    s = compare_all_heads("padded", dict(q=p.q, k=p.k, v=p.v, o=o, lse=lse), tasks, p.scale,
+                          True)
+    assert s["max_o"] == 0.0 and s["all_finite"]
