@@ -89,8 +89,14 @@ typedef enum {
   SDPA_ERR_SEQLEN = 8,    /* bad sequence-length arguments or cu_seqlens contents */
   SDPA_ERR_SCALE = 9,     /* scale is not finite and positive */
   SDPA_ERR_HIP = 10,      /* the HIP runtime rejected the launch */
-  SDPA_ERR_WORKSPACE = 11 /* split forward: workspace NULL, misaligned or too small */
+  SDPA_ERR_WORKSPACE = 11, /* split forward: workspace NULL, misaligned or too small */
+  SDPA_ERR_SCRATCH = 12    /* attn_fwd_splitk_noalloc: the plan needs more than the
+                              library's static scratch (SDPA_NOALLOC_SCRATCH_BYTES) */
 } sdpa_status;
+
+/* Bytes of the library's static per-device scratch that
+ * attn_fwd_splitk_noalloc uses in place of a caller's workspace. */
+#define SDPA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Static text for a status code (never NULL). */
 const char* sdpa_status_string(sdpa_status status);
@@ -253,6 +259,39 @@ sdpa_status attn_fwd_splitk(const void* q, const void* k, const void* v, void* o
                             const int64_t v_stride[4], const int64_t o_stride[4],
                             float scale, int32_t causal, int32_t num_splits, void* workspace,
                             uint64_t workspace_bytes, void* hip_stream);
+
+/*
+ * The split forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  Same arguments and results as
+ * attn_fwd_splitk, minus workspace and workspace_bytes: the partial outputs
+ * and logsumexps go to a static buffer of SDPA_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * that the library holds on every GPU it runs on, from that GPU's first call
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); its first call on a device looks
+ * the buffer's address up once, with that device current.
+ *
+ *  - A problem whose plan (sdpa_fwd_splitk_plan with the same arguments)
+ *    needs more than SDPA_NOALLOC_SCRATCH_BYTES is refused with
+ *    SDPA_ERR_SCRATCH before anything is launched; e.g. 512 queries against
+ *    8192 keys at head_dim 64 for B = 2, H = 32 in two splits need 17 MB.
+ *  - Nothing in the buffer needs to start at zero: every partial result the
+ *    merge reads is written earlier in the same call.  Each call leaves its
+ *    own partial results behind.
+ *  - Every call on a GPU shares that GPU's buffer: calls that overlap in time
+ *    on one GPU (other streams, other host threads) race and may return
+ *    garbage.  Serialise them, or use attn_fwd_splitk with a workspace each.
+ *  - hip_stream must belong to the current device (SDPA_ERR_HIP otherwise).
+ * Errors as attn_fwd_splitk (without the workspace ones), plus
+ * SDPA_ERR_SCRATCH.
+ */
+sdpa_status attn_fwd_splitk_noalloc(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                    const int64_t q_stride[4], const int64_t k_stride[4],
+                                    const int64_t v_stride[4], const int64_t o_stride[4],
+                                    float scale, int32_t causal, int32_t num_splits,
+                                    void* hip_stream);
 
 /*
  * The split count attn_fwd_splitk will use for these sizes and request

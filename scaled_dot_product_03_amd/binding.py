@@ -25,7 +25,11 @@ STATUS_NAMES = {
     0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_DTYPE", 3: "SDPA_ERR_HEAD_DIM",
     4: "SDPA_ERR_SHAPE", 5: "SDPA_ERR_STRIDE", 6: "SDPA_ERR_ALIGN", 7: "SDPA_ERR_BATCH",
     8: "SDPA_ERR_SEQLEN", 9: "SDPA_ERR_SCALE", 10: "SDPA_ERR_HIP", 11: "SDPA_ERR_WORKSPACE",
+    12: "SDPA_ERR_SCRATCH",
 }
+
+# Bytes of the static scratch attn_fwd_splitk_noalloc uses (sdpa03.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = (
     "sdpa_status_string",
@@ -36,6 +40,7 @@ EXPORTED = (
     "attn_fwd_compact_varlen_bias",
     "attn_fwd_padded_varlen_bias",
     "attn_fwd_splitk",
+    "attn_fwd_splitk_noalloc",
     "sdpa_fwd_splitk_plan",
     "attn_bwd",
     "attn_bwd_compact_varlen",
@@ -104,6 +109,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_splitk.argtypes = (
         [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _stride, _stride, _stride,
          _stride, ctypes.c_float, _i32, _i32, _p, ctypes.c_uint64, _p])
+    lib.attn_fwd_splitk_noalloc.restype = ctypes.c_int
+    lib.attn_fwd_splitk_noalloc.argtypes = (
+        [_p, _p, _p, _p, _p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _stride, _stride, _stride,
+         _stride, ctypes.c_float, _i32, _i32, _p])
     lib.sdpa_fwd_splitk_plan.restype = ctypes.c_int
     lib.sdpa_fwd_splitk_plan.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32, _i32p,
                                          ctypes.POINTER(ctypes.c_uint64)]
@@ -279,6 +288,32 @@ def attn_fwd_splitk(q, k, v, scale=None, causal=False, num_splits=0, out=None, l
         _strides(q), _strides(k), _strides(v), _strides(o),
         _scale(scale, D), int(bool(causal)), int(num_splits), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
+    return o, lse
+
+
+def attn_fwd_splitk_noalloc(q, k, v, scale=None, causal=False, num_splits=0, out=None,
+                            lse=None):
+    """The split forward on the library's static per-device scratch (no
+    workspace, nothing allocated by the library; calls that overlap on one
+    GPU race).  Same arguments and results as attn_fwd_splitk without
+    ``workspace``; a problem whose plan needs more than NOALLOC_SCRATCH_BYTES
+    raises SdpaError (SDPA_ERR_SCRATCH).  Pass ``out`` and ``lse`` to
+    allocate nothing here either."""
+    lib = load_library()
+    _require_gpu(q, k, v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    o, lse = _outputs(q, out, lse, (B, H, Sq))
+    with torch.cuda.device(q.device):
+        _check(lib.attn_fwd_splitk_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            _dtype_code(q), B, H, Sq, Sk, D,
+            _strides(q), _strides(k), _strides(v), _strides(o),
+            _scale(scale, D), int(bool(causal)), int(num_splits), _stream_handle(q.device)))
     return o, lse
 
 

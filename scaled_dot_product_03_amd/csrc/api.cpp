@@ -1,14 +1,24 @@
 // C-ABI entry points of libsdpa03.so: argument validation on the host, then
 // one kernel launch.  The declarations and the contract are in sdpa03.h.
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/sdpa03.h"
 #include "bwd_args.h"
 #include "fwd_args.h"
+
+// Scratch of attn_fwd_splitk_noalloc, for callers that cannot allocate: the
+// split forward's partial outputs and logsumexps.  Every GPU the library
+// runs on holds its own copy from the first call there until the process
+// ends.  In host code `scratch` is only the handle hipGetSymbolAddress
+// resolves (scratch_address below); kernels get the per-device address it
+// returns, never the name.
+static __device__ __align__(256) unsigned char scratch[SDPA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -313,6 +323,62 @@ sdpa_status padded_args(const void* q, const void* k, const void* v, void* o, fl
   return SDPA_OK;
 }
 
+// The two launches of a split forward whose arguments are validated and
+// whose workspace (partial outputs, then partial logsumexps, as the plan
+// lays them out) is at `workspace`.
+sdpa_status launch_split(FwdArgs& a, const SplitPlan& p, void* workspace, void* o, float* lse,
+                         sdpa_dtype dtype, int32_t H, int32_t seqlen_q, int32_t head_dim,
+                         int32_t causal, void* stream) {
+  a.m_tiles = p.m_tiles;
+  a.num_splits = p.splits;
+  a.split_tiles = p.split_tiles;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.o_bytes);
+  a.ws_rows = p.rows;
+  sdpa03::MergeArgs mg{};
+  mg.ws_o = a.ws_o;
+  mg.ws_lse = a.ws_lse;
+  mg.o = o;
+  mg.lse = lse;
+  mg.o_sb = a.o_sb;
+  mg.o_sh = a.o_sh;
+  mg.o_ss = a.o_ss;
+  mg.lse_sb = a.lse_sb;
+  mg.lse_sh = a.lse_sh;
+  mg.ws_rows = p.rows;
+  mg.num_heads = H;
+  mg.seqlen_q = seqlen_q;
+  mg.num_splits = p.splits;
+  const int err = sdpa03::launch_attn_fwd_split(a, mg, dtype, head_dim, causal != 0, stream);
+  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (that device current) on its first call.  The stream must belong to
+// the current device.
+sdpa_status scratch_address(void* stream, void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SDPA_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess || sdev != dev)
+      return SDPA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SDPA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return SDPA_OK;
+}
+
 sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, int mode,
                               int32_t causal, void* stream) {
   sdpa03::KernelConfig cfg;
@@ -458,6 +524,9 @@ const char* sdpa_status_string(sdpa_status status) {
     case SDPA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case SDPA_ERR_WORKSPACE:
       return "split forward workspace is NULL, not 16-byte aligned or smaller than the plan";
+    case SDPA_ERR_SCRATCH:
+      return "the problem needs more split-forward scratch than the library's static buffer "
+             "(SDPA_NOALLOC_SCRATCH_BYTES) holds";
   }
   return "unknown status";
 }
@@ -600,28 +669,28 @@ sdpa_status attn_fwd_splitk(const void* q, const void* k, const void* v, void* o
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 ||
       workspace_bytes < p.bytes)
     return SDPA_ERR_WORKSPACE;
-  a.m_tiles = p.m_tiles;
-  a.num_splits = p.splits;
-  a.split_tiles = p.split_tiles;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.o_bytes);
-  a.ws_rows = p.rows;
-  sdpa03::MergeArgs mg{};
-  mg.ws_o = a.ws_o;
-  mg.ws_lse = a.ws_lse;
-  mg.o = o;
-  mg.lse = lse;
-  mg.o_sb = a.o_sb;
-  mg.o_sh = a.o_sh;
-  mg.o_ss = a.o_ss;
-  mg.lse_sb = a.lse_sb;
-  mg.lse_sh = a.lse_sh;
-  mg.ws_rows = p.rows;
-  mg.num_heads = H;
-  mg.seqlen_q = seqlen_q;
-  mg.num_splits = p.splits;
-  const int err = sdpa03::launch_attn_fwd_split(a, mg, dtype, head_dim, causal != 0, hip_stream);
-  return err == 0 ? SDPA_OK : SDPA_ERR_HIP;
+  return launch_split(a, p, workspace, o, lse, dtype, H, seqlen_q, head_dim, causal, hip_stream);
+}
+
+sdpa_status attn_fwd_splitk_noalloc(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, sdpa_dtype dtype, int32_t B, int32_t H,
+                                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                    const int64_t q_stride[4], const int64_t k_stride[4],
+                                    const int64_t v_stride[4], const int64_t o_stride[4],
+                                    float scale, int32_t causal, int32_t num_splits,
+                                    void* hip_stream) {
+  FwdArgs a;
+  bool empty;
+  sdpa_status st = dense_args(q, k, v, o, lse, dtype, B, H, seqlen_q, seqlen_k, head_dim,
+                              q_stride, k_stride, v_stride, o_stride, scale, &a, &empty);
+  if (st != SDPA_OK || empty) return st;
+  SplitPlan p;
+  if ((st = split_plan(dtype, B, H, seqlen_q, seqlen_k, head_dim, num_splits, &p)) != SDPA_OK)
+    return st;
+  if (p.bytes > SDPA_NOALLOC_SCRATCH_BYTES) return SDPA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = scratch_address(hip_stream, &ws)) != SDPA_OK) return st;
+  return launch_split(a, p, ws, o, lse, dtype, H, seqlen_q, head_dim, causal, hip_stream);
 }
 
 sdpa_status attn_fwd_compact_varlen(const void* q, const void* k, const void* v, void* o,

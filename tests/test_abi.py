@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = binding.load_library()
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = lib.sdpa_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.sdpa_status_string(123).decode() == "unknown status"
@@ -224,6 +224,39 @@ def test_splitk_validation(kw, status):
 @no_gpu
 def test_splitk_empty_problem_is_ok_without_launch():
     assert _splitk(q=None, ws=None, Sq=0) == 0
+
+
+def _splitk_noalloc(**kw):
+    lib = binding.load_library()
+    a = dict(q=DUMMY, k=DUMMY, v=DUMMY, o=DUMMY, lse=DUMMY, dtype=2, B=1, H=2, Sq=8, Sk=512,
+             D=64, scale=0.125, splits=4)
+    a.update(kw)
+    st = _st(1024 * 64, 512 * 64, 64, 1)
+    return lib.attn_fwd_splitk_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dtype"],
+                                       a["B"], a["H"], a["Sq"], a["Sk"], a["D"], st, st, st, st,
+                                       a["scale"], 0, a["splits"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(D=32), 3), (dict(dtype=5), 2), (dict(scale=0.0), 9),
+    (dict(Sk=-1), 4),
+    # 65,536 rows x 16 splits x 65 floats (272 MB) exceed the 32 MiB scratch
+    (dict(B=128, H=64, Sq=8, Sk=16 * 1024, splits=16), 12),
+])
+def test_splitk_noalloc_validation(kw, status):
+    assert _splitk_noalloc(**kw) == status
+
+
+@no_gpu
+def test_splitk_noalloc_scratch_limit_matches_the_plan():
+    # The limit is the plan's workspace size: just over it is refused.
+    bf = torch.bfloat16
+    used, nbytes = binding.splitk_plan(bf, 128, 64, 8, 16 * 1024, 64, 16)
+    assert nbytes > binding.NOALLOC_SCRATCH_BYTES
+    used, nbytes = binding.splitk_plan(bf, 2, 64, 8, 16 * 1024, 64, 16)
+    assert nbytes <= binding.NOALLOC_SCRATCH_BYTES
+    assert _splitk_noalloc(q=None, Sq=0) == 0  # empty: nothing to do, no device touched
 
 
 # --- backward: workspace size and validation --------------------------------
