@@ -348,7 +348,6 @@ def main():
         bd = torch.empty((B, H, Sq, bpad), dtype=q.dtype, device=dev)[..., :Sk]
         bd.copy_(bias)
         del bias
-        bm_, bn_, _ = binding.kernel_config(torch.bfloat16, D, Sq, Sk, single_group=True)
         io_bytes = B * H * (2 * Sq * D * 2 + 2 * Sk * D * 2 + Sq * 4)
         entry = {"workload": "dense_bf16_b4h16s2048d128 (seed 2) + bias (B,H,Sq,Sk) bf16 seed 402"}
         for causal in (False, True):
@@ -356,6 +355,8 @@ def main():
                                                       out=o, lse=lse, bias=bd))
             if causal:
                 # query tile m reads key tiles 0 .. (m+1)*bm/bn - 1, bm rows each
+                bm_ = binding.kernel_config(torch.bfloat16, D, Sq, Sk, causal=True,
+                                            single_group=True)[0]
                 keys = sum(min(Sk, (m + 1) * bm_) for m in range((Sq + bm_ - 1) // bm_))
                 bias_bytes = B * H * bm_ * keys * 2
             else:

@@ -406,21 +406,21 @@ sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t tot
                                        int32_t max_len);
 
 /*
- * The compiled-in kernel choice of the forward (attn_fwd and the varlen
- * calls without a bias) for a problem: query rows per workgroup (block_m),
- * keys per tile (block_n) and wavefronts per workgroup.  The dispatch key
- * is the dtype, head_dim and the sequence extents, as in the tuning
- * database of AOTriton issue #12 (the maintainer's replies: an
- * ahead-of-time autotune probing sequence lengths, head dim and dtype that
- * guides which kernel serves an input): seqlen_q and seqlen_k are the dense
- * lengths, the varlen calls'
+ * The compiled-in kernel choice of the forward for a problem: query rows
+ * per workgroup (block_m), keys per tile (block_n) and wavefronts per
+ * workgroup.  The dispatch key is the dtype, head_dim, the sequence extents,
+ * the mask and the layout, as in the tuning database of AOTriton issue #12
+ * (the maintainer's replies: an ahead-of-time autotune probing sequence
+ * lengths, head dim and dtype that guides which kernel serves an input).
+ * seqlen_q and seqlen_k are the dense lengths, the varlen calls'
  * max_seqlen_q / max_seqlen_k, or the padded calls' seqlen_*_max, in four
- * query buckets (<= 128, <= 512, <= 4096, longer) and two key buckets (<= 512,
- * longer).  causal and mode are accepted for a finer key later and do not
- * change the choice today (mode: 0 dense, 1 compact, 2 padded).
- * single_group != 0 asks for the shape of the split forward and of the
- * forward with a bias, which never use the two-group (ping-pong) schedule.
- * Any output pointer may be NULL.  Returns SDPA_ERR_DTYPE /
+ * query buckets (<= 128, <= 512, <= 4096, longer) and two key buckets
+ * (<= 512, longer); causal != 0 selects the causal entries and mode the
+ * layout's (0 dense, 1 compact, 2 padded; the two variable-length layouts
+ * share their entries).  single_group != 0 asks for the shape of the forward
+ * with a bias (for its mask and layout) and of the split forward, which
+ * uses the dense non-causal entry for both masks (query it with causal = 0,
+ * mode = 0).  Any output pointer may be NULL.  Returns SDPA_ERR_DTYPE /
  * SDPA_ERR_HEAD_DIM for unsupported classes, SDPA_ERR_SHAPE for a bad mode
  * or negative length.
  */

@@ -173,8 +173,10 @@ def _require_gpu(*ts):
 def kernel_config(dtype: torch.dtype, head_dim: int, seqlen_q: int, seqlen_k: int,
                   causal: bool = False, mode: int = 0, single_group: bool = False):
     """(block_m, block_n, waves) of the compiled forward kernel for these
-    sizes (varlen: the longest sequence's lengths); single_group for the
-    split forward and the forward with a bias."""
+    sizes (varlen: the longest sequence's lengths), mask and layout (mode 0
+    dense, 1 compact, 2 padded); single_group for the forward with a bias
+    and for the split forward (which uses causal=False, mode=0 for both
+    masks)."""
     lib = load_library()
     bm, bn, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib.sdpa_kernel_config(_DTYPE_CODES.get(dtype, _BAD_DTYPE), head_dim, int(causal), mode,

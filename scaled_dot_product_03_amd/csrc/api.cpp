@@ -186,7 +186,8 @@ sdpa_status split_plan(int dtype, int32_t B, int32_t H, int32_t seqlen_q, int32_
   if (head_dim != 64 && head_dim != 128) return SDPA_ERR_HEAD_DIM;
   if (B < 0 || H < 0 || seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
   sdpa03::KernelConfig cfg;
-  if (!sdpa03::kernel_config(dtype, head_dim, seqlen_q, seqlen_k, true, &cfg))
+  if (!sdpa03::kernel_config(dtype, head_dim, seqlen_q, seqlen_k, false, sdpa03::MODE_DENSE, true,
+                             &cfg))
     return SDPA_ERR_HEAD_DIM;
   const int64_t key_tiles = (static_cast<int64_t>(seqlen_k) + cfg.block_n - 1) / cfg.block_n;
   const int64_t m_tiles = (static_cast<int64_t>(seqlen_q) + cfg.block_m - 1) / cfg.block_m;
@@ -382,7 +383,8 @@ sdpa_status scratch_address(void* stream, void** addr) {
 sdpa_status finish_and_launch(FwdArgs& a, sdpa_dtype dtype, int32_t head_dim, int mode,
                               int32_t causal, void* stream) {
   sdpa03::KernelConfig cfg;
-  if (!sdpa03::kernel_config(dtype, head_dim, a.seqlen_q, a.seqlen_k, a.bias != nullptr, &cfg))
+  if (!sdpa03::kernel_config(dtype, head_dim, a.seqlen_q, a.seqlen_k, causal != 0, mode,
+                             a.bias != nullptr, &cfg))
     return SDPA_ERR_HEAD_DIM;
   const int64_t m_tiles = (static_cast<int64_t>(a.seqlen_q) + cfg.block_m - 1) / cfg.block_m;
   const int64_t grid = m_tiles * a.num_heads * static_cast<int64_t>(a.num_z);
@@ -617,9 +619,9 @@ sdpa_status sdpa_kernel_config(sdpa_dtype dtype, int32_t head_dim, int32_t causa
   if (!dtype_ok(dtype)) return SDPA_ERR_DTYPE;
   if (mode < 0 || mode > 2) return SDPA_ERR_SHAPE;
   if (seqlen_q < 0 || seqlen_k < 0) return SDPA_ERR_SHAPE;
-  (void)causal;
   sdpa03::KernelConfig cfg;
-  if (!sdpa03::kernel_config(dtype, head_dim, seqlen_q, seqlen_k, single_group != 0, &cfg))
+  if (!sdpa03::kernel_config(dtype, head_dim, seqlen_q, seqlen_k, causal != 0, mode,
+                             single_group != 0, &cfg))
     return SDPA_ERR_HEAD_DIM;
   if (block_m) *block_m = cfg.block_m;
   if (block_n) *block_n = cfg.block_n;

@@ -6,14 +6,17 @@
 
 namespace sdpa03 {
 
-bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool single_group,
-                   KernelConfig* cfg) {
+bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool causal, int mode,
+                   bool single_group, KernelConfig* cfg) {
   if (head_dim != 64 && head_dim != 128) return false;
   const int b = seq_bucket(seqlen_q, seqlen_k);
+  const int v = mask_variant(causal, mode);
   auto pick = [&](auto tag) {
     using T = decltype(tag);
-    if (head_dim == 64) return single_group ? entry_for<T, 64, true>(b) : entry_for<T, 64, false>(b);
-    return single_group ? entry_for<T, 128, true>(b) : entry_for<T, 128, false>(b);
+    if (head_dim == 64) {
+      return single_group ? entry_for<T, 64, true>(b, v) : entry_for<T, 64, false>(b, v);
+    }
+    return single_group ? entry_for<T, 128, true>(b, v) : entry_for<T, 128, false>(b, v);
   };
   TableEntry e;
   switch (dtype) {

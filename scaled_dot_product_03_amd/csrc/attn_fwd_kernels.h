@@ -214,6 +214,35 @@ struct Path16 {
     }
   }
 
+  // The single phase of the lagged schedule: the next tile's scores and the
+  // previous tile's P.V on the matrix cores, this tile's probabilities on
+  // the VALU.  Keep a few LDS reads ahead; per product one or two reads (the
+  // K reads of Q.K^T and the transposing V reads of P.V) and an even share
+  // of the softmax VALU work.
+  template <int NB, int DB>
+  __device__ static __forceinline__ void interleave_lag() {
+    constexpr int n_qk = NB * kQFrags;
+    constexpr int n_pv = NB * 2 * DB;
+    constexpr int n_mfma = n_qk + n_pv;
+    constexpr int n_reads = n_qk + 2 * n_pv;
+    constexpr int valu_per = (NB * 16 * 4 + n_mfma - 1) / n_mfma;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < n_mfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      // reads after product i (the branches fold away once the loop unrolls)
+      const int r = (n_reads * (i + 1)) / n_mfma - (n_reads * i) / n_mfma;
+      if (r == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      } else if (r == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      } else if (r >= 3) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, valu_per, 0);
+    }
+  }
+
   // One C interval of the ping-pong schedule: the scores of the next tile
   // and P.V of the current one, both on the matrix cores; keep a few LDS
   // reads ahead of the products.
@@ -367,6 +396,8 @@ struct Path32 {
   __device__ static __forceinline__ void interleave_qk() {}
   template <int NB, int DB, int RB = 1>
   __device__ static __forceinline__ void interleave_pv() {}
+  template <int NB, int DB>
+  __device__ static __forceinline__ void interleave_lag() {}
 
   template <int NB>
   __device__ static __forceinline__ float softmax_p(const f32x16 (&s)[NB], float c2, float m_sub,
@@ -593,6 +624,12 @@ struct Stage {
   static constexpr int value = S;
 };
 
+// A compile-time flag passed to the step bodies.
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // The LDS arrays of the K and V stages.  Separate arrays (not one
 // [STAGES][...] array): each is its own alias scope, so the compiler can see
 // that fragment reads of one stage do not depend on the tile copies still
@@ -638,9 +675,10 @@ __device__ __forceinline__ StageArrays<T> stage_arrays(T* k0, T* k1, T* k2, T* k
 // scale * q.k + bias (natural-log units) and the softmax multiplies by
 // log2(e) alone.
 template <typename T, int D, int NW, int RB, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
-          bool BIAS>
+          bool BIAS, bool LAG = false>
 __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArrays<T>& st) {
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+  static_assert(!LAG || (RB == 1 && STAGES >= 3), "the lagged schedule: one row block, >= 3 stages");
   static_assert(RB == 1 || RB == 2, "one or two row blocks per wave");
   static_assert(!SPLIT || MODE == MODE_DENSE, "the split forward serves the dense mode");
   static_assert(!(SPLIT && BIAS), "the split forward has no bias");
@@ -824,6 +862,115 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
 
   f32x16 s[RB][NB];
   Bias bias_next[RB];
+  if constexpr (LAG) {
+    // Lagged schedule: step t turns tile t's scores into probabilities (VALU)
+    // while the matrix cores compute tile t+1's scores AND P(t-1).V(t-1), all
+    // in one interleaved phase, so a wave overlaps its own softmax with its
+    // own products (one wave per SIMD has no other wave to overlap with).
+    // V(t-1) is read one step after K(t-1), so tile t's V lands in stage
+    // t % STAGES as K does but is loaded STAGES - 2 steps ahead instead of
+    // STAGES: at step t, K(t+STAGES) goes into K(t)'s stage (read in step
+    // t-1) and V(t+STAGES-2) into V(t-2)'s (read in step t-1).  Both tiles
+    // a step reads were issued STAGES - 1 steps earlier.
+    if (n_tiles > 0) {
+      if constexpr (BIAS) load_bias(0, bias_next);
+#pragma unroll
+      for (int i = 0; i < STAGES; ++i) {
+        issue_k(i, i, i < n_tiles ? kend : 0);
+        if (i < STAGES - 2) issue_v(i, i, i < n_tiles ? kend : 0);
+      }
+      wait_vmem();
+      barrier_lds();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x16{};
+      Path::template qk<NB, 1>(st.k[0], lanes, qr, s);
+      if constexpr (BIAS) bias_next[0].fold(s[0], a.scale);
+      mask_tile(0, s);
+      // The stages are not refilled before every wave has read K(0).
+      barrier_lds();
+    }
+    PRegs p_prev[1];
+    // Step t (tile t+1 exists): K(t+1) in stage (t+1) % STAGES, V(t-1) in
+    // stage (t-1) % STAGES (absent at t = 0).
+    auto lag_step = [&](int t, auto stage, auto with_pv) {
+      constexpr int ST = decltype(stage)::value;
+      constexpr bool PV = decltype(with_pv)::value;
+      if constexpr (BIAS) load_bias(t + 1, bias_next);
+      issue_k(t + STAGES, ST, t + STAGES < n_tiles ? kend : 0);
+      issue_v(t + STAGES - 2, (ST + STAGES - 2) % STAGES, t + STAGES - 2 < n_tiles ? kend : 0);
+      PRegs p_cur[1];
+      f32x16 s_next[1][NB];
+      using P1 = typename Path::template PRegs<1>;
+      const float m_sub = (m_run[0] == kNegInf) ? 0.f : m_run[0];
+      float tile_sum = 0.f;
+      // One scheduling region per 32-key block: its probabilities, its
+      // scores of the next tile and its share of P(t-1).V(t-1), so only one
+      // block's operands are live at a time.
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        P1& pc = reinterpret_cast<P1&>(p_cur[0].f[nb]);
+        f32x16(&sn)[1][1] = reinterpret_cast<f32x16(&)[1][1]>(s_next[0][nb]);
+        sn[0][0] = f32x16{};
+        tile_sum += Path::template softmax_p<1>(reinterpret_cast<const f32x16(&)[1]>(s[0][nb]),
+                                                c2, m_sub, pc);
+        Path::template qk<1, 1>(st.k[(ST + 1) % STAGES] + nb * 32 * (Path::kRowK / sizeof(T)),
+                                lanes, qr, sn);
+        if constexpr (PV) {
+          Path::template pv<1, DB, 1>(st.v[(ST + STAGES - 1) % STAGES] +
+                                          nb * 32 * (Path::kRowV / sizeof(T)),
+                                      lanes, reinterpret_cast<const P1(&)[1]>(p_prev[0].f[nb]),
+                                      acc);
+          Path::pin(pc);
+          Path::template interleave_lag<1, DB>();
+        } else {
+          Path::pin(pc);
+          Path::template interleave_qk<1, 1>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // A rescale (rare) also rescales P(t-1).V(t-1), which used the old reference.
+      settle(0, s[0], p_cur[0], tile_sum);
+      if constexpr (BIAS) bias_next[0].fold(s_next[0], a.scale);
+      mask_tile(t + 1, s_next);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[0][nb] = s_next[0][nb];
+      p_prev[0] = p_cur[0];
+      // K(t+2) and V(t), issued STAGES - 2 steps before this one ends, must
+      // have landed before the next step.
+      wait_vmem_allow<kInFlightAtStepEnd>();
+      barrier_lds();
+    };
+    if (n_tiles > 1) {
+      lag_step(0, Stage<0>{}, Flag<false>{});
+      for (int t = 1;; t += STAGES) {
+        if (t + 1 >= n_tiles) break;
+        lag_step(t, Stage<1 % STAGES>{}, Flag<true>{});
+        if (t + 2 >= n_tiles) break;
+        lag_step(t + 1, Stage<2 % STAGES>{}, Flag<true>{});
+        if (t + 3 >= n_tiles) break;
+        lag_step(t + 2, Stage<3 % STAGES>{}, Flag<true>{});
+        if constexpr (STAGES > 3) {
+          if (t + 4 >= n_tiles) break;
+          lag_step(t + 3, Stage<4 % STAGES>{}, Flag<true>{});
+        }
+      }
+    }
+    if (n_tiles > 0) {
+      // The last tile: its probabilities beside P(n-2).V(n-2), then P(n-1).V(n-1)
+      // once every wave's share of V(n-1) has landed.
+      auto v_stage = [&](int t) {
+        const int i = t % STAGES;
+        return i == 0 ? st.v[0] : (i == 1 ? st.v[1] : (i == 2 ? st.v[2] : st.v[3]));
+      };
+      PRegs p_cur[1];
+      const float tile_sum = first_pass(0, s[0], p_cur[0]);
+      if (n_tiles > 1) Path::template pv<NB, DB, 1>(v_stage(n_tiles - 2), lanes, p_prev, acc);
+      settle(0, s[0], p_cur[0], tile_sum);
+      wait_vmem();
+      barrier_lds();
+      Path::template pv<NB, DB, 1>(v_stage(n_tiles - 1), lanes, p_cur, acc);
+    }
+  } else {
   if (n_tiles > 0) {
     // K(0), then K(i) and V(i-1) for i < STAGES: the order the step-end
     // waits count on.  (The full wait also settles Q's loads, which are the
@@ -957,6 +1104,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
     const int last = (n_tiles - 1) % STAGES;
     last_step(last == 0 ? st.v[0] : (last == 1 ? st.v[1] : (last == 2 ? st.v[2] : st.v[3])));
   }
+  }  // LAG
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
 #pragma unroll
@@ -1288,6 +1436,56 @@ __global__ __launch_bounds__(NW * 64, RB == 2 ? 1 : 2) void attn_fwd_kernel(FwdA
   }
 }
 
+// The single-group kernel built for three waves per SIMD: the launch bound
+// limits a wave to 168 registers, so three four-wave workgroups (or a
+// mix) share a CU where the LDS stages allow it.
+template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT, bool BIAS>
+__global__ __launch_bounds__(NW * 64, 3) void attn_fwd_3w_kernel(FwdArgs a) {
+  using Path = typename PathFor<T, D>::type;
+  constexpr int kES = static_cast<int>(sizeof(T));
+  constexpr int kKElems = Path::template KCopy<BN, NW>::kArrayBytes / kES;
+  constexpr int kVElems = Path::template VCopy<BN, NW>::kArrayBytes / kES;
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  if constexpr (STAGES == 2) {
+    attn_fwd_body<T, D, NW, 1, BN, 2, MODE, CAUSAL, SPLIT, BIAS>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds0, k_lds1, v_lds0, v_lds1, v_lds0, v_lds1));
+  } else {
+    static_assert(STAGES == 3, "two or three stages");
+    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+    attn_fwd_body<T, D, NW, 1, BN, 3, MODE, CAUSAL, SPLIT, BIAS>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds2, k_lds0, v_lds0, v_lds1, v_lds2, v_lds0));
+  }
+}
+
+// The lagged schedule (one row block per wave, three or four LDS stages).
+template <typename T, int D, int NW, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT, bool BIAS>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_lagged_kernel(FwdArgs a) {
+  static_assert(STAGES == 3 || STAGES == 4, "the lagged schedule keeps three or four stages");
+  using Path = typename PathFor<T, D>::type;
+  constexpr int kES = static_cast<int>(sizeof(T));
+  constexpr int kKElems = Path::template KCopy<BN, NW>::kArrayBytes / kES;
+  constexpr int kVElems = Path::template VCopy<BN, NW>::kArrayBytes / kES;
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+  if constexpr (STAGES == 3) {
+    attn_fwd_body<T, D, NW, 1, BN, 3, MODE, CAUSAL, SPLIT, BIAS, true>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds2, k_lds0, v_lds0, v_lds1, v_lds2, v_lds0));
+  } else {
+    __shared__ __attribute__((aligned(1024))) T k_lds3[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds3[kVElems];
+    attn_fwd_body<T, D, NW, 1, BN, 4, MODE, CAUSAL, SPLIT, BIAS, true>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds2, k_lds3, v_lds0, v_lds1, v_lds2, v_lds3));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Merge of a split forward
 // ---------------------------------------------------------------------------
@@ -1348,7 +1546,7 @@ namespace {
 
 template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
 int launch_bucket(const FwdArgs& args, hipStream_t stream) {
-  constexpr TableEntry e = launch_entry<T, D, BUCKET, BIAS>();
+  constexpr TableEntry e = launch_entry<T, D, BUCKET, mask_variant(CAUSAL, MODE), BIAS>();
   FwdArgs a = args;
   a.causal_span = CAUSAL ? causal_span(static_cast<int64_t>(a.num_heads) * a.num_z, a.m_tiles, e.waves)
                          : 0;
@@ -1357,6 +1555,14 @@ int launch_bucket(const FwdArgs& args, hipStream_t stream) {
     static_assert(e.waves == 8 && sizeof(T) == 2, "ping-pong: 8 waves, 16-bit inputs");
     hipLaunchKernelGGL((attn_fwd_pingpong_kernel<T, D, e.block_n, e.stages, MODE, CAUSAL>),
                        dim3(grid), dim3(512), 0, stream, a);
+  } else if constexpr (e.schedule == kSchedLagged) {
+    hipLaunchKernelGGL((attn_fwd_lagged_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL,
+                                               false, BIAS>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  } else if constexpr (e.schedule == kSchedThreeWaves) {
+    hipLaunchKernelGGL((attn_fwd_3w_kernel<T, D, e.waves, e.block_n, e.stages, MODE, CAUSAL, false,
+                                           BIAS>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, row_blocks(e), e.block_n, e.stages, MODE,
                                         CAUSAL, false, BIAS>),
@@ -1383,12 +1589,22 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
 
 template <typename T, int D, bool CAUSAL, int BUCKET>
 int launch_split_bucket(const FwdArgs& a, const MergeArgs& mg, hipStream_t stream) {
-  constexpr TableEntry e = launch_entry<T, D, BUCKET, true>();
+  constexpr TableEntry e = launch_entry<T, D, BUCKET, 0, true>();
   const uint32_t grid =
       static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z * static_cast<uint32_t>(a.num_splits);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, row_blocks(e), e.block_n, e.stages, MODE_DENSE,
-                                      CAUSAL, true, false>),
-                     dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  if constexpr (e.schedule == kSchedLagged) {
+    hipLaunchKernelGGL((attn_fwd_lagged_kernel<T, D, e.waves, e.block_n, e.stages, MODE_DENSE,
+                                               CAUSAL, true, false>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  } else if constexpr (e.schedule == kSchedThreeWaves) {
+    hipLaunchKernelGGL((attn_fwd_3w_kernel<T, D, e.waves, e.block_n, e.stages, MODE_DENSE, CAUSAL,
+                                           true, false>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, row_blocks(e), e.block_n, e.stages,
+                                        MODE_DENSE, CAUSAL, true, false>),
+                       dim3(grid), dim3(e.waves * 64), 0, stream, a);
+  }
   int err = static_cast<int>(hipGetLastError());
   if (err != 0) return err;
   const int64_t threads = mg.ws_rows * (D / 4);
@@ -1412,17 +1628,27 @@ int launch_split_typed(const FwdArgs& a, const MergeArgs& mg, hipStream_t s) {
 }
 
 // The table entry a launch will use, at run time (host side).
+template <typename T, int D, bool SINGLE_GROUP, int BUCKET>
+TableEntry entry_for_bucket(int variant) {
+  switch (variant) {
+    case 0: return launch_entry<T, D, BUCKET, 0, SINGLE_GROUP>();
+    case 1: return launch_entry<T, D, BUCKET, 1, SINGLE_GROUP>();
+    case 2: return launch_entry<T, D, BUCKET, 2, SINGLE_GROUP>();
+    default: return launch_entry<T, D, BUCKET, 3, SINGLE_GROUP>();
+  }
+}
+
 template <typename T, int D, bool SINGLE_GROUP>
-TableEntry entry_for(int bucket) {
+TableEntry entry_for(int bucket, int variant) {
   switch (bucket) {
-    case 0: return launch_entry<T, D, 0, SINGLE_GROUP>();
-    case 1: return launch_entry<T, D, 1, SINGLE_GROUP>();
-    case 2: return launch_entry<T, D, 2, SINGLE_GROUP>();
-    case 3: return launch_entry<T, D, 3, SINGLE_GROUP>();
-    case 4: return launch_entry<T, D, 4, SINGLE_GROUP>();
-    case 5: return launch_entry<T, D, 5, SINGLE_GROUP>();
-    case 6: return launch_entry<T, D, 6, SINGLE_GROUP>();
-    default: return launch_entry<T, D, 7, SINGLE_GROUP>();
+    case 0: return entry_for_bucket<T, D, SINGLE_GROUP, 0>(variant);
+    case 1: return entry_for_bucket<T, D, SINGLE_GROUP, 1>(variant);
+    case 2: return entry_for_bucket<T, D, SINGLE_GROUP, 2>(variant);
+    case 3: return entry_for_bucket<T, D, SINGLE_GROUP, 3>(variant);
+    case 4: return entry_for_bucket<T, D, SINGLE_GROUP, 4>(variant);
+    case 5: return entry_for_bucket<T, D, SINGLE_GROUP, 5>(variant);
+    case 6: return entry_for_bucket<T, D, SINGLE_GROUP, 6>(variant);
+    default: return entry_for_bucket<T, D, SINGLE_GROUP, 7>(variant);
   }
 }
 

@@ -71,11 +71,13 @@ struct KernelConfig {
   int waves;
 };
 
-// The compiled kernel shape a launch uses for (dtype, head_dim) and the
-// sequence extents (seqlen_q and seqlen_k of FwdArgs); single_group for the
-// split forward and the forward with a bias.  False if unsupported.
-bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool single_group,
-                   KernelConfig* cfg);
+// The compiled kernel shape a launch uses for (dtype, head_dim), the
+// sequence extents (seqlen_q and seqlen_k of FwdArgs), the mask and the
+// layout (mode); single_group for the split forward (which takes the dense
+// non-causal entry for both masks) and the forward with a bias.  False if
+// unsupported.
+bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool causal, int mode,
+                   bool single_group, KernelConfig* cfg);
 
 // Launches the forward on `stream` (a hipStream_t).  Returns the HIP error
 // code of the launch (0 on success).  Arguments are assumed validated.

@@ -67,7 +67,8 @@ SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU
 # profiler serialises dispatches; steady clocks are the trace pass's job).
 PROFILED = ["--no-cpu-baseline", "--settle-s", "0", "--launch-stats", "0"]
 TEMPLATE_NOTE = ("Forward template arguments: <element type, head_dim, waves, row blocks per wave, "
-                 "block_n, stages, mode (0 dense, 1 compact, 2 padded), causal, split, bias>; "
+                 "block_n, stages, mode (0 dense, 1 compact, 2 padded), causal, split, bias> "
+                 "(attn_fwd_3w_kernel and attn_fwd_lagged_kernel: the same without row blocks); "
                  "merge: <element type, head_dim>; backward: <element type, head_dim, mode[, "
                  "causal]>.")
 
@@ -214,6 +215,10 @@ def kernel_accounting(short: str, splits: int | None = None, block_m: int | None
         mode, causal = int(args[6]), args[7] == "true"
         split, bias = args[8] == "true", args[9] == "true"
         block_m = 32 * int(args[2]) * int(args[3])
+    elif ident in ("attn_fwd_lagged_kernel", "attn_fwd_3w_kernel") and len(args) == 9:
+        mode, causal = int(args[5]), args[6] == "true"
+        split, bias = args[7] == "true", args[8] == "true"
+        block_m = 32 * int(args[2])
     elif ident == "attn_fwd_pingpong_kernel" and len(args) == 6:
         mode, causal, split, bias, block_m = int(args[4]), args[5] == "true", False, False, 256
     elif ident == "attn_fwd_merge_kernel":

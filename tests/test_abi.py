@@ -61,11 +61,16 @@ def test_kernel_config_table():
     for dt in (torch.float32, torch.float16, torch.bfloat16):
         for d in (64, 128):
             for sq, sk in [(1, 1), (128, 512), (129, 513), (512, 8192), (513, 100), (8192, 8192)]:
-                for sg in (False, True):
-                    bm, bn, w = binding.kernel_config(dt, d, sq, sk, single_group=sg)
-                    assert bm == 32 * w and bn % 32 == 0 and bm > 0
-                    if sg:  # the split and bias kernels are single-group shapes
-                        assert w in (2, 4, 8)
+                for causal in (False, True):
+                    for mode in (0, 1, 2):
+                        for sg in (False, True):
+                            bm, bn, w = binding.kernel_config(dt, d, sq, sk, causal, mode, sg)
+                            assert bm in (32 * w, 64 * w) and bn % 32 == 0 and bm > 0
+                            if sg:  # the split and bias kernels are single-group shapes
+                                assert w in (2, 4, 8)
+                    # the two variable-length layouts share their entries
+                    assert (binding.kernel_config(dt, d, sq, sk, causal, 1) ==
+                            binding.kernel_config(dt, d, sq, sk, causal, 2))
     with pytest.raises(binding.SdpaError) as e:
         binding.kernel_config(torch.float16, 96, 64, 64)
     assert e.value.status == 3
@@ -74,6 +79,9 @@ def test_kernel_config_table():
     assert e.value.status == 2
     with pytest.raises(binding.SdpaError) as e:
         binding.kernel_config(torch.float16, 64, -1, 64)
+    assert e.value.status == 4
+    with pytest.raises(binding.SdpaError) as e:
+        binding.kernel_config(torch.float16, 64, 64, 64, mode=3)
     assert e.value.status == 4
 
 

@@ -1,14 +1,15 @@
 """GPU parity of every entry of the compiled-in dispatch table.
 
 The table keys the kernel shape on (dtype, head_dim, sequence-length
-bucket).  For every 16-bit class and every bucket, a dense problem whose
-lengths fall in that bucket runs through attn_fwd (both masks), a compact
-and a padded problem whose longest sequence has those lengths run through
-the varlen calls, and in the long buckets the forward with a bias and the
-split forward (which take the bucket's single-group shape) run too; sampled
-rows are compared with the float64 oracle, so each compiled kernel of the
-committed library is parity-checked, not only those the small parity shapes
-happen to reach.
+bucket, mask and layout).  For every class and every bucket, a dense problem
+whose lengths fall in that bucket runs through attn_fwd (both masks: the
+dense variants), a compact and a padded problem whose longest sequence has
+those lengths run through the varlen calls (both masks: the variable-length
+variants), and in the long buckets the forward with a bias and the split
+forward (which take the single-group shapes) run too; sampled rows are
+compared with the float64 oracle, so each compiled kernel of the committed
+library is parity-checked, not only those the small parity shapes happen to
+reach.
 """
 
 import sys
@@ -61,16 +62,19 @@ def _sampled_check(x, o, lse, causal, dt, label, bias=None, heads=((0, 0), (0, 1
           label=label)
 
 
-@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 64)])
+CLASSES = [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 64), ("fp32", 64), ("fp32", 128)]
+
+
+@pytest.mark.parametrize("dt,D", CLASSES)
 @pytest.mark.parametrize("bucket", range(len(BUCKET_SHAPES)))
 def test_every_table_entry(dt, D, bucket):
     sq, sk = BUCKET_SHAPES[bucket]
-    bm, bn, w = binding.kernel_config(inputs.DTYPES[dt], D, sq, sk)
-    _log(f"dispatch {dt} D{D} bucket {bucket} Sq{sq} Sk{sk}: block_m {bm} block_n {bn} "
-         f"waves {w}")
     x = inputs.dense_inputs(1, 2, sq, sk, D, dt, seed=500 + bucket)
     q, k, v = x.q.to(DEV), x.k.to(DEV), x.v.to(DEV)
     for causal in (False, True):
+        bm, bn, w = binding.kernel_config(inputs.DTYPES[dt], D, sq, sk, causal=causal)
+        _log(f"dispatch {dt} D{D} bucket {bucket} Sq{sq} Sk{sk} causal={causal}: block_m {bm} "
+             f"block_n {bn} waves {w}")
         o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=causal)
         torch.cuda.synchronize()
         _sampled_check(x, o, lse, causal, dt, f"{dt} D{D} bucket {bucket} causal={causal}")
@@ -95,7 +99,7 @@ def test_single_group_entries_with_bias_and_split(dt, D, bucket):
     _sampled_check(x, o, lse, False, dt, f"split {dt} D{D} bucket {bucket}")
 
 
-@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 64)])
+@pytest.mark.parametrize("dt,D", CLASSES)
 @pytest.mark.parametrize("bucket", range(len(BUCKET_SHAPES)))
 def test_every_table_entry_varlen(dt, D, bucket):
     """The compact and padded kernels of every entry: two sequences whose

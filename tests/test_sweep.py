@@ -1,122 +1,146 @@
-"""The dispatch-table sweep's selection rule (CPU only, no GPU work)."""
+"""The dispatch-table sweep's selection rule, table writer and workload plan
+(CPU only, no GPU work)."""
 
 import json
 import re
 import shutil
 
+import numpy as np
+
 from scaled_dot_product_03_amd import sweep
 
 
 def _table_entries(text, cond):
-    """The per-bucket entries the generated table holds for one class."""
-    m = re.search(re.escape(cond) + r"\) \{\s*constexpr TableEntry e\[kSeqBuckets\] = \{(.*?)\};",
-                  text, re.S)
+    """The [bucket][variant] entries the generated table holds for one class."""
+    m = re.search(re.escape(cond) + r"\) \{\s*constexpr TableEntry e\[kSeqBuckets\]\[kVariants\] "
+                  r"= \{(.*?)\};", text, re.S)
     assert m, cond
-    return [tuple(int(x) for x in e.split(",")) for e in re.findall(r"\{([^{}]*)\}", m.group(1))]
+    rows = re.findall(r"\{(\{[^{}]*\}(?:, \{[^{}]*\})*)\}", m.group(1))
+    return [[tuple(int(x) for x in e.split(",")) for e in re.findall(r"\{([^{}]*)\}", r)]
+            for r in rows]
 
 
-def test_write_picks_per_bucket_fastest_candidate_that_passed_parity(tmp_path):
-    results = [
-        {"dtype": "bf16", "head_dim": 128, "cand": [8, 64, 3], "parity": False, "ms": None},
-        # fastest in the long bucket, slower in the short one
-        {"dtype": "bf16", "head_dim": 128, "cand": [4, 64, 2], "parity": True,
-         "ms": {"5": {"w": [0.2, 0.1]}, "0": {"s": [0.05]}}},
-        {"dtype": "bf16", "head_dim": 128, "cand": [2, 32, 2], "parity": True,
-         "ms": {"5": {"w": [0.25, 0.1]}, "0": {"s": [0.03]}}},
-        # fastest of all but failed parity: never chosen
-        {"dtype": "fp16", "head_dim": 64, "cand": [8, 64, 3], "parity": False,
-         "ms": {"3": {"w": [0.01]}}},
-        {"dtype": "fp16", "head_dim": 64, "cand": [4, 32, 3], "parity": True,
-         "ms": {"3": {"w": [0.3]}}},
-        {"dtype": "fp16", "head_dim": 64, "cand": [8, 64, 3, 1], "parity": True,
-         "ms": {"3": {"w": [0.4]}}},
-    ]
+def _ms(per_bucket):
+    """{bucket: {workload: {variant: ms}}} with string keys, as results.json has."""
+    return {str(b): {w: {str(v): t for v, t in per.items()} for w, per in wl.items()}
+            for b, wl in per_bucket.items()}
+
+
+def _write(tmp_path, results):
     rp = tmp_path / "results.json"
     rp.write_text(json.dumps(results))
     table = tmp_path / "dispatch_table.inc"
     shutil.copy(sweep.TABLE, table)
-    pick = sweep.write(str(rp), str(table))
-    assert pick[("bf16", 128, 5)] == (4, 64, 2, 0)
-    assert pick[("bf16", 128, 0)] == (2, 32, 2, 0)
-    assert pick[("fp16", 64, 3)] == (4, 32, 3, 0)
-    # buckets without timings keep the class default
-    assert pick[("bf16", 128, 2)] == (4, 64, 2, 0) and pick[("fp16", 64, 0)] == (4, 64, 3, 0)
-    # untimed classes follow the timed class of the same head_dim, bucket by bucket
-    assert pick[("fp16", 128, 0)] == (2, 32, 2, 0) and pick[("bf16", 64, 3)] == (4, 32, 3, 0)
-    text = table.read_text()
-    assert _table_entries(text, "dtype_code<T>() == DT_BF16 && D == 128") == [
-        (2, 32, 2, 0)] + [(4, 64, 2, 0)] * 7
-    assert _table_entries(text, "dtype_code<T>() == DT_F16 && D == 64")[3] == (4, 32, 3, 0)
+    summary = tmp_path / "summary.md"
+    pick = sweep.write(str(rp), str(table), str(summary))
+    return pick, table.read_text(), summary.read_text()
+
+
+def test_write_picks_per_bucket_and_variant_among_candidates_that_passed_parity(tmp_path):
+    results = [
+        # fastest everywhere but failed parity: never chosen
+        {"dtype": "bf16", "head_dim": 128, "cand": [8, 64, 3, 0], "parity": False, "ms": None},
+        # best on the dense non-causal calls of bucket 5, worse causal
+        {"dtype": "bf16", "head_dim": 128, "cand": [4, 64, 2, 0], "parity": True,
+         "ms": _ms({5: {"a": {0: 0.10, 1: 0.09}, "b": {0: 0.20, 1: 0.12}, "t": {3: 0.5}}})},
+        {"dtype": "bf16", "head_dim": 128, "cand": [4, 32, 2, 4], "parity": True,
+         "ms": _ms({5: {"a": {0: 0.12, 1: 0.07}, "b": {0: 0.22, 1: 0.10}, "t": {3: 0.4}}})},
+        {"dtype": "fp16", "head_dim": 64, "cand": [4, 32, 3, 3], "parity": True,
+         "ms": _ms({3: {"c": {0: 0.3}}})},
+        {"dtype": "fp16", "head_dim": 64, "cand": [4, 64, 2, 0], "parity": True,
+         "ms": _ms({3: {"c": {0: 0.2}}})},
+    ]
+    pick, text, summary = _write(tmp_path, results)
+    assert pick[("bf16", 128, 5, 0)] == (4, 64, 2, 0)
+    assert pick[("bf16", 128, 5, 1)] == (4, 32, 2, 4)
+    assert pick[("bf16", 128, 5, 3)] == (4, 32, 2, 4)
+    # variable-length without the mask has no timing here: dense without the mask
+    assert pick[("bf16", 128, 5, 2)] == (4, 64, 2, 0)
+    assert pick[("fp16", 64, 3, 0)] == (4, 64, 2, 0)
+    # keys no timing reaches (other buckets, untimed classes) keep the default
+    assert pick[("bf16", 128, 0, 0)] == sweep.DEFAULT
+    assert pick[("fp32", 64, 5, 1)] == sweep.DEFAULT
+    ent = _table_entries(text, "dtype_code<T>() == DT_BF16 && D == 128")
+    assert len(ent) == len(sweep.BUCKETS) and all(len(r) == len(sweep.VARIANTS) for r in ent)
+    assert ent[5] == [(4, 64, 2, 0), (4, 32, 2, 4), (4, 64, 2, 0), (4, 32, 2, 4)]
     assert text.count("// BEGIN TABLE (generated)") == 1 and text.count("// END TABLE") == 1
+    # the summary traces each entry to its timings
+    assert "| 5 | dense causal | (4, 32, 2, 4) | own timings |" in summary
+    assert "| 5 | varlen | (4, 64, 2, 0) | variant dense |" in summary
+    assert "FAIL" in summary
 
 
-def test_write_emits_the_pingpong_field(tmp_path):
+def test_scores_count_every_call_alike():
+    # one long and one short call: 10% slower on the long one and 20% faster
+    # on the short one wins (1.1 + 1.0 < 1.0 + 1.25)
     results = [
         {"dtype": "bf16", "head_dim": 128, "cand": [4, 64, 2, 0], "parity": True,
-         "ms": {"5": {"w": [0.3]}}},
-        {"dtype": "bf16", "head_dim": 128, "cand": [8, 64, 3, 1], "parity": True,
-         "ms": {"5": {"w": [0.2]}}},
+         "ms": _ms({7: {"long": {0: 2.0}, "short": {0: 0.0125}}})},
+        {"dtype": "bf16", "head_dim": 128, "cand": [8, 64, 2, 0], "parity": True,
+         "ms": _ms({7: {"long": {0: 2.2}, "short": {0: 0.0100}}})},
     ]
-    rp = tmp_path / "results.json"
-    rp.write_text(json.dumps(results))
-    table = tmp_path / "dispatch_table.inc"
-    shutil.copy(sweep.TABLE, table)
-    pick = sweep.write(str(rp), str(table))
-    assert pick[("bf16", 128, 5)] == (8, 64, 3, 1) and pick[("fp16", 128, 5)] == (8, 64, 3, 1)
-    assert _table_entries(table.read_text(), "dtype_code<T>() == DT_BF16 && D == 128")[5] == \
-        (8, 64, 3, 1)
+    pick, best = sweep.select(results)
+    assert pick[("bf16", 128, 7, 0)][0] == (8, 64, 2, 0)
+    assert abs(best[("bf16", 128, 7, 0)][1] - 2.1) < 1e-9
+
+
+def test_names_and_defines_of_every_schedule():
+    assert sweep._name(("bf16", 128), (4, 32, 3, 2)) == "bf16_d128_w4_n32_s3_rb2"
     assert sweep._name(("bf16", 128), (8, 64, 3, 1)) == "bf16_d128_w8_n64_s3_pp"
+    assert sweep._name(("fp16", 64), (4, 32, 3, 3)) == "fp16_d64_w4_n32_s3_lag"
+    assert sweep._name(("fp16", 64), (4, 64, 2, 4)) == "fp16_d64_w4_n64_s2_3w"
+    assert sweep._name(("fp32", 64), (4, 64, 2)) == "fp32_d64_w4_n64_s2"
+    assert "-DSDPA03_SWEEP_SCHEDULE=3" in sweep._defines(("fp16", 64), (4, 32, 3, 3))
+    assert "-DSDPA03_SWEEP_DTYPE=0" in sweep._defines(("fp32", 128), (4, 32, 2, 0))
+    assert sweep._kernel_prefix(("fp16", 64), (4, 32, 3, 3)).startswith("attn_fwd_lagged_kernel")
+    assert sweep._kernel_prefix(("bf16", 128), (4, 32, 2, 4)).startswith("attn_fwd_3w_kernel")
 
 
-def test_every_bucket_has_timed_workloads_in_its_own_bucket():
+def test_every_class_is_swept_with_several_schedules():
+    assert set(sweep.CANDIDATES) == set(sweep.CLASSES)
+    for cls, cands in sweep.CANDIDATES.items():
+        scheds = {sweep._cand4(c)[3] for c in cands}
+        assert len(cands) >= 4, cls
+        if cls[0] != "fp32":
+            assert {0, 1, 4} <= scheds, (cls, scheds)
+        else:  # the ping-pong and lagged schedules are 16-bit only
+            assert scheds == {0}
+
+
+def _lengths(kind, kw):
+    if kind == "dense":
+        return kw["Sq"], kw["Sk"]
+    rng = np.random.default_rng(kw["seed"])
+    if kw["k_lo"] is None:
+        lq = rng.integers(kw["len_lo"], kw["len_hi"], size=kw["n_seqs"], endpoint=True)
+        return int(lq.max()), int(lq.max())
+    rng = np.random.default_rng(kw["seed"] + 1)
+    lq = rng.integers(kw["len_lo"], kw["len_hi"], size=kw["n_seqs"], endpoint=True)
+    lk = rng.integers(kw["k_lo"], kw["k_hi"], size=kw["n_seqs"], endpoint=True)
+    return int(lq.max()), int(lk.max())
+
+
+def test_every_bucket_has_two_dense_and_a_varlen_workload_in_its_own_bucket():
     for cls, per_bucket in sweep.TIMED.items():
         assert sorted(per_bucket) == list(range(len(sweep.BUCKETS)))
         for b, specs in per_bucket.items():
+            kinds = [kind for _, kind, _ in specs]
+            assert kinds.count("dense") >= 2 and "compact" in kinds, (cls, b)
             for name, kind, kw in specs:
                 if kind == "named":
                     continue
-                if kind == "dense":
-                    sq, sk = kw["Sq"], kw["Sk"]
-                else:  # compact: the longest sequence is at most len_hi
-                    sq = sk = kw["len_hi"]
+                sq, sk = _lengths(kind, kw)
                 qb = 0 if sq <= 128 else (1 if sq <= 512 else (2 if sq <= 4096 else 3))
                 kb = 0 if sk <= 512 else 1
-                assert 2 * qb + kb == b, (cls, b, name)
+                assert 2 * qb + kb == b, (cls, b, name, sq, sk)
 
 
-def test_written_table_compiles_into_the_committed_format():
+def test_committed_table_holds_every_class_bucket_and_variant():
     text = open(sweep.TABLE).read()
-    for cond in ("dtype_code<T>() == DT_BF16 && D == 128", "dtype_code<T>() == DT_F16 && D == 64",
-                 "dtype_code<T>() == DT_BF16 && D == 64", "dtype_code<T>() == DT_F16 && D == 128"):
-        assert len(_table_entries(text, cond)) == len(sweep.BUCKETS)
-
-
-def test_schedule_field_names_defines_and_table_entries(tmp_path):
-    # schedule 2 (two 32-row blocks per wave) is named, built and written like the others
-    assert sweep._name(("bf16", 128), (4, 32, 3, 2)) == "bf16_d128_w4_n32_s3_rb2"
-    assert sweep._name(("fp16", 64), (4, 64, 2, 0)) == "fp16_d64_w4_n64_s2"
-    assert "-DSDPA03_SWEEP_SCHEDULE=2" in sweep._defines(("bf16", 128), (4, 32, 3, 2))
-    assert "-DSDPA03_SWEEP_SCHEDULE=0" in sweep._defines(("fp16", 64), (4, 64, 2))
-    results = [
-        {"dtype": "bf16", "head_dim": 128, "cand": [4, 32, 3, 2], "parity": True,
-         "ms": {"5": {"w": [0.1]}}},
-        {"dtype": "bf16", "head_dim": 128, "cand": [4, 64, 2, 0], "parity": True,
-         "ms": {"5": {"w": [0.2]}}},
-    ]
-    rp = tmp_path / "results.json"
-    rp.write_text(json.dumps(results))
-    table = tmp_path / "dispatch_table.inc"
-    shutil.copy(sweep.TABLE, table)
-    pick = sweep.write(str(rp), str(table))
-    assert pick[("bf16", 128, 5)] == (4, 32, 3, 2)
-    assert _table_entries(table.read_text(), "dtype_code<T>() == DT_BF16 && D == 128")[5] == \
-        (4, 32, 3, 2)
-
-
-def test_every_candidate_class_offers_each_schedule():
-    for cls, cands in sweep.CANDIDATES.items():
-        scheds = {sweep._cand4(c)[3] for c in cands}
-        assert scheds == {0, 1, 2}, (cls, scheds)
+    for dt, d in sweep.CLASSES:
+        ent = _table_entries(text, sweep._cond(dt, d))
+        assert len(ent) == len(sweep.BUCKETS), (dt, d)
+        assert all(len(r) == len(sweep.VARIANTS) for r in ent), (dt, d)
 
 
 def test_child_faults_stop_the_sweep_but_failed_comparisons_do_not():
