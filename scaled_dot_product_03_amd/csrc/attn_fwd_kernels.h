@@ -1548,7 +1548,9 @@ template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
 int launch_bucket(const FwdArgs& args, hipStream_t stream) {
   constexpr TableEntry e = launch_entry<T, D, BUCKET, mask_variant(CAUSAL, MODE), BIAS>();
   FwdArgs a = args;
-  a.causal_span = CAUSAL ? causal_span(static_cast<int64_t>(a.num_heads) * a.num_z, a.m_tiles, e.waves)
+  a.causal_span = CAUSAL ? causal_span(static_cast<int64_t>(a.num_heads) * a.num_z, a.m_tiles, e.waves,
+                                       MODE == MODE_COMPACT ? kCausalPartWavesCompact
+                                                            : kCausalPartWaves)
                          : 0;
   const uint32_t grid = static_cast<uint32_t>(a.m_tiles) * a.num_heads * a.num_z;
   if constexpr (e.schedule == kSchedPingPong) {

@@ -153,15 +153,22 @@ def _kernel_prefix(cls, cand):
     return f"attn_fwd_kernelI{dt_tag}Li{d}ELi{w}ELi{rb}ELi{n}ELi{st}E"
 
 
+# Spilled registers the forward with a bias may have (its bias tile adds 16
+# registers to the kernel; a couple of spills there cost less than a shape
+# the other kernels cannot use).
+BIAS_SPILL_LIMIT = 8
+
+
 def _resources(cls, cand):
-    """(max VGPRs, spills, waves/SIMD) of the candidate's kernels for its class."""
+    """(max VGPRs, spills of the kernels without a bias, spills of those with
+    one, waves/SIMD) of the candidate's forward kernels for its class."""
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-c",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-x", "hip", os.path.join(CSRC, TU_OF[cls[0]]),
            "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage", *_defines(cls, cand)]
     out = subprocess.run(cmd, capture_output=True, text=True).stderr
     want = _kernel_prefix(cls, cand)
-    vg, sp, occ, cur = 0, 0, 99, None
+    vg, sp, sp_bias, occ, cur = 0, 0, 0, 99, None
     for line in out.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
         if m:
@@ -169,18 +176,23 @@ def _resources(cls, cand):
             continue
         if cur is None or want not in cur:
             continue
+        # the bias flag is the last template argument of every forward kernel
+        bias = cur.endswith("ELb1EEEvNS_7FwdArgsE")
         m = re.search(r"remark:\s+(VGPRs|VGPRs Spill|Occupancy \[waves/SIMD\]): (\d+)", line)
         if m:
             val = int(m.group(2))
             if m.group(1) == "VGPRs":
                 vg = max(vg, val)
             elif m.group(1) == "VGPRs Spill":
-                sp = max(sp, val)
-            else:
+                if bias:
+                    sp_bias = max(sp_bias, val)
+                else:
+                    sp = max(sp, val)
+            elif not bias:
                 occ = min(occ, val)
     if occ == 99:
         raise RuntimeError(f"no kernel {want} in the resource report of {_name(cls, cand)}")
-    return vg, sp, occ
+    return vg, sp, sp_bias, occ
 
 
 def _source_digest():
@@ -228,17 +240,17 @@ def build(only=None):
     cache = os.path.join(SWEEP_DIR, "objcache")
     os.makedirs(cache, exist_ok=True)
     plan, skipped = [], []
-    for cls in CLASSES:
-        for cand in CANDIDATES[cls]:
-            if only and not any(o in _name(cls, cand) for o in only):
-                continue
-            vg, sp, occ = _resources(cls, cand)
-            ok = sp == 0 and occ >= 1
-            print(f"{_name(cls, cand):30s} vgpr={vg} spill={sp} waves/simd={occ} "
-                  f"{'build' if ok else 'skip'}", flush=True)
-            rec = {"dtype": cls[0], "head_dim": cls[1], "cand": list(_cand4(cand)), "vgpr": vg,
-                   "spill": sp, "waves_per_simd": occ}
-            (plan if ok else skipped).append(rec)
+    todo = [(cls, cand) for cls in CLASSES for cand in CANDIDATES[cls]
+            if not only or any(o in _name(cls, cand) for o in only)]
+    with ThreadPoolExecutor(max_workers=6) as pool:
+        res = list(pool.map(lambda cc: _resources(*cc), todo))
+    for (cls, cand), (vg, sp, sp_bias, occ) in zip(todo, res):
+        ok = sp == 0 and sp_bias <= BIAS_SPILL_LIMIT and occ >= 1
+        print(f"{_name(cls, cand):30s} vgpr={vg} spill={sp} bias-kernel spill={sp_bias} "
+              f"waves/simd={occ} {'build' if ok else 'skip'}", flush=True)
+        rec = {"dtype": cls[0], "head_dim": cls[1], "cand": list(_cand4(cand)), "vgpr": vg,
+               "spill": sp, "bias_spill": sp_bias, "waves_per_simd": occ}
+        (plan if ok else skipped).append(rec)
     # the units shared by every candidate first, then the candidates in parallel
     if plan:
         first = plan[0]
@@ -485,7 +497,8 @@ def write(results_path=RESULTS, table_path=TABLE, summary_path=SUMMARY):
              "  // variants: " + ", ".join(f"{i} {v}" for i, v in enumerate(VARIANTS))]
     first = True
     for dt, d in CLASSES:
-        lines.append(f"  {'if' if first else '}} else if'} constexpr ({_cond(dt, d)}) {{")
+        opener = "if" if first else "} else if"
+        lines.append(f"  {opener} constexpr ({_cond(dt, d)}) {{")
         first = False
         lines.append("    constexpr TableEntry e[kSeqBuckets][kVariants] = {")
         for b in range(len(BUCKETS)):

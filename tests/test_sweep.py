@@ -64,6 +64,10 @@ def test_write_picks_per_bucket_and_variant_among_candidates_that_passed_parity(
     assert len(ent) == len(sweep.BUCKETS) and all(len(r) == len(sweep.VARIANTS) for r in ent)
     assert ent[5] == [(4, 64, 2, 0), (4, 32, 2, 4), (4, 64, 2, 0), (4, 32, 2, 4)]
     assert text.count("// BEGIN TABLE (generated)") == 1 and text.count("// END TABLE") == 1
+    # braces balance: one opened per class, one for the default, all closed
+    body = text[text.index("// BEGIN TABLE"):text.index("// END TABLE")]
+    assert not re.search(r"^\s*\}\}", body, re.M)
+    assert body.count("{") == body.count("}")
     # the summary traces each entry to its timings
     assert "| 5 | dense causal | (4, 32, 2, 4) | own timings |" in summary
     assert "| 5 | varlen | (4, 64, 2, 0) | variant dense |" in summary
