@@ -1031,6 +1031,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
     if (!wave_done(t)) {
 
     // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
+    // At head dim 128 the wave raises its issue priority for this phase and
+    // drops it for phase B: a SIMD's other wave, in its product-only phase
+    // B, then fills the matrix cores between this wave's softmax
+    // instructions instead of the other way round.  Measured on the bf16
+    // D128 workloads: dense causal S2048 73.8 against 77.0 us, padded varlen
+    // 1808 against 1870 us, non-causal and THD unchanged; at head dim 64 the
+    // unsplit Sq512 Sk8192 forward ran 16 % slower with it, so it stays off.
+    if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
     PRegs p[RB];
     f32x16 s_next[RB][NB];
     float tile_sum[RB];
@@ -1050,6 +1058,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
     if constexpr (!BIAS) mask_tile(t + 1, s_next);
 
     // Phase B: O += P(t) V(t) on the matrix cores.
+    if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
     Path::template pv<NB, DB, RB>(v_cur, lanes, p, acc);
     Path::template interleave_pv<NB, DB, RB>();
     if constexpr (BIAS) {
