@@ -25,7 +25,7 @@ bool kernel_config(int dtype, int head_dim, int seqlen_q, int seqlen_k, bool cau
     case DT_BF16: e = pick(__bf16{}); break;
     default: return false;
   }
-  cfg->block_m = e.waves * 32 * row_blocks(e);
+  cfg->block_m = block_m_of(e);
   cfg->block_n = e.block_n;
   cfg->waves = e.waves;
   return true;

@@ -674,19 +674,33 @@ __device__ __forceinline__ StageArrays<T> stage_arrays(T* k0, T* k1, T* k2, T* k
 // P.V, so the loads have the whole step to land; the scores then hold
 // scale * q.k + bias (natural-log units) and the softmax multiplies by
 // log2(e) alone.
+// KG: key groups.  With KG > 1 the workgroup's NW = 4 KG waves form KG
+// groups of four that share the same 128 query rows: every step copies a
+// tile of KG * BN keys, group g takes its keys [g * BN, (g + 1) * BN), and
+// each group keeps its own running max, sum and O.  At the end groups 1 ..
+// KG-1 hand their state to group 0 through LDS, which merges them and writes
+// O and LSE.  A launch with few query tiles and long key ranges then runs
+// KG waves per SIMD on one copy of each key tile, where one row group per
+// workgroup ran one (dense or varlen scores without mask, bias or split;
+// 16-bit inputs).
 template <typename T, int D, int NW, int RB, int BN, int STAGES, int MODE, bool CAUSAL, bool SPLIT,
-          bool BIAS, bool LAG = false>
+          bool BIAS, bool LAG = false, int KG = 1>
 __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArrays<T>& st) {
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+  static_assert(KG == 1 || (NW == 4 * KG && RB == 1 && !CAUSAL && !SPLIT && !BIAS && !LAG &&
+                            sizeof(T) == 2),
+                "key groups: four waves each, 16-bit, scores without mask, bias or split");
   static_assert(!LAG || (RB == 1 && STAGES >= 3), "the lagged schedule: one row block, >= 3 stages");
   static_assert(RB == 1 || RB == 2, "one or two row blocks per wave");
   static_assert(!SPLIT || MODE == MODE_DENSE, "the split forward serves the dense mode");
   static_assert(!(SPLIT && BIAS), "the split forward has no bias");
   using Path = typename PathFor<T, D>::type;
-  using KCopy = typename Path::template KCopy<BN, NW>;
-  using VCopy = typename Path::template VCopy<BN, NW>;
+  using KCopy = typename Path::template KCopy<KG * BN, NW>;
+  using VCopy = typename Path::template VCopy<KG * BN, NW>;
   using PRegs = typename Path::template PRegs<BN / 32>;
-  constexpr int BM = NW * 32 * RB;
+  constexpr int NWR = NW / KG;  // waves per key group, one row block each
+  constexpr int BM = NWR * 32 * RB;
+  constexpr int TBN = KG * BN;  // keys copied per step
   constexpr int NB = BN / 32;
   constexpr int DB = D / 32;
   // Loads one step issues per wave; those of the last STAGES - 2 steps may
@@ -720,7 +734,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
           static_cast<int64_t>(sr.q_start) * a.o_ss;
   float* lsep = a.lse + sr.b * a.lse_sb + h * a.lse_sh + sr.q_start;
 
-  const int row0 = m0 + wave * 32 * RB;  // first query row of this wave
+  const int wr = KG == 1 ? wave : wave % NWR;  // row block of this wave
+  const int kg = KG == 1 ? 0 : wave / NWR;     // key group of this wave
+  const int row0 = m0 + wr * 32 * RB;          // first query row of this wave
   int qi[RB];                            // this lane's query row in each block
   bool row_ok[RB];
 #pragma unroll
@@ -734,7 +750,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
   // Key tiles [tile0, tile0 + n_tiles): all of them, or this split's share
   // (possibly none: an empty split still writes its partial result).
   int tile0 = 0;
-  int n_tiles = (kend + BN - 1) / BN;
+  int n_tiles = (kend + TBN - 1) / TBN;
   if constexpr (SPLIT) {
     tile0 = split * a.split_tiles;
     n_tiles = max(0, min(n_tiles - tile0, a.split_tiles));
@@ -749,14 +765,21 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
   // Rows at or past `end` are not fetched (they read back as zeros); a load
   // past the last tile fetches nothing.
   auto issue_k = [&](int t, int stage, int end) {
-    const int j0 = (tile0 + t) * BN;
+    const int j0 = (tile0 + t) * TBN;
     kcopy.issue(kp + j0 * k_row_bytes, end - j0, k_row_bytes, st.k[stage], wave);
   };
   auto issue_v = [&](int t, int stage, int end) {
-    const int j0 = (tile0 + t) * BN;
+    const int j0 = (tile0 + t) * TBN;
     vcopy.issue(vp + j0 * v_row_bytes, end - j0, v_row_bytes, st.v[stage], wave);
   };
   const typename Path::Lanes lanes = Path::lanes(lane);
+  // Element offsets of this wave's key group inside a K and a V tile.
+  int k_grp = 0;
+  int v_grp = 0;
+  if constexpr (KG > 1) {
+    k_grp = kg * BN * (Path::kRowK / static_cast<int>(sizeof(T)));
+    v_grp = kg * BN * (Path::kRowV / static_cast<int>(sizeof(T)));
+  }
 
   typename Path::QRegs qr[RB];
 #pragma unroll
@@ -807,7 +830,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
   // Masks the scores of tile t where keys run past the sequence or, under
   // the causal mask, past the lane's row (only tail and diagonal tiles).
   auto mask_tile = [&](int t, f32x16 (&s)[RB][NB]) {
-    const int j0 = (tile0 + t) * BN;
+    const int j0 = (tile0 + t) * TBN + kg * BN;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const bool need_mask = (j0 + BN > sr.len_k) || (CAUSAL && j0 + BN - 1 > row0 + 32 * rb);
@@ -989,7 +1012,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[rb][nb] = f32x16{};
     }
-    Path::template qk<NB, RB>(st.k[0], lanes, qr, s);
+    Path::template qk<NB, RB>(st.k[0] + k_grp, lanes, qr, s);
     if constexpr (BIAS) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) bias_next[rb].fold(s[rb], a.scale);
@@ -1015,8 +1038,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
   // softmax VALU work with the next tile's score MFMAs.
   auto step = [&](int t, auto stage) {
     constexpr int ST = decltype(stage)::value;
-    const T* k_nxt = st.k[(ST + 1) % STAGES];
-    const T* v_cur = st.v[ST];
+    const T* k_nxt = st.k[(ST + 1) % STAGES] + k_grp;
+    const T* v_cur = st.v[ST] + v_grp;
     // The next tile's bias goes out before the tile copies, so waiting for it
     // never waits for them (also when this wave skips the tile: a
     // conditional load would keep two copies of the bias registers alive).
@@ -1031,14 +1054,18 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
     if (!wave_done(t)) {
 
     // Phase A: probabilities of tile t (VALU) || scores of tile t+1 (MFMA).
-    // At head dim 128 the wave raises its issue priority for this phase and
-    // drops it for phase B: a SIMD's other wave, in its product-only phase
-    // B, then fills the matrix cores between this wave's softmax
-    // instructions instead of the other way round.  Measured on the bf16
-    // D128 workloads: dense causal S2048 73.8 against 77.0 us, padded varlen
-    // 1808 against 1870 us, non-causal and THD unchanged; at head dim 64 the
-    // unsplit Sq512 Sk8192 forward ran 16 % slower with it, so it stays off.
-    if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
+    // At head dim 128, in the split forward and with key groups, the wave
+    // raises its issue priority for this phase and drops it for phase B: a
+    // SIMD's other wave, in its product-only phase B, then fills the matrix
+    // cores between this wave's softmax instructions instead of the other way
+    // round.  Measured on the bf16 D128 workloads: dense causal S2048 73.8
+    // against 77.0 us, padded varlen 1808 against 1870 us, non-causal and THD
+    // unchanged; split fp16 D64 Sq512 Sk8192 87 against 89-91 us, with two key
+    // groups 85.3-86.0 against 86.6-86.7 us.  The single-group D64 kernel keeps
+    // one priority: with the instructions in its loop (even skipped at run
+    // time) it compiled to a schedule 16-22 % slower on that workload.
+    constexpr bool kPhasePrio = D == 128 || SPLIT || KG > 1;
+    if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(1);
     PRegs p[RB];
     f32x16 s_next[RB][NB];
     float tile_sum[RB];
@@ -1058,7 +1085,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
     if constexpr (!BIAS) mask_tile(t + 1, s_next);
 
     // Phase B: O += P(t) V(t) on the matrix cores.
-    if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
+    if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(0);
     Path::template pv<NB, DB, RB>(v_cur, lanes, p, acc);
     Path::template interleave_pv<NB, DB, RB>();
     if constexpr (BIAS) {
@@ -1111,9 +1138,55 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, const StageArray
       }
     }
     const int last = (n_tiles - 1) % STAGES;
-    last_step(last == 0 ? st.v[0] : (last == 1 ? st.v[1] : (last == 2 ? st.v[2] : st.v[3])));
+    last_step((last == 0 ? st.v[0] : (last == 1 ? st.v[1] : (last == 2 ? st.v[2] : st.v[3]))) +
+              v_grp);
   }
   }  // LAG
+
+  if constexpr (KG > 1) {
+    // Groups 1 .. KG-1 hand their running max, sum and O to group 0 through
+    // LDS once every wave is done with the tiles: wave r of each group owns
+    // rows [32 r, 32 r + 32), and lane (i, h) of every group holds the same
+    // row and half of the sums, so the exchange is lane to lane.  Row block
+    // r's buffers lie in one stage array (K0, K1, V0, V1 for r = 0..3),
+    // group g's at float (g - 1) * kVals * 64, its value i of lane L at
+    // float i * 64 + L after that.
+    constexpr int kVals = DB * 16 + 2;
+    barrier_lds();
+    float* xbase = reinterpret_cast<float*>(
+        wr == 0 ? st.k[0] : (wr == 1 ? st.k[1] : (wr == 2 ? st.v[0] : st.v[1])));
+    if (kg > 0) {
+      float* xbuf = xbase + (kg - 1) * kVals * 64;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xbuf[(db * 16 + r) * 64 + lane] = acc[0][db][r];
+      }
+      xbuf[(kVals - 2) * 64 + lane] = m_run[0];
+      xbuf[(kVals - 1) * 64 + lane] = l_run[0];
+    }
+    barrier_lds();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g) {
+      const float* xbuf = xbase + (g - 1) * kVals * 64;
+      const float m1 = xbuf[(kVals - 2) * 64 + lane];
+      const float l1 = xbuf[(kVals - 1) * 64 + lane];
+      const float m_new = fmaxf(m_run[0], m1);
+      // A group that saw no key keeps m = -inf and l = 0: its factor is 0.
+      const float f0 = m_run[0] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m_new);
+      const float f1 = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[0][db][r] = acc[0][db][r] * f0 + xbuf[(db * 16 + r) * 64 + lane] * f1;
+        }
+      }
+      l_run[0] = l_run[0] * f0 + l1 * f1;
+      m_run[0] = m_new;
+    }
+  }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2, valid rows only.
 #pragma unroll
@@ -1445,6 +1518,34 @@ __global__ __launch_bounds__(NW * 64, RB == 2 ? 1 : 2) void attn_fwd_kernel(FwdA
   }
 }
 
+// KG key groups of four waves (see attn_fwd_body): 4 KG waves, KG waves per
+// SIMD, two or three stages of KG * BN-key tiles.
+template <typename T, int D, int KG, int BN, int STAGES, int MODE>
+__global__ __launch_bounds__(KG * 256, KG) void attn_fwd_kg_kernel(FwdArgs a) {
+  static_assert(KG == 2 || KG == 3, "two or three key groups");
+  using Path = typename PathFor<T, D>::type;
+  constexpr int kES = static_cast<int>(sizeof(T));
+  constexpr int kKElems = Path::template KCopy<KG * BN, 4 * KG>::kArrayBytes / kES;
+  constexpr int kVElems = Path::template VCopy<KG * BN, 4 * KG>::kArrayBytes / kES;
+  static_assert(kKElems * kES >= (KG - 1) * (D / 2 + 2) * 256 &&
+                    kVElems * kES >= (KG - 1) * (D / 2 + 2) * 256,
+                "each stage array holds one row block's exchange buffers");
+  __shared__ __attribute__((aligned(1024))) T k_lds0[kKElems];
+  __shared__ __attribute__((aligned(1024))) T k_lds1[kKElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds0[kVElems];
+  __shared__ __attribute__((aligned(1024))) T v_lds1[kVElems];
+  if constexpr (STAGES == 2) {
+    attn_fwd_body<T, D, 4 * KG, 1, BN, 2, MODE, false, false, false, false, KG>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds0, k_lds1, v_lds0, v_lds1, v_lds0, v_lds1));
+  } else {
+    static_assert(STAGES == 3, "two or three stages");
+    __shared__ __attribute__((aligned(1024))) T k_lds2[kKElems];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[kVElems];
+    attn_fwd_body<T, D, 4 * KG, 1, BN, 3, MODE, false, false, false, false, KG>(
+        a, stage_arrays(k_lds0, k_lds1, k_lds2, k_lds0, v_lds0, v_lds1, v_lds2, v_lds0));
+  }
+}
+
 // The single-group kernel built for three waves per SIMD: the launch bound
 // limits a wave to 168 registers, so three four-wave workgroups (or a
 // mix) share a CU where the LDS stages allow it.
@@ -1553,6 +1654,26 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeArgs a) {
 
 namespace {
 
+// Launches the key-group kernel serves (16-bit, no mask, no bias) and the
+// largest grid for which it replaces four-wave single-group workgroups (one
+// workgroup per CU of the 256).  Measured with two key groups against the
+// best single-group shape, on grids of 256 workgroups of 128 rows: fp16 D64
+// B2 H32 Sq512 Sk8192 85.0 against 91.9 us, bf16 D128 of that shape 141.1
+// against 148.5 us, bf16 D128 B16 H16 Sq128 Sk4096 100.0 against 106.5 us;
+// on grids of 384 to 768 workgroups 8-18 % slower.
+template <typename T, bool CAUSAL, bool BIAS>
+constexpr bool kKeyGroupsServe = sizeof(T) == 2 && !CAUSAL && !BIAS;
+constexpr uint32_t kKeyGroupMaxWorkgroups = 256;
+// Whether a stage array of the two-key-group tile holds one row block's
+// exchange buffer (D / 2 + 2 floats per lane; not so for D 128 with 32-key
+// groups, whose K and V arrays are 16 KiB).
+template <typename T, int D, int BN>
+constexpr bool key_groups_fit() {
+  using Path = typename PathFor<T, D>::type;
+  return Path::template KCopy<2 * BN, 8>::kArrayBytes >= (D / 2 + 2) * 256 &&
+         Path::template VCopy<2 * BN, 8>::kArrayBytes >= (D / 2 + 2) * 256;
+}
+
 template <typename T, int D, int MODE, bool CAUSAL, bool BIAS, int BUCKET>
 int launch_bucket(const FwdArgs& args, hipStream_t stream) {
   constexpr TableEntry e = launch_entry<T, D, BUCKET, mask_variant(CAUSAL, MODE), BIAS>();
@@ -1575,6 +1696,18 @@ int launch_bucket(const FwdArgs& args, hipStream_t stream) {
                                            BIAS>),
                        dim3(grid), dim3(e.waves * 64), 0, stream, a);
   } else {
+    // A launch of four-wave workgroups that holds at most one workgroup per
+    // CU would run one wave per SIMD: two key groups of the same 128-row
+    // tiles give each SIMD two waves instead (same m-tiles, same work).
+    if constexpr (kKeyGroupsServe<T, CAUSAL, BIAS> && e.schedule == kSchedSingle &&
+                  e.waves == 4 && key_groups_fit<T, D, e.block_n>()) {
+      if (grid <= kKeyGroupMaxWorkgroups) {
+        constexpr int kStages = D == 128 ? 2 : e.stages;
+        hipLaunchKernelGGL((attn_fwd_kg_kernel<T, D, 2, e.block_n, kStages, MODE>), dim3(grid),
+                           dim3(512), 0, stream, a);
+        return static_cast<int>(hipGetLastError());
+      }
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, e.waves, row_blocks(e), e.block_n, e.stages, MODE,
                                         CAUSAL, false, BIAS>),
                        dim3(grid), dim3(e.waves * 64), 0, stream, a);

@@ -68,7 +68,9 @@ SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU
 PROFILED = ["--no-cpu-baseline", "--settle-s", "0", "--launch-stats", "0"]
 TEMPLATE_NOTE = ("Forward template arguments: <element type, head_dim, waves, row blocks per wave, "
                  "block_n, stages, mode (0 dense, 1 compact, 2 padded), causal, split, bias> "
-                 "(attn_fwd_3w_kernel and attn_fwd_lagged_kernel: the same without row blocks); "
+                 "(attn_fwd_3w_kernel and attn_fwd_lagged_kernel: the same without row blocks; "
+                 "attn_fwd_kg_kernel: <element type, head_dim, key groups, block_n, stages, "
+                 "mode>); "
                  "merge: <element type, head_dim>; backward: <element type, head_dim, mode[, "
                  "causal]>.")
 
@@ -219,6 +221,10 @@ def kernel_accounting(short: str, splits: int | None = None, block_m: int | None
         mode, causal = int(args[5]), args[6] == "true"
         split, bias = args[7] == "true", args[8] == "true"
         block_m = 32 * int(args[2])
+    elif ident == "attn_fwd_kg_kernel" and len(args) == 6:
+        # <element, head_dim, key groups, block_n, stages, mode>: four waves of
+        # 32 rows share the query tile, no mask, bias or split.
+        mode, causal, split, bias, block_m = int(args[5]), False, False, False, 128
     elif ident == "attn_fwd_pingpong_kernel" and len(args) == 6:
         mode, causal, split, bias, block_m = int(args[4]), args[5] == "true", False, False, 256
     elif ident == "attn_fwd_merge_kernel":

@@ -377,11 +377,18 @@ def run(only=None):
     one of `only`, if given: their results replace earlier ones of the same
     candidate in results.json, the others are kept)."""
     with open(os.path.join(SWEEP_DIR, "built.json")) as f:
-        built = [b for b in json.load(f) if not b.get("skipped")]
+        records = json.load(f)
+    built = [b for b in records if not b.get("skipped")]
     results = []
     if os.path.exists(RESULTS):
         with open(RESULTS) as f:
             results = json.load(f)
+    # A candidate the last build skipped (it spills with the current source)
+    # keeps no timing from an earlier source.
+    skipped = {((b["dtype"], b["head_dim"]), _cand4(b["cand"])) for b in records
+               if b.get("skipped")}
+    results = [r for r in results
+               if ((r["dtype"], r["head_dim"]), _cand4(r["cand"])) not in skipped]
     for b in built:
         cls, cand = (b["dtype"], b["head_dim"]), _cand4(b["cand"])
         if only and not any(o in _name(cls, cand) for o in only):
@@ -442,7 +449,8 @@ def select(results):
     """Per (dtype, d, bucket, variant): (candidate, score, calls, runner-up)
     among the candidates that passed parity, from their timings.  The score is
     the sum over the key's timed calls of the candidate's time over the best
-    time any passing candidate reached on that call."""
+    time any passing candidate reached on that call.  A candidate competes
+    for a key only if it was timed on every call of that key."""
     passing = [r for r in results if r["parity"] and r["ms"]]
     fastest = {}
     for r in passing:
@@ -451,6 +459,9 @@ def select(results):
                 for var, t in per_var.items():
                     k = (r["dtype"], r["head_dim"], int(bucket), int(var), wl)
                     fastest[k] = min(fastest.get(k, t), t)
+    calls_of = {}
+    for k in fastest:
+        calls_of.setdefault(k[:4], set()).add(k[4])
     scores = {}
     for r in passing:
         acc = {}
@@ -458,10 +469,11 @@ def select(results):
             for wl, per_var in per_wl.items():
                 for var, t in per_var.items():
                     key = (r["dtype"], r["head_dim"], int(bucket), int(var))
-                    s, n = acc.get(key, (0.0, 0))
-                    acc[key] = (s + t / fastest[key + (wl,)], n + 1)
-        for key, (s, n) in acc.items():
-            scores.setdefault(key, []).append((s, n, _cand4(r["cand"])))
+                    s, n, seen = acc.get(key, (0.0, 0, frozenset()))
+                    acc[key] = (s + t / fastest[key + (wl,)], n + 1, seen | {wl})
+        for key, (s, n, seen) in acc.items():
+            if seen == calls_of[key]:
+                scores.setdefault(key, []).append((s, n, _cand4(r["cand"])))
     best = {}
     for key, lst in scores.items():
         lst.sort()
@@ -524,8 +536,9 @@ def write_summary(results, pick, best, path):
            "Written by `python -m scaled_dot_product_03_amd.sweep write` from the results of "
            "`python -m scaled_dot_product_03_amd.sweep build` (CPU) and `... sweep run` (one "
            "MI355X).  Candidates: (waves, block_n, stages, schedule) with schedule 0 single "
-           "group, 1 ping-pong, 2 two row blocks per wave, 3 lagged P.V, 4 three waves per SIMD. "
-           "Times in microseconds, the mean of 10 back-to-back calls after 0.2 s of untimed "
+           "group, 1 ping-pong, 2 two row blocks per wave, 3 lagged P.V, 4 three waves per SIMD, "
+           "'-' marks a call a candidate was not timed on.  A four-wave single-group candidate "
+           "runs as two key groups on grids of at most 256 workgroups.  Times in microseconds, the mean of 10 back-to-back calls after 0.2 s of untimed "
            "calls.  Score = sum over the key's calls of time / best time among passing "
            "candidates (1.000 per call is best).", ""]
     for dt, d in CLASSES:
@@ -548,7 +561,7 @@ def write_summary(results, pick, best, path):
             for wl, var in wls:
                 ts = [r["ms"].get(str(b), {}).get(wl, {}).get(var) for r in cands]
                 out.append(f"| {b} | {wl} | {VARIANTS[int(var)]} | " +
-                           " | ".join("" if t is None else f"{t * 1e3:.1f}" for t in ts) + " |")
+                           " | ".join("-" if t is None else f"{t * 1e3:.1f}" for t in ts) + " |")
         out += ["", "| bucket | variant | entry | from | score | timed calls | runner-up |",
                 "|---|---|---|---|---|---|---|"]
         for b in range(len(BUCKETS)):

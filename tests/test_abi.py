@@ -190,11 +190,13 @@ def test_splitk_plan():
     assert used == 2
     assert nbytes == 2 * rows * 64 * 4 + 2 * rows * 4
     # a request is cut to the key tiles and then dealt out without empty ranges
-    bn_of = lambda sk: binding.kernel_config(bf, 128, 64, sk, single_group=True)[1]
-    assert binding.splitk_plan(bf, 1, 1, 64, 100, 128, 1000)[0] == -(-100 // bn_of(100))
-    bn = next(n for n in (32, 64, 128) if bn_of(10 * n) == n)  # ten tiles in the same bucket
-    assert binding.splitk_plan(bf, 1, 1, 64, 10 * bn, 128, 4)[0] == 4   # 3+3+3+1 tiles
-    assert binding.splitk_plan(bf, 1, 1, 64, 10 * bn, 128, 6)[0] == 5   # 2 tiles each
+    bn_of = lambda sq, sk: binding.kernel_config(bf, 128, sq, sk, single_group=True)[1]
+    assert binding.splitk_plan(bf, 1, 1, 64, 100, 128, 1000)[0] == -(-100 // bn_of(64, 100))
+    # a query length and key tile whose ten tiles fall in the same bucket
+    sq, bn = next((sq, n) for sq in (64, 300, 1000, 5000) for n in (32, 64, 128)
+                  if bn_of(sq, 10 * n) == n)
+    assert binding.splitk_plan(bf, 1, 1, sq, 10 * bn, 128, 4)[0] == 4   # 3+3+3+1 tiles
+    assert binding.splitk_plan(bf, 1, 1, sq, 10 * bn, 128, 6)[0] == 5   # 2 tiles each
     assert binding.splitk_plan(bf, 1, 1, 64, 0, 128, 8)[0] == 1
     # enough query tiles already: no split by default
     assert binding.splitk_plan(bf, 4, 16, 2048, 2048, 128)[0] == 1

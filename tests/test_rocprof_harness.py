@@ -68,6 +68,9 @@ def test_accounting_of_every_bench_kernel():
                                       "false>", splits=2)
     assert split["bytes"] == rq * d * 2 + rk * 2 * d * 2 + 2 * rq * (d + 1) * 4
     assert split["flops"] == plain["flops"]
+    kg = rocprof.kernel_accounting("attn_fwd_kg_kernel<fp16, 64, 2, 64, 2, 0>")
+    assert kg["workload"] == plain["workload"]
+    assert kg["bytes"] == plain["bytes"] and kg["flops"] == plain["flops"]
     merge = rocprof.kernel_accounting("attn_fwd_merge_kernel<fp16, 64>", splits=2)
     assert merge["bytes"] == 2 * rq * (d + 1) * 4 + rq * (d * 2 + 4)
     assert merge["flops"] is None

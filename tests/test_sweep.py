@@ -88,6 +88,26 @@ def test_scores_count_every_call_alike():
     assert abs(best[("bf16", 128, 7, 0)][1] - 2.1) < 1e-9
 
 
+def test_a_candidate_missing_a_call_of_a_key_does_not_compete_for_it():
+    # a candidate timed without the mask only wins the unmasked key and is
+    # absent from the causal one, though its (missing) causal calls would
+    # otherwise make its score look small
+    results = [
+        {"dtype": "fp16", "head_dim": 64, "cand": [4, 64, 2, 0], "parity": True,
+         "ms": _ms({3: {"a": {0: 0.10, 1: 0.05}, "b": {0: 0.20, 1: 0.08}}})},
+        {"dtype": "fp16", "head_dim": 64, "cand": [8, 64, 2, 5], "parity": True,
+         "ms": _ms({3: {"a": {0: 0.09}, "b": {0: 0.18}}})},
+        {"dtype": "fp16", "head_dim": 64, "cand": [4, 32, 2, 0], "parity": True,
+         "ms": _ms({3: {"a": {0: 0.12, 1: 0.06}, "b": {1: 0.09}}})},
+    ]
+    pick, best = sweep.select(results)
+    assert pick[("fp16", 64, 3, 0)][0] == (8, 64, 2, 5)
+    assert pick[("fp16", 64, 3, 1)][0] == (4, 64, 2, 0)
+    assert best[("fp16", 64, 3, 0)][2] == 2
+    # (4, 32, 2, 0) lacks workload b's unmasked call: not a runner-up there
+    assert best[("fp16", 64, 3, 0)][3][2] == (4, 64, 2, 0)
+
+
 def test_names_and_defines_of_every_schedule():
     assert sweep._name(("bf16", 128), (4, 32, 3, 2)) == "bf16_d128_w4_n32_s3_rb2"
     assert sweep._name(("bf16", 128), (8, 64, 3, 1)) == "bf16_d128_w8_n64_s3_pp"
