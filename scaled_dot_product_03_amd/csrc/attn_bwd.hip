@@ -331,6 +331,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma nounroll
     for (int nb = 0; nb < NB; ++nb) {
       const int j0 = t * BN + nb * 32;
+      // Under the causal mask a block whose first key follows the wave's
+      // last row adds nothing (every weight is 0): skipped, wave-uniform.
+      if (CAUSAL && decltype(masked)::value && j0 > row0 + 31) continue;
       const uint32_t row_off = static_cast<uint32_t>(nb * 32 * kRow);
       f32x16 st_[1] = {f32x16{}};
       addr_rows_x_regs<T, D, kRow, 1>(k_plain + row_off, qf, st_);
@@ -531,6 +534,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma nounroll
     for (int nb = 0; nb < NB; ++nb) {
       const int q0 = qbeg + t * BQ + nb * 32;
+      // Under the causal mask a block whose last row precedes the wave's
+      // first key adds nothing to its dK and dV: skipped, wave-uniform.
+      if (CAUSAL && q0 + 31 < key0) continue;
       const uint32_t row_off = static_cast<uint32_t>(nb * 32 * kRow);
       const uint32_t qtr[2] = {q_tr[0] + row_off, q_tr[1] + row_off};
       const uint32_t dtr[2] = {d_tr[0] + row_off, d_tr[1] + row_off};
