@@ -420,7 +420,11 @@ sdpa_status sdpa_check_cu_seqlens_host(const int32_t* cu, int32_t n, int32_t tot
  * share their entries).  single_group != 0 asks for the shape of the forward
  * with a bias (for its mask and layout) and of the split forward, which
  * uses the dense non-causal entry for both masks (query it with causal = 0,
- * mode = 0).  Any output pointer may be NULL.  Returns SDPA_ERR_DTYPE /
+ * mode = 0).  A 16-bit launch without the causal mask or a bias whose
+ * entry has four waves, and which has at most 256 workgroups of block_m
+ * rows, runs them as two key groups of four waves each (eight in all) over
+ * the same block_m rows; block_m and block_n are unchanged, waves reports
+ * the entry's four.  Any output pointer may be NULL.  Returns SDPA_ERR_DTYPE /
  * SDPA_ERR_HEAD_DIM for unsupported classes, SDPA_ERR_SHAPE for a bad mode
  * or negative length.
  */
