@@ -480,13 +480,15 @@ struct BiasTile {
                              __builtin_assume_aligned(row + j0 + nb * 32 + 16 * j + 8 * lh, 16), 16);
             // h = 0 holds keys 16j .. 16j+7 and keeps the first four (group
             // 2j); h = 1 holds 16j+8 .. 16j+15 and keeps the last four
-            // (group 2j+1).  Each sends the other half to its partner.
-            const uint32_t s0 = lh ? v[0] : v[2];
-            const uint32_t s1 = lh ? v[1] : v[3];
-            const uint32_t r0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), 32));
-            const uint32_t r1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), 32));
-            const uint32_t lo[2] = {lh ? r0 : v[0], lh ? r1 : v[1]};  // group 2j
-            const uint32_t hi[2] = {lh ? v[2] : r0, lh ? v[3] : r1};  // group 2j+1
+            // (group 2j+1).  The halves trade h = 0's dwords 2, 3 for h = 1's
+            // dwords 0, 1: v_permlane32_swap of (dwords 0, 1) with (dwords
+            // 2, 3) swaps exactly those between the lane halves, leaving
+            // group 2j in the first result and group 2j+1 in the second on
+            // both halves (a VALU swap; a shuffle would go through LDS).
+            const auto x0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+            const uint32_t lo[2] = {x0[0], x1[0]};  // group 2j
+            const uint32_t hi[2] = {x0[1], x1[1]};  // group 2j+1
             __builtin_memcpy(&b[nb][8 * j], lo, 8);
             __builtin_memcpy(&b[nb][8 * j + 4], hi, 8);
           }
