@@ -80,6 +80,28 @@ def test_every_table_entry(dt, D, bucket):
         _sampled_check(x, o, lse, causal, dt, f"{dt} D{D} bucket {bucket} causal={causal}")
 
 
+@pytest.mark.parametrize("dt,D", [c for c in CLASSES if c[0] != "fp32"])
+@pytest.mark.parametrize("bucket", range(len(BUCKET_SHAPES)))
+def test_unmasked_16bit_entries_on_grids_past_one_workgroup_per_cu(dt, D, bucket):
+    """A 16-bit launch without the mask runs a four-wave entry as two key
+    groups while it has at most 256 workgroups (the small shapes above all
+    do); with enough heads to pass that, the entry's own single-group kernel
+    runs, and is checked here on two sampled heads."""
+    sq, sk = BUCKET_SHAPES[bucket]
+    bm, bn, w = binding.kernel_config(inputs.DTYPES[dt], D, sq, sk, causal=False)
+    m_tiles = -(-sq // bm)
+    H = 256 // m_tiles + 1
+    _log(f"dispatch grid > 256 {dt} D{D} bucket {bucket} Sq{sq} Sk{sk}: block_m {bm} waves {w} "
+         f"H {H} ({m_tiles * H} workgroups)")
+    assert m_tiles * H > 256
+    x = inputs.dense_inputs(1, H, sq, sk, D, dt, seed=800 + bucket, causal_modes=(False,))
+    q, k, v = x.q.to(DEV), x.k.to(DEV), x.v.to(DEV)
+    o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=False)
+    torch.cuda.synchronize()
+    _sampled_check(x, o, lse, False, dt, f"grid>256 {dt} D{D} bucket {bucket}",
+                   heads=((0, 0), (0, H - 1)))
+
+
 @pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64)])
 @pytest.mark.parametrize("bucket", [5, 7])
 def test_single_group_entries_with_bias_and_split(dt, D, bucket):
