@@ -1,7 +1,7 @@
 """rocprofv3 harness: kernel times, matrix-core, VALU and LDS use, HBM traffic.
 
     python -m scaled_dot_product_03_amd.rocprof [trace] [counters] [traffic]
-        [--out gpurun_out/prof] [--profiles profiles] [--steps 20]
+        [--out rocprof_out] [--profiles profiles] [--steps 20]
 
 Runs ``bench.py`` under rocprofv3 as child processes (this process never
 touches the GPU) and writes short markdown summaries into ``profiles/``,
@@ -549,13 +549,13 @@ PASSES = ["trace", "counters", "traffic"]
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("passes", nargs="*", help=f"any of {PASSES} (default: all)")
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "rocprof_out"))
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--limit", type=int, default=240, help="seconds per rocprofv3 run")
     ap.add_argument("--summarize", action="store_true",
                     help="run nothing: write the summaries from the results an earlier run "
-                         "left under --out (a GPU box returns only that directory)")
+                         "left under --out (copied back from the machine that ran them)")
     args = ap.parse_args(argv)
     bad = [p for p in args.passes if p not in PASSES]
     if bad:

@@ -8,8 +8,8 @@ oracle then computes every (batch or sequence, head) in a pool of host
 processes (tests/oracle_pool.py) and every element of O and LSE is compared
 (padded: every row inside the true lengths).  Each test prints the oracle's
 wall time on this host's cores and the mean |dO| over all elements, and
-appends them to gpurun_out/oracle_full_workloads.json when that directory
-exists.
+appends them to oracle_full_workloads.json in the directory that the
+environment variable SDPA03_RECORD_DIR names, if set.
 """
 
 import json
@@ -27,7 +27,6 @@ from scaled_dot_product_03_amd import binding, inputs
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 DEV = "cuda:0"
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _log(msg):
@@ -49,8 +48,8 @@ def _record(name, stats, dtype):
          f"mean|dO| {stats['mean_o']:.3e} max|dLSE| {stats['max_lse']:.3e}; oracle "
          f"{stats['oracle_s']:.1f} s on {stats['workers']} host processes "
          f"({os.cpu_count()} CPUs visible)")
-    out_dir = os.path.join(ROOT, "gpurun_out")
-    if os.path.isdir(out_dir):
+    out_dir = os.environ.get("SDPA03_RECORD_DIR")
+    if out_dir and os.path.isdir(out_dir):
         path = os.path.join(out_dir, "oracle_full_workloads.json")
         rec = json.load(open(path)) if os.path.exists(path) else {}
         rec[name] = dict(stats, cpu_count=os.cpu_count())
