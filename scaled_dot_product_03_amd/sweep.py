@@ -262,6 +262,8 @@ def build(only=None):
             f.result()
     path = os.path.join(SWEEP_DIR, "built.json")
     old = json.load(open(path)) if (only and os.path.exists(path)) else []
+    # records of schedules this source no longer has are dropped
+    old = [r for r in old if _cand4(r["cand"])[3] in SCHED_TAG]
     keep = [r for r in old if not any(o in _name((r["dtype"], r["head_dim"]), r["cand"])
                                       for o in (only or []))]
     with open(path, "w") as f:
