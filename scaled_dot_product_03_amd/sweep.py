@@ -82,8 +82,9 @@ def variant_of(mode: str, causal: bool) -> int:
 def _bucket_workloads(dtype, d):
     """Timed workloads per bucket: (name, kind, kwargs).  Every bucket has two
     dense shapes, each timed with both masks, and variable-length workloads
-    whose longest sequence falls in the bucket (compact THD; the padded
-    workload of the bench in the longest bucket of bf16 head dim 128).  The
+    whose longest sequence falls in the bucket (compact THD; for bf16 head
+    dim 128 also the bench's compact THD workload in its bucket and its padded
+    workload in the longest one).  The
     named workloads sit in their buckets; the others are seeded synthetic
     shapes of the same recipe (inputs.py)."""
     def dense(B, H, Sq, Sk):
@@ -110,6 +111,7 @@ def _bucket_workloads(dtype, d):
         7: [dense(1, 16, 8192, 8192), dense(2, 8, 6144, 6144), thd(4, 4200, 8192)],
     }
     if (dtype, d) == ("bf16", 128):
+        w[5].append(("thd_bf16_16seq_len1to4096_h16d128_causal", "named", {}))
         w[7].append(("padded_bf16_b8h32smax8192d128_len2048to8192_causal", "named", {}))
     return w
 
