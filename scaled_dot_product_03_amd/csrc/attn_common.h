@@ -193,9 +193,11 @@ struct TileCopy {
   // waits with explicit vmcnt counts, and must have no compiler-issued
   // vector-memory load outstanding that it relies on the compiler to wait
   // for.  The memory clobber keeps LDS reads of earlier code before the
-  // loads.  s_nop 4 covers the wait states between a VALU write of a
-  // descriptor SGPR (readfirstlane) and its use by a vector-memory
-  // instruction; s_nop 0 those between writing M0 and an LDS load.
+  // loads.  M0 (the LDS destination) is an input bound to the register, so
+  // the compiler writes it and knows its value; s_nop 4 covers the wait
+  // states between a VALU write of a descriptor SGPR (readfirstlane) and its
+  // use by a vector-memory instruction, and with them the one between
+  // writing M0 and an LDS load.
   __device__ __forceinline__ void issue_untracked(const char* tile, int valid_rows,
                                                   int64_t row_bytes, T* lds_tile, int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -215,12 +217,10 @@ struct TileCopy {
           static_cast<int>(lds + static_cast<uint32_t>((i * NW + wave) * 1024))));
       asm volatile(
           "s_nop 4\n\t"
-          "s_mov_b32 m0, %1\n\t"
-          "s_nop 0\n\t"
-          "buffer_load_dwordx4 %0, %2, 0 offen lds"
+          "buffer_load_dwordx4 %0, %1, 0 offen lds"
           :
-          : "v"(voff[i]), "s"(m0v), "s"(rsrc)
-          : "memory", "m0");
+          : "v"(voff[i]), "s"(rsrc), "{m0}"(m0v)
+          : "memory");
     }
 #endif
   }
