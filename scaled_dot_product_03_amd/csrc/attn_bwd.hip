@@ -96,9 +96,16 @@ __device__ __forceinline__ void interleave_reads() {
 // give the eight rows of one operand.  lane_addr[sub] is the address of the
 // lane's row and column (its chunk bits XORed with the swizzle of the row,
 // which modulo 16 depends only on sub and the lane) for nb = half = db = 0.
+// An LDS byte address as a typed LDS pointer (through uintptr_t, so that the
+// host pass, where such pointers are 64-bit, sees no widening cast).
+template <typename P>
+__device__ __forceinline__ __attribute__((address_space(3))) P* lds_ptr(uint32_t addr) {
+  return (__attribute__((address_space(3))) P*)(static_cast<uintptr_t>(addr));
+}
+
 template <typename T>
 __device__ __forceinline__ frag_t<T> lds_frag(uint32_t addr) {
-  return *(const __attribute__((address_space(3))) frag_t<T>*)(addr);
+  return *lds_ptr<const frag_t<T>>(addr);
 }
 
 template <typename T, int D, int ROW, int NB>
@@ -129,8 +136,7 @@ __device__ __forceinline__ void addr_tr_x_frags(const uint32_t (&lane_addr)[2],
         for (int sub = 0; sub < 2; ++sub) {
           const uint32_t src = (lane_addr[sub] ^ static_cast<uint32_t>(db * 64)) +
                                (nb * 32 + half * 16 + sub * 8) * ROW;
-          x[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(src));
+          x[sub] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<s16x4>(src));
         }
         frag_t<T> xf;
         __builtin_memcpy(&xf, x, sizeof(xf));
@@ -557,8 +563,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = q0 + 8 * g4 + 4 * lh;
-        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(
-            lb + static_cast<uint32_t>((8 * g4 + 4 * lh) * 4));
+        const f32x4 l4 = *lds_ptr<const f32x4>(lb + static_cast<uint32_t>((8 * g4 + 4 * lh) * 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
@@ -577,8 +582,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
       frag ws[1][2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(
-            eb + static_cast<uint32_t>((8 * g4 + 4 * lh) * 4));
+        const f32x4 d4 = *lds_ptr<const f32x4>(eb + static_cast<uint32_t>((8 * g4 + 4 * lh) * 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
