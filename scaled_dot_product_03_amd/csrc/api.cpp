@@ -467,9 +467,8 @@ sdpa_status run_bwd(const BwdCall& c) {
   const int64_t q_tiles = (static_cast<int64_t>(c.seqlen_q) + sdpa03::kBwdDqRows - 1) / sdpa03::kBwdDqRows;
   const int64_t k_tiles = (static_cast<int64_t>(c.seqlen_k) + sdpa03::kBwdDkvKeys - 1) / sdpa03::kBwdDkvKeys;
   const int64_t groups = static_cast<int64_t>(c.num_z) * H;  // (sequence, head) pairs
-  // The prep kernel covers 16 (D = 128) or 32 workspace rows per workgroup.
   if (pad > INT32_MAX || q_tiles * groups > kMaxGrid || k_tiles * groups > kMaxGrid ||
-      ws_groups * pad > (int64_t(1) << 40) || (ws_groups * pad + 15) / 16 > kMaxGrid)
+      ws_groups * pad > (int64_t(1) << 40))
     return SDPA_ERR_SHAPE;
   const uint64_t need = 2ull * static_cast<uint64_t>(ws_groups * pad) * 4ull;
   if (q_tiles > 0 && (c.workspace == nullptr ||

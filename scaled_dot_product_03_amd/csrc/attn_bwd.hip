@@ -6,7 +6,7 @@
 // forward to stash for its SdpaOpBwd node -- and never writes the score
 // matrix to memory.  With c = scale:
 //
-//   delta_i = sum_d dO_id O_id                          (prep kernel)
+//   delta_i = sum_d dO_id O_id                          (dQ kernel)
 //   P_ij    = exp(c q_i . k_j - LSE_i), 0 where masked
 //   dP_ij   = dO_i . v_j
 //   dS_ij   = P_ij (dP_ij - delta_i)
@@ -176,57 +176,6 @@ __device__ __forceinline__ void store_row(T* row, const f32x16 (&acc)[DB], float
 }
 
 // ---------------------------------------------------------------------------
-// Prep: delta = rowsum(dO * O) and LSE * log2(e) per workspace row.  D / 8
-// threads share a row, each reading 16 contiguous bytes of O and of dO (so a
-// wave reads whole rows), and a butterfly over the row's threads sums them.
-// Rows that belong to no sequence (past the end, or padding) get delta = 0
-// and +inf, so that any weight computed from them is exactly 0.
-// ---------------------------------------------------------------------------
-template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
-  constexpr int kThreadsPerRow = D / 8;
-  constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
-  const int c = threadIdx.x % kThreadsPerRow;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
-  const int64_t rows = static_cast<int64_t>(a.num_b) * a.num_heads * a.ws_rows_pad;
-  const bool in_range = gid < rows;
-  const int64_t i = gid % a.ws_rows_pad;
-  const int64_t zh = gid / a.ws_rows_pad;
-  const int64_t h = zh % a.num_heads;
-  const int64_t z = zh / a.num_heads;  // batch of the rank-4 view
-  // Rows that belong to a sequence: all rows (dense), the tokens before the
-  // last sequence's end (compact), the batch's true length (padded).
-  int64_t real_rows = a.total_q;
-  if constexpr (MODE == MODE_COMPACT) {
-    real_rows = min(max(static_cast<int64_t>(a.cu_q[a.num_z]), int64_t(0)),
-                    static_cast<int64_t>(a.total_q));
-  } else if constexpr (MODE == MODE_PADDED) {
-    if (in_range) {
-      const int64_t len = static_cast<int64_t>(a.cu_q[z + 1]) - a.cu_q[z];
-      real_rows = min(max(len, int64_t(0)), static_cast<int64_t>(a.total_q));
-    }
-  }
-  const bool real_row = in_range && i < real_rows;
-  float acc = 0.f;
-  if (real_row) {
-    const T* orow = static_cast<const T*>(a.o) + z * a.o_sb + h * a.o_sh + i * a.o_ss;
-    const T* drow = static_cast<const T*>(a.dout) + z * a.do_sb + h * a.do_sh + i * a.do_ss;
-    const frag_t<T> ov = *reinterpret_cast<const frag_t<T>*>(orow + 8 * c);
-    const frag_t<T> dv = *reinterpret_cast<const frag_t<T>*>(drow + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(ov[e]), static_cast<float>(dv[e]), acc);
-  }
-  // Every lane takes part in the butterfly (the groups are aligned in the wave).
-#pragma unroll
-  for (int off = kThreadsPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kThreadsPerRow);
-  if (in_range && c == 0) {
-    a.ws_delta[gid] = real_row ? acc : 0.f;
-    a.ws_lse2[gid] = real_row ? a.lse[z * a.lse_sb + h * a.lse_sh + i] * kLog2e
-                              : __builtin_huge_valf();
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dQ: one workgroup per 256 query rows of one (batch, head); 8 waves of 32
 // rows; key tiles of 64 stream through two LDS stages.
 // ---------------------------------------------------------------------------
@@ -286,9 +235,46 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   frag df[D / 16];
   load_row_frags<T, D>(qrow, row_ok, lh, qf);
   load_row_frags<T, D>(drow, row_ok, lh, df);
-  const int64_t wrow = (static_cast<int64_t>(sr.b) * a.num_heads + h) * a.ws_rows_pad + token;
-  const float lse2 = row_ok ? a.ws_lse2[wrow] : 0.f;
-  const float delta = row_ok ? a.ws_delta[wrow] : 0.f;
+  // The row's delta = rowsum(dO * O) (lanes l and l + 32 hold half the row
+  // each) and LSE * log2(e), kept here and written to the workspace for the
+  // dK/dV kernel.  Rows of the tile that belong to no sequence -- past the
+  // end (dense, padded) or past the last sequence (compact; rows past any
+  // other sequence are the next one's) -- get delta = 0 and +inf, so any
+  // weight computed from them is exactly 0: the dK/dV kernel reads whole
+  // 64-row tiles, which end inside this 256-row tile.
+  float delta = 0.f;
+  float lse2 = __builtin_huge_valf();
+  {
+    const T* orow = static_cast<const T*>(a.o) + sr.b * a.o_sb + h * a.o_sh + token * a.o_ss;
+    frag of[D / 16];
+    load_row_frags<T, D>(orow, row_ok, lh, of);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        part = fmaf(static_cast<float>(of[ks][e]), static_cast<float>(df[ks][e]), part);
+      }
+    }
+    const float row_delta = sum_across_halves(part);
+    if (row_ok) {
+      delta = row_delta;
+      lse2 = a.lse[sr.b * a.lse_sb + h * a.lse_sh + token] * kLog2e;
+    }
+    bool owned = row_ok;
+    if constexpr (MODE == MODE_COMPACT) {
+      const int real_rows = min(max(a.cu_q[a.num_z], 0), a.total_q);
+      owned = owned || token >= real_rows;
+    } else {
+      owned = true;
+    }
+    if (lh == 0 && owned && token < a.ws_rows_pad) {
+      const int64_t wrow = (static_cast<int64_t>(sr.b) * a.num_heads + h) * a.ws_rows_pad + token;
+      a.ws_delta[wrow] = delta;
+      a.ws_lse2[wrow] = lse2;
+    }
+  }
+  if (!row_ok) lse2 = 0.f;
   const float c2 = a.scale_log2;
 
   f32x16 acc[DB];
@@ -624,17 +610,10 @@ int launch_typed(const BwdArgs& args, hipStream_t s) {
   const uint32_t groups = static_cast<uint32_t>(a.num_heads) * static_cast<uint32_t>(a.num_z);
   a.span_q = CAUSAL ? causal_span(groups, a.q_tiles, kBwdDqRows * 2 / 64) : 0;
   a.span_k = CAUSAL ? causal_span(groups, a.k_tiles, kBwdDkvKeys * 2 / 64) : 0;
-  const int64_t rows = static_cast<int64_t>(a.num_b) * a.num_heads * a.ws_rows_pad;
   if (a.q_tiles > 0) {
-    constexpr int64_t kRowsPerBlock = 256 / (D / 8);
-    hipLaunchKernelGGL((attn_bwd_prep_kernel<T, D, MODE>),
-                       dim3(static_cast<uint32_t>((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
-                       dim3(256), 0, s, a);
-    int err = static_cast<int>(hipGetLastError());
-    if (err != 0) return err;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MODE, CAUSAL>),
                        dim3(static_cast<uint32_t>(a.q_tiles) * groups), dim3(kBwdDqRows * 2), 0, s, a);
-    err = static_cast<int>(hipGetLastError());
+    const int err = static_cast<int>(hipGetLastError());
     if (err != 0) return err;
   }
   if (a.k_tiles > 0) {

@@ -56,9 +56,9 @@ constexpr int64_t bwd_ws_rows_pad(int64_t rows) { return (rows + 63) / 64 * 64 +
 constexpr int kBwdDqRows = 256;
 constexpr int kBwdDkvKeys = 128;
 
-// Launches the three backward kernels on `stream`; returns the HIP error of
-// the first launch that fails (0 on success).  Arguments are assumed
-// validated; dtype is 16-bit.
+// Launches the two backward kernels (dQ, then dK/dV) on `stream`; returns
+// the HIP error of the first launch that fails (0 on success).  Arguments are
+// assumed validated; dtype is 16-bit.
 int launch_attn_bwd(const BwdArgs& args, int dtype, int head_dim, int mode, bool causal,
                     void* stream);
 

@@ -205,10 +205,11 @@ def kernel_accounting(short: str, splits: int | None = None, block_m: int | None
     mask; under the causal mask query tile m of block_m rows loads keys
     0 .. block_m (m + 1) - 1).  Split forward: Q, K, V read and each split's
     fp32 partial output and logsumexp written; merge: those read, O and LSE
-    written.  Backward: prep reads O, dO, LSE and writes two fp32 values per
-    row; dQ reads Q, dO, K, V and the two row values and writes dQ; dK/dV
-    reads the same and writes dK, dV.  FLOPs: 2 products per forward, 3 in
-    the dQ kernel (S, dP, dQ) and 4 in the dK/dV kernel (S, dP, dV, dK)."""
+    written.  Backward: dQ reads Q, O, dO, K, V and the fp32 LSE and writes
+    dQ and two fp32 values per row (rowsum(dO * O) and LSE * log2(e)); dK/dV
+    reads Q, dO, K, V and those row values and writes dK, dV.  FLOPs: 2
+    products per forward, 3 in the dQ kernel (S, dP, dQ) and 4 in the dK/dV
+    kernel (S, dP, dV, dK)."""
     ident, args = template_args(short)
     if len(args) < 2 or args[0] not in ELEM_BYTES:
         return None
@@ -229,7 +230,7 @@ def kernel_accounting(short: str, splits: int | None = None, block_m: int | None
         mode, causal, split, bias, block_m = int(args[4]), args[5] == "true", False, False, 256
     elif ident == "attn_fwd_merge_kernel":
         mode, causal, split, bias = 0, False, False, False
-    elif ident in ("attn_bwd_prep_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel"):
+    elif ident in ("attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel"):
         mode = int(args[2])
         causal = len(args) > 3 and args[3] == "true"
         split = bias = False
@@ -243,10 +244,8 @@ def kernel_accounting(short: str, splits: int | None = None, block_m: int | None
     rk = H * sum(lk for _, lk in pairs)
     prod = product_flops(pairs, H, D, causal)
     out = {"workload": name, "bytes": None, "flops": None}
-    if ident == "attn_bwd_prep_kernel":
-        out["bytes"] = rq * (2 * D * es + 4) + rq * 2 * 4
-    elif ident == "attn_bwd_dq_kernel":
-        out["bytes"] = rq * 3 * D * es + rk * 2 * D * es + rq * 2 * 4
+    if ident == "attn_bwd_dq_kernel":
+        out["bytes"] = rq * (4 * D * es + 4) + rk * 2 * D * es + rq * 2 * 4
         out["flops"] = 3 * prod
     elif ident == "attn_bwd_dkdv_kernel":
         out["bytes"] = rq * 2 * D * es + rq * 2 * 4 + rk * 4 * D * es
@@ -528,9 +527,9 @@ def write_traffic(fetch, write, stats, cmds, path, splits=None):
               "every key tile a query tile loads (all of them without the mask; under the "
               "causal mask query tile m of block_m rows loads keys 0 .. block_m (m + 1) - 1); "
               "split forward: Q, K, V read and every split's fp32 partial output and "
-              "logsumexp written; merge: those read, O and LSE written; backward prep: O, "
-              "dO and LSE read, two fp32 values per row written; dQ: Q, dO, K, V and the row "
-              "values read, dQ written; dK/dV: the same read, dK and dV written.  HBM GB/s = "
+              "logsumexp written; merge: those read, O and LSE written; backward dQ: Q, O, "
+              "dO, K, V and the fp32 LSE read, dQ and two fp32 values per row written; dK/dV: "
+              "Q, dO, K, V and the row values read, dK and dV written.  HBM GB/s = "
               "scaled bytes over the kernel's average duration in the trace pass.  The dense "
               "non-causal forward without bias is the kernel bench.py reports as "
               "roofline.traffic.", "", TEMPLATE_NOTE]
