@@ -8,7 +8,8 @@ and dO alone.  Every gradient element of small and ragged shapes is compared
 B4 H16 S2048 D128 workload and whole (sequence, head) pairs of the THD and
 padded workloads are compared in full.  Also: determinism, empty query or key
 axes, untouched rows outside every sequence, no gradient crossing a sequence
-boundary, the fp32 refusal and a too-small workspace.
+boundary, the fp32 refusal, a too-small workspace, and a workspace whose old
+contents (NaN bytes) are never read.
 
 Tolerance.  The gradients are sums of products whose factors were rounded to
 the input type (P and dS before the matrix products, O before delta), so the
@@ -244,6 +245,65 @@ def test_bwd_padded_small(dt, D, causal):
             if n:
                 _grad_check(g[b, :, :n], r[b, :, :n], dt,
                             f"padded {dt} D{D} causal={causal} b={b} {name}")
+
+
+@pytest.mark.parametrize("layout", ["dense", "compact", "padded"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_workspace_contents_never_read_before_written(layout, causal):
+    """The dQ kernel writes each query row's row values (and the padding rows
+    the dK/dV kernel's tiles reach) into the caller's workspace before the
+    dK/dV kernel reads them: a workspace full of NaN bytes and one full of
+    zeros give bit-identical, finite gradients.  Ragged lengths (not multiples
+    of 64 or 256), an empty sequence and tokens past the last sequence."""
+    dt, D, H = "bf16", 128, 2
+    _log(f"bwd workspace poison {layout} causal={causal}")
+    if layout == "dense":
+        x = inputs.dense_inputs(1, H, 300, 333, D, dt, seed=91)
+        do = _dout_like(tuple(x.q.shape), dt, 92)
+        q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+        o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=causal)
+        nbytes = binding.bwd_workspace_bytes(1, H, 300)
+        call = lambda ws: binding.attn_bwd(q, k, v, o, dod, lse, scale=x.scale, causal=causal,
+                                           workspace=ws)
+    elif layout == "compact":
+        lengths = [70, 0, 257, 130]
+        x = inputs.compact_inputs(len(lengths), H, D, dt, seed=93, len_lo=1, len_hi=2,
+                                  lengths_q=lengths, lengths_k=lengths, extra_tokens=7)
+        do = _dout_like(tuple(x.q.shape), dt, 94)
+        q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+        o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                                 scale=x.scale, causal=causal)
+        nbytes = binding.bwd_workspace_bytes(1, H, int(q.shape[0]))
+        call = lambda ws: binding.attn_bwd_compact_varlen(
+            q, k, v, o, dod, lse, x.cu_seqlens_q, x.cu_seqlens_k, scale=x.scale, causal=causal,
+            workspace=ws)
+    else:
+        lengths = [300, 0, 65, 190]
+        x = inputs.padded_inputs(4, H, 300, 300, D, dt, seed=95, len_lo=1, len_hi=2,
+                                 lengths_q=lengths, lengths_k=lengths)
+        do = _dout_like(tuple(x.q.shape), dt, 96)
+        q, k, v, dod = _dev(x.q), _dev(x.k), _dev(x.v), _dev(do)
+        o, lse = binding.attn_fwd_padded_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                                scale=x.scale, causal=causal)
+        nbytes = binding.bwd_workspace_bytes(4, H, 300)
+        call = lambda ws: binding.attn_bwd_padded_varlen(
+            q, k, v, o, dod, lse, x.cu_seqlens_q, x.cu_seqlens_k, scale=x.scale, causal=causal,
+            workspace=ws)
+    zeros = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    poison = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    a = call(zeros)
+    b = call(poison)
+    torch.cuda.synchronize()
+    if layout == "compact":
+        tq, tk = int(x.cu_seqlens_q[-1]), int(x.cu_seqlens_k[-1])
+        a = (a[0][:tq], a[1][:tk], a[2][:tk])
+        b = (b[0][:tq], b[1][:tk], b[2][:tk])
+    elif layout == "padded":
+        a = tuple(torch.cat([g[i, :, :n] for i, n in enumerate(lengths)], dim=1) for g in a)
+        b = tuple(torch.cat([g[i, :, :n] for i, n in enumerate(lengths)], dim=1) for g in b)
+    for name, ga, gb in zip(("dq", "dk", "dv"), a, b):
+        assert torch.isfinite(ga).all(), name
+        assert torch.equal(ga, gb), name
 
 
 def test_bwd_compact_no_cross_sequence_leak_bit_exact():
