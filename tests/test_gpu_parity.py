@@ -1,9 +1,10 @@
 """GPU parity: the HIP library against the float64 oracle on seeded inputs.
 
 Small and ragged shapes are compared element by element over every output;
-the five named workloads at their full sizes are compared on sampled rows
-(the oracle computes those rows one by one) and checked for properties that
-hold at any size.  Bookkeeping (which rows are written, which keys are read)
+the five named workloads at their full sizes, and sequences far longer than
+they are (64K queries and keys; 128K keys against 256 queries), are compared
+on sampled rows (the oracle computes those rows one by one) and checked for
+properties that hold at any size.  Bookkeeping (which rows are written, which keys are read)
 is checked bit-exactly.
 """
 
@@ -139,6 +140,53 @@ def test_workload_dense_bf16_s2048_sampled():
 def test_workload_dense_fp16_sq512_sk8192_sampled():
     x = inputs.workload("dense_fp16_b2h32sq512sk8192d64")
     _dense_sampled(x, "dense fp16 B2H32 Sq512 Sk8192 D64", [(0, 0), (0, 31), (1, 16)], 3)
+
+
+def test_long_sequence_dense_bf16_s65536_sampled():
+    """Sequences far past the named workloads: B1 H2 S65536 D128 bf16 (512
+    query tiles, 1024 key tiles per row), both masks, on rows at tile edges
+    spread over the whole sequence and random ones."""
+    x = inputs.dense_inputs(1, 2, 65536, 65536, 128, "bf16", seed=101)
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    rng = np.random.default_rng(102)
+    for causal in (False, True):
+        _log(f"long dense bf16 S65536 causal={causal}")
+        o, lse = binding.attn_fwd(q, k, v, scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        go, gl, ro, rl = [], [], [], []
+        for h in range(2):
+            rows = sample_rows(65536, rng, tile=1024, extra=16)
+            r_o, r_l = attention_head(to64(x.q[0, h]), to64(x.k[0, h]), to64(x.v[0, h]), x.scale,
+                                      causal, rows=rows)
+            go.append(to64(o[0, h, rows]))
+            gl.append(to64(lse[0, h, rows]))
+            ro.append(r_o)
+            rl.append(r_l)
+        stats = check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro),
+                      np.concatenate(rl), "bf16", label=f"long dense causal={causal}")
+        _log(f"  {stats}")
+
+
+def test_long_keys_few_queries_fp16_sk131072_sampled():
+    """Few queries against very many keys (fp16 B1 H4 Sq256 Sk131072 D64),
+    through attn_fwd and the split forward, on sampled rows."""
+    x = inputs.dense_inputs(1, 4, 256, 131072, 64, "fp16", seed=103)
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    rng = np.random.default_rng(104)
+    rows = sample_rows(256, rng, tile=64, extra=8)
+    refs = [attention_head(to64(x.q[0, h]), to64(x.k[0, h]), to64(x.v[0, h]), x.scale, False,
+                           rows=rows) for h in range(4)]
+    for name, call in (("attn_fwd", lambda: binding.attn_fwd(q, k, v, scale=x.scale)),
+                       ("attn_fwd_splitk", lambda: binding.attn_fwd_splitk(q, k, v,
+                                                                           scale=x.scale))):
+        _log(f"long keys fp16 Sk131072 {name}")
+        o, lse = call()
+        torch.cuda.synchronize()
+        stats = check(np.concatenate([to64(o[0, h, rows]) for h in range(4)]),
+                      np.concatenate([to64(lse[0, h, rows]) for h in range(4)]),
+                      np.concatenate([r[0] for r in refs]), np.concatenate([r[1] for r in refs]),
+                      "fp16", label=f"long keys {name}")
+        _log(f"  {stats}")
 
 
 def test_workload_compact_thd_sampled():
