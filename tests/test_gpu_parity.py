@@ -2,7 +2,8 @@
 
 Small and ragged shapes are compared element by element over every output;
 the five named workloads at their full sizes, and sequences far longer than
-they are (64K queries and keys; 128K keys against 256 queries), are compared
+they are (64K queries and keys; 128K keys against 256 queries; a compact
+sequence of 40,000 tokens), are compared
 on sampled rows (the oracle computes those rows one by one) and checked for
 properties that hold at any size.  Bookkeeping (which rows are written, which keys are read)
 is checked bit-exactly.
@@ -221,6 +222,40 @@ def test_workload_compact_thd_sampled():
     stats = check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl),
                   "bf16", label="compact THD")
     _log(f"  {stats}")
+
+
+def test_long_compact_sequences_sampled():
+    """Compact varlen with sequences far longer than the THD workload's (a
+    40,000-token one beside short ones), both masks, on sampled rows; every
+    token's output is written."""
+    lengths = [1, 40000, 3, 20001]
+    x = inputs.compact_inputs(len(lengths), 2, 128, "bf16", seed=105, len_lo=1, len_hi=2,
+                              lengths_q=lengths, lengths_k=lengths)
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    cu = x.cu_seqlens_q
+    rng = np.random.default_rng(106)
+    for causal in (False, True):
+        _log(f"long compact lengths {lengths} causal={causal}")
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((1, q.shape[1], q.shape[0]), float("nan"), device=DEV)
+        o, lse = binding.attn_fwd_compact_varlen(q, k, v, x.cu_seqlens_q, x.cu_seqlens_k,
+                                                 scale=x.scale, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        go, gl, ro, rl = [], [], [], []
+        for z in range(len(cu) - 1):
+            s, e = int(cu[z]), int(cu[z + 1])
+            for h in range(2):
+                rows = sample_rows(e - s, rng, tile=1024, extra=8)
+                r_o, r_l = attention_head(to64(x.q[s:e, h]), to64(x.k[s:e, h]),
+                                          to64(x.v[s:e, h]), x.scale, causal, rows=rows)
+                go.append(to64(o[s + rows, h]))
+                gl.append(to64(lse[0, h, s + rows]))
+                ro.append(r_o)
+                rl.append(r_l)
+        stats = check(np.concatenate(go), np.concatenate(gl), np.concatenate(ro),
+                      np.concatenate(rl), "bf16", label=f"long compact causal={causal}")
+        _log(f"  {stats}")
 
 
 def test_workload_padded_sampled():
