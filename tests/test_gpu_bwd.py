@@ -5,8 +5,8 @@ The forward's own outputs (O and LSE from the GPU forward) feed the
 backward, as in training; the oracle's gradients are computed from Q, K, V
 and dO alone.  Every gradient element of small and ragged shapes is compared
 (both masks, D 64 and 128, bf16 and fp16); whole heads of the dense bf16
-B4 H16 S2048 D128 workload and whole (sequence, head) pairs of the THD and
-padded workloads are compared in full.  Also: determinism, empty query or key
+B4 H16 S2048 D128 workload, a whole S8192 head and whole (sequence, head)
+pairs of the THD and padded workloads are compared in full.  Also: determinism, empty query or key
 axes, untouched rows outside every sequence, no gradient crossing a sequence
 boundary, the fp32 refusal, a too-small workspace, and a workspace whose old
 contents (NaN bytes) are never read.
@@ -116,6 +116,16 @@ def test_bwd_workload_dense_bf16_s2048_heads():
             gg = torch.stack([g[b, h] for b, h in heads])
             rr = np.stack([r[b, h] for b, h in heads])
             _grad_check(gg, rr, "bf16", f"S2048 causal={causal} {name}")
+
+
+def test_bwd_long_sequence_bf16_s8192_one_head():
+    """A sequence four times the workload's (bf16 B1 H1 S8192 D128), both
+    masks, every gradient element of the head against the oracle."""
+    for causal in (False, True):
+        _log(f"bwd B1H1S8192D128 causal={causal}")
+        got, ref = _run(1, 1, 8192, 8192, 128, "bf16", causal, seed=107)
+        for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+            _grad_check(g, r, "bf16", f"S8192 causal={causal} {name}")
 
 
 def test_bwd_deterministic():
