@@ -1,4 +1,4 @@
-"""The process-pool driver of the full-size GPU comparisons, on the CPU: it
+"""The process pool behind the full-size GPU comparisons, on the CPU: it
 must reproduce the oracle head by head (zero error when handed the oracle's
 own outputs) in every layout and element type, and must see an error planted
 in one element of the compared output."""
